@@ -1,0 +1,228 @@
+/*
+ * oracle/gemm_ref.c -- the plain fp64 CPU oracle of the blocked GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this file.  It shares no code,
+ * header, table or constant with the HIP library and includes nothing from it.
+ *
+ * What it computes is the plain definition of the operation the pages build:
+ *
+ *   C(m,n) = epilogue( sum_{k=0}^{K-1} A(m,k) * B(k,n) )
+ *
+ * "Named layouts" (NineToothed), the GEMM arrangement at the top of the page:
+ * an fp32 zero accumulator, acc = acc + dot(lhs[k], rhs[k]) over the K blocks
+ * in ascending order, then one cast to the output dtype.  The same page,
+ * section "Contract", admits same-output-domain bias / ReLU / residual
+ * postprocessing; the order used here is relu(acc + bias) + residual.
+ *
+ * The oracle takes the sum in fp64 instead of fp32: every product of two
+ * 16-bit floats is exact in fp64, and the k order is ascending for every
+ * cell, so the result does not depend on thread count or loop nesting.
+ * Build with -O2 -ffp-contract=off and without fast-math so that no fused
+ * multiply-add or reassociation changes a single rounding.
+ *
+ * Element addressing follows the explicit-transpose rule ("Named layouts",
+ * section "Contract": a transpose is never implied by matching sizes):
+ *   opA = 0 : A(m,k) = A[m*lda + k]      opA = 1 : A(m,k) = A[k*lda + m]
+ *   opB = 0 : B(k,n) = B[k*ldb + n]      opB = 1 : B(k,n) = B[n*ldb + k]
+ *   residual: R(m,n) = R[m*ldr + n]      bias:     bias(n) = bias[n]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F16 1
+#define ORC_BF16 2
+
+/* ---- 16-bit formats, decoded from their definitions -------------------- */
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent field 0 holds zeros and subnormals (fraction * 2^-24); field 31
+ * holds infinities (fraction 0) and NaNs. */
+double orc_decode_f16(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 0x1f;
+  int frac = h & 0x3ff;
+  double v;
+  if (expo == 0)
+    v = ldexp((double)frac, -24);
+  else if (expo == 31)
+    v = frac ? NAN : INFINITY;
+  else
+    v = ldexp((double)(frac + 1024), expo - 25); /* (1 + f/2^10) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ * Exponent field 0 holds zeros and subnormals (fraction * 2^-133); field 255
+ * holds infinities and NaNs. */
+double orc_decode_bf16(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 7) & 0xff;
+  int frac = h & 0x7f;
+  double v;
+  if (expo == 0)
+    v = ldexp((double)frac, -133);
+  else if (expo == 255)
+    v = frac ? NAN : INFINITY;
+  else
+    v = ldexp((double)(frac + 128), expo - 134); /* (1 + f/2^7) * 2^(e-127) */
+  return sign ? -v : v;
+}
+
+static double decode(uint16_t h, int dtype) {
+  return dtype == ORC_BF16 ? orc_decode_bf16(h) : orc_decode_f16(h);
+}
+
+/* Round an fp64 value to a 16-bit float, to nearest with ties to even.
+ * frac_bits: 10 (binary16) or 7 (bfloat16); emin: -14 or -126;
+ * emax: 15 or 127.  The significand is scaled by a power of two (exact) and
+ * rounded with nearbyint() under the default round-to-nearest-even mode. */
+static uint16_t round_to_16(double x, int frac_bits, int emin, int emax,
+                            int exp_bits) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  uint16_t inf = (uint16_t)(((1u << exp_bits) - 1) << frac_bits);
+  if (isnan(x)) return (uint16_t)(inf | (1u << (frac_bits - 1))); /* quiet NaN */
+  double ax = fabs(x);
+  if (isinf(ax)) return sign | inf;
+  if (ax == 0.0) return sign;
+  int e2;
+  (void)frexp(ax, &e2); /* ax = f * 2^e2, f in [0.5, 1) */
+  int E = e2 - 1;       /* ax in [2^E, 2^(E+1)) */
+  if (E < emin) {
+    /* subnormal range: integer multiples of 2^(emin - frac_bits) */
+    double q = nearbyint(ldexp(ax, frac_bits - emin));
+    /* q == 2^frac_bits rounds up into the smallest normal, which has the
+     * same bit pattern as the fraction overflowing into the exponent. */
+    return sign | (uint16_t)q;
+  }
+  double q = nearbyint(ldexp(ax, frac_bits - E)); /* in [2^fb, 2^(fb+1)] */
+  if (q == ldexp(1.0, frac_bits + 1)) {
+    q = ldexp(1.0, frac_bits);
+    E += 1;
+  }
+  if (E > emax) return sign | inf;
+  uint16_t expo_field = (uint16_t)(E + ((1 << (exp_bits - 1)) - 1));
+  uint16_t frac_field = (uint16_t)((int64_t)q - (1 << frac_bits));
+  return sign | (uint16_t)(expo_field << frac_bits) | frac_field;
+}
+
+uint16_t orc_round_f16(double x) { return round_to_16(x, 10, -14, 15, 5); }
+uint16_t orc_round_bf16(double x) { return round_to_16(x, 7, -126, 127, 8); }
+
+void orc_round_array(const double* x, uint16_t* out, int64_t n, int dtype) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = dtype == ORC_BF16 ? orc_round_bf16(x[i]) : orc_round_f16(x[i]);
+}
+
+void orc_decode_array(const uint16_t* h, double* out, int64_t n, int dtype) {
+  for (int64_t i = 0; i < n; ++i) out[i] = decode(h[i], dtype);
+}
+
+/* ---- the GEMM and its epilogue ------------------------------------------ */
+
+static double elem_a(const uint16_t* A, int64_t lda, int opA, int64_t m,
+                     int64_t k, int dt) {
+  return decode(opA ? A[k * lda + m] : A[m * lda + k], dt);
+}
+
+static double elem_b(const uint16_t* B, int64_t ldb, int opB, int64_t k,
+                     int64_t n, int dt) {
+  return decode(opB ? B[n * ldb + k] : B[k * ldb + n], dt);
+}
+
+/* Epilogue of one cell, in fp64: y = acc; y += bias(n); y = max(y, 0);
+ * y += R(m,n).  Each step only when its operand or flag is present. */
+static double epilogue(double acc, int64_t m, int64_t n, const uint16_t* bias,
+                       int relu, const uint16_t* R, int64_t ldr, int epi_dt) {
+  double y = acc;
+  if (bias) y += decode(bias[n], epi_dt);
+  if (relu) y = y > 0.0 ? y : 0.0;
+  if (R) y += decode(R[m * ldr + n], epi_dt);
+  return y;
+}
+
+/*
+ * Reference values of the block [m_lo, m_hi) x [n_lo, n_hi) of C, written to
+ * out[(m - m_lo) * (n_hi - n_lo) + (n - n_lo)] unrounded (fp64).
+ *
+ * Each row is an independent job (OpenMP over rows when nthreads > 1).  For a
+ * row, the accumulators of all its cells start at zero and receive the terms
+ * k = 0, 1, ..., K-1 in that order; walking k in the outer loop and n in the
+ * inner loop does not change the order of any single cell's sum.
+ * Returns 0, or -1 on an argument error.
+ */
+int orc_gemm_block(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                   int64_t lda, int opA, const uint16_t* B, int64_t ldb,
+                   int opB, int in_dt, const uint16_t* bias, int relu,
+                   const uint16_t* R, int64_t ldr, int epi_dt, int64_t m_lo,
+                   int64_t m_hi, int64_t n_lo, int64_t n_hi, double* out,
+                   int nthreads) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if (m_lo < 0 || m_hi > M || m_lo >= m_hi) return -1;
+  if (n_lo < 0 || n_hi > N || n_lo >= n_hi) return -1;
+  int64_t W = n_hi - n_lo;
+  /* Decode B's needed columns once per call: Bd[k][n - n_lo]. */
+  double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * W));
+  if (!Bd) return -1;
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t n = n_lo; n < n_hi; ++n)
+      Bd[k * W + (n - n_lo)] = elem_b(B, ldb, opB, k, n, in_dt);
+
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t m = m_lo; m < m_hi; ++m) {
+    double* acc = out + (m - m_lo) * W;
+    for (int64_t j = 0; j < W; ++j) acc[j] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double a = elem_a(A, lda, opA, m, k, in_dt);
+      const double* brow = Bd + k * W;
+      for (int64_t j = 0; j < W; ++j) acc[j] += a * brow[j];
+    }
+    for (int64_t j = 0; j < W; ++j)
+      acc[j] = epilogue(acc[j], m, n_lo + j, bias, relu, R, ldr, epi_dt);
+  }
+  free(Bd);
+  return 0;
+}
+
+/* Reference values of scattered cells (ms[i], ns[i]), one by one, with the
+ * same per-cell order (k ascending).  Used to sample outputs of shapes too
+ * large for a full oracle run. */
+int orc_gemm_cells(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                   int64_t lda, int opA, const uint16_t* B, int64_t ldb,
+                   int opB, int in_dt, const uint16_t* bias, int relu,
+                   const uint16_t* R, int64_t ldr, int epi_dt,
+                   const int64_t* ms, const int64_t* ns, int64_t count,
+                   double* out, int nthreads) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  for (int64_t i = 0; i < count; ++i)
+    if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+#endif
+  for (int64_t i = 0; i < count; ++i) {
+    int64_t m = ms[i], n = ns[i];
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+      acc += elem_a(A, lda, opA, m, k, in_dt) * elem_b(B, ldb, opB, k, n, in_dt);
+    out[i] = epilogue(acc, m, n, bias, relu, R, ldr, epi_dt);
+  }
+  return 0;
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

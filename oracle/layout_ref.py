@@ -1,0 +1,328 @@
+"""Layout oracle: ownership, copy and swizzle maps in plain Python integers.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).  Every function restates a
+formula from the pages, or from the stated design of the MI355X kernel, with
+no shared code with the HIP layout module it is compared against.
+
+Page maps
+  * cooperative tile layout -- "My Triton From Scratch, Part 12: CUDA Tile
+    Layouts", sections "Cooperative tile layouts" and "Validation is part of
+    the model";
+  * kernel layout and projections -- same page, sections "Kernel layout",
+    "Projecting logical values onto threads", "Explicit broadcast axes";
+  * register tiles -- "My Triton From Scratch, Part 16: Register Tiles",
+    sections "Describing the mapping", "A strided ownership rule" and
+    "Choosing the physical thread shape";
+  * GF(2) linear layouts -- "Triton LinearLayout", sections "Basis-vector
+    representation", "LinearLayout::apply" and "Surjectivity, injectivity,
+    and broadcasts".
+
+MI355X maps (not on the pages; the matrix-core operand layout is AMD's
+documented v_mfma_f32_16x16x32_{f16,bf16} register layout)
+  * mfma16_a / mfma16_b / mfma16_c -- one 16x16x32 fragment;
+  * gemm_c_owner -- (register, lane, wave) -> (row, col) of a workgroup tile;
+  * lds_slot -- the XOR-swizzled 16-byte chunk slot of an operand tile;
+  * copy_kcontig / copy_mncontig -- the cooperative global->LDS copy maps.
+"""
+from math import prod
+
+MAX_THREADS_PER_BLOCK = 1024
+
+
+# --------------------------------------------------------------------------
+# Part 12: kernel layout, projection, cooperative traversal
+# --------------------------------------------------------------------------
+
+def _check_shape(shape, what):
+    if not isinstance(shape, tuple) or len(shape) not in (1, 2):
+        raise ValueError(f"{what} must be a rank-1 or rank-2 tuple")
+    for d in shape:
+        if not isinstance(d, int) or isinstance(d, bool) or d <= 0:
+            raise ValueError(f"{what} dims must be positive integers")
+
+
+def kernel_layout(output_tile_shape, thread_shape):
+    """Program-instance layout: both shapes rank 1 or 2, positive, same rank,
+    thread product within the 1024-thread block limit (Part 12, "Kernel
+    layout").  Returns rank, is_rank2 and threads_per_block."""
+    _check_shape(output_tile_shape, "output_tile_shape")
+    _check_shape(thread_shape, "thread_shape")
+    if len(output_tile_shape) != len(thread_shape):
+        raise ValueError("output and thread shapes must have equal rank")
+    tpb = prod(thread_shape)
+    if tpb > MAX_THREADS_PER_BLOCK:
+        raise ValueError("thread product exceeds the block limit")
+    return {"rank": len(thread_shape), "is_rank2": len(thread_shape) == 2,
+            "threads_per_block": tpb}
+
+
+def tile_layout(thread_shape, logical_shape, broadcast_axes=()):
+    """Projection of a per-thread logical value onto thread axes (Part 12,
+    "Projecting logical values onto threads" and "Explicit broadcast axes"):
+    an axis listed as broadcast maps to None; otherwise an extent equal to
+    the thread extent maps to that axis, an extent of one maps to None, and
+    any other extent is rejected."""
+    _check_shape(logical_shape, "logical_shape")
+    if len(logical_shape) != len(thread_shape):
+        raise ValueError("logical and thread shapes must have equal rank")
+    for a in broadcast_axes:
+        if not (0 <= a < len(logical_shape)):
+            raise ValueError("broadcast axis out of range")
+    axes = []
+    for axis, (ld, td) in enumerate(zip(logical_shape, thread_shape)):
+        if axis in broadcast_axes:
+            axes.append(None)
+        elif ld == td:
+            axes.append(axis)
+        elif ld == 1:
+            axes.append(None)
+        else:
+            raise ValueError("logical dim cannot be projected onto threads")
+    return tuple(axes)
+
+
+def coop_iterations(logical_shape, threads):
+    """ceil(tile size / threads per block) (Part 12, "Cooperative tile layouts")."""
+    _check_shape(logical_shape, "logical_shape")
+    if not (1 <= threads <= MAX_THREADS_PER_BLOCK):
+        raise ValueError("threads out of range")
+    return -(-prod(logical_shape) // threads)
+
+
+def coop_linear(logical_shape, threads, t, i):
+    """Linear index that thread t visits at iteration i: t + i*threads."""
+    if not (0 <= t < threads):
+        raise ValueError("thread index out of range")
+    if not (0 <= i < coop_iterations(logical_shape, threads)):
+        raise ValueError("iteration out of range")
+    return t + i * threads
+
+
+def coop_contains(logical_shape, threads, t, i):
+    """False for the inactive tail lanes of the last iteration."""
+    return coop_linear(logical_shape, threads, t, i) < prod(logical_shape)
+
+
+def coop_coordinate(logical_shape, order, linear):
+    """Coordinate of a linear index: peel axes in `order`, fastest first."""
+    _check_shape(logical_shape, "logical_shape")
+    if sorted(order) != list(range(len(logical_shape))):
+        raise ValueError("order must be a permutation of the axes")
+    if not (0 <= linear < prod(logical_shape)):
+        raise ValueError("linear index outside the tile")
+    coord = [0] * len(logical_shape)
+    rem = linear
+    for axis in order:
+        coord[axis] = rem % logical_shape[axis]
+        rem //= logical_shape[axis]
+    return tuple(coord)
+
+
+# --------------------------------------------------------------------------
+# Part 16: register tiles and the one-warp thread-shape policy
+# --------------------------------------------------------------------------
+
+def register_shape(logical_shape, thread_shape):
+    """Elementwise quotient, requiring positive rank-2 shapes that divide."""
+    for s in (logical_shape, thread_shape):
+        if not isinstance(s, tuple) or len(s) != 2 or any(
+                not isinstance(d, int) or d <= 0 for d in s):
+            raise ValueError("register tiles need positive rank-2 shapes")
+    if any(l % t for l, t in zip(logical_shape, thread_shape)):
+        raise ValueError("logical dims must be divisible by thread dims")
+    return tuple(l // t for l, t in zip(logical_shape, thread_shape))
+
+
+def registers_per_thread(logical_shape, thread_shape):
+    return prod(register_shape(logical_shape, thread_shape))
+
+
+def regtile_coordinate(logical_shape, thread_shape, thread_coord, reg_coord):
+    """Strided ownership: logical = thread + register * thread_shape, per axis."""
+    rs = register_shape(logical_shape, thread_shape)
+    for c, lim in zip(thread_coord, thread_shape):
+        if not (0 <= c < lim):
+            raise ValueError("thread coordinate out of range")
+    for c, lim in zip(reg_coord, rs):
+        if not (0 <= c < lim):
+            raise ValueError("register coordinate out of range")
+    return tuple(t + r * ts for t, r, ts in zip(thread_coord, reg_coord, thread_shape))
+
+
+def dot_thread_shape(logical_shape, max_threads=32):
+    """Divisor pairs with product <= max_threads, largest by (product,
+    smaller side, columns) -- the deterministic one-warp policy."""
+    def divisors(n):
+        return [d for d in range(1, n + 1) if n % d == 0]
+    best = None
+    for a in divisors(logical_shape[0]):
+        for b in divisors(logical_shape[1]):
+            if a * b <= max_threads:
+                key = (a * b, min(a, b), b)
+                if best is None or key > best[0]:
+                    best = (key, (a, b))
+    return best[1]
+
+
+# --------------------------------------------------------------------------
+# Triton LinearLayout: GF(2)-linear maps given by basis vectors
+# --------------------------------------------------------------------------
+
+def gf2_apply(bases, ins):
+    """bases: {in_dim: [basis, ...]} with basis = tuple of out coordinates;
+    ins: {in_dim: value}.  Each set bit i of an input selects basis i of that
+    input dimension; the selected bases are XOR-ed coordinate by coordinate."""
+    n_out = None
+    for vecs in bases.values():
+        for v in vecs:
+            n_out = len(v)
+            break
+    out = [0] * (n_out or 0)
+    for dim, val in ins.items():
+        vecs = bases[dim]
+        if val < 0 or val >= (1 << len(vecs)):
+            raise ValueError(f"input {dim}={val} out of range")
+        for i, v in enumerate(vecs):
+            if (val >> i) & 1:
+                out = [o ^ c for o, c in zip(out, v)]
+    return tuple(out)
+
+
+def _pack(vec, out_bits):
+    """Concatenate the coordinates of an output vector into one integer."""
+    word, shift = 0, 0
+    for c, nb in zip(vec, out_bits):
+        word |= c << shift
+        shift += nb
+    return word
+
+
+def gf2_rank(bases, out_bits):
+    """Rank over GF(2) of the matrix whose columns are all basis vectors,
+    by Gaussian elimination on the packed words."""
+    rows = [_pack(v, out_bits) for vecs in bases.values() for v in vecs]
+    rank = 0
+    for bit in range(sum(out_bits)):
+        pivot = next((r for r in rows if (r >> bit) & 1), None)
+        if pivot is None:
+            continue
+        rows.remove(pivot)
+        rows = [r ^ pivot if (r >> bit) & 1 else r for r in rows]
+        rank += 1
+    return rank
+
+
+def gf2_is_injective(bases, out_bits):
+    return gf2_rank(bases, out_bits) == sum(len(v) for v in bases.values())
+
+
+def gf2_is_surjective(bases, out_bits):
+    return gf2_rank(bases, out_bits) == sum(out_bits)
+
+
+def log2_exact(n):
+    if n <= 0 or n & (n - 1):
+        raise ValueError(f"{n} is not a power of two")
+    return n.bit_length() - 1
+
+
+# --------------------------------------------------------------------------
+# MI355X matrix-core fragments (v_mfma_f32_16x16x32_{f16,bf16})
+# --------------------------------------------------------------------------
+# One wave of 64 lanes.  Operand A (16 rows x 32 k): lane l holds row l % 16,
+# k = 8*(l // 16) + e for its elements e = 0..7.  Operand B (32 k x 16 cols):
+# lane l holds column l % 16 with the same k rule.  Result (16 x 16, fp32):
+# lane l, register r holds row 4*(l // 16) + r, column l % 16.
+# The k rule only has to agree between A and B: the instruction sums over the
+# k slots, so any k order common to both operands gives the same sum.
+
+def mfma16_a(lane, elem):
+    return (lane % 16, 8 * (lane // 16) + elem)          # (row, k)
+
+
+def mfma16_b(lane, elem):
+    return (8 * (lane // 16) + elem, lane % 16)          # (k, col)
+
+
+def mfma16_c(lane, reg):
+    return (4 * (lane // 16) + reg, lane % 16)           # (row, col)
+
+
+# --------------------------------------------------------------------------
+# The workgroup tile of the MI355X kernel
+# --------------------------------------------------------------------------
+# A tile config is (BM, BN, BK, WAVES_M, WAVES_N).  Wave w sits at wave row
+# w // WAVES_N, wave column w % WAVES_N, and owns the sub-tile of
+# WTM = BM / WAVES_M rows by WTN = BN / WAVES_N columns, made of
+# (WTM/16) x (WTN/16) fragments.  The kernel feeds the B tile to the matrix
+# core's row operand and the A tile to its column operand, so a fragment's
+# result row is a C column and vice versa: within fragment (fm, fn), lane l,
+# register r holds C(16*fm + l % 16, 16*fn + 4*(l // 16) + r).  The register
+# index of that value is 4*(fm*(WTN/16) + fn) + r.
+
+def gemm_c_owner(cfg, reg, lane, wave):
+    BM, BN, BK, WM, WN = cfg
+    WTM, WTN = BM // WM, BN // WN
+    FN = WTN // 16
+    r, f = reg % 4, reg // 4
+    fm, fn = f // FN, f % FN
+    frag_row, frag_col = mfma16_c(lane, r)       # (C column, C row) when swapped
+    row = (wave // WN) * WTM + 16 * fm + frag_col
+    col = (wave % WN) * WTN + 16 * fn + frag_row
+    return (row, col)
+
+
+def gemm_regs_per_lane(cfg):
+    BM, BN, BK, WM, WN = cfg
+    return (BM // WM) * (BN // WN) // 64
+
+
+def gemm_c_bases(cfg):
+    """The same ownership written as GF(2) bases {reg, lane, wave} -> (row, col)."""
+    BM, BN, BK, WM, WN = cfg
+    WTM, WTN = BM // WM, BN // WN
+    FM, FN = WTM // 16, WTN // 16
+    reg = [(0, 1), (0, 2)]
+    reg += [(0, 16 << i) for i in range(log2_exact(FN))]
+    reg += [(16 << i, 0) for i in range(log2_exact(FM))]
+    lane = [(1, 0), (2, 0), (4, 0), (8, 0), (0, 4), (0, 8)]
+    wave = [(0, WTN << i) for i in range(log2_exact(WN))]
+    wave += [(WTM << i, 0) for i in range(log2_exact(WM))]
+    return {"reg": reg, "lane": lane, "wave": wave}
+
+
+# --------------------------------------------------------------------------
+# LDS operand tiles: 16-byte chunks, XOR swizzle
+# --------------------------------------------------------------------------
+# An operand tile has R rows (M rows for A, N rows for B) and G = BK/8 chunks
+# of 8 consecutive k per row.  Chunk (r, g) lives in slot r*G + (g XOR s(r))
+# with s(r) = ((r >> (3 - log2 G)) XOR (r >> 3)) mod G.
+
+def lds_swizzle(r, G):
+    shift = 3 - log2_exact(G)
+    return ((r >> shift) ^ (r >> 3)) % G
+
+
+def lds_slot(r, g, G):
+    return r * G + (g ^ lds_swizzle(r, G))
+
+
+def copy_kcontig(R, G, T, t, i):
+    """Chunk moved by thread t at iteration i when the operand is stored with
+    k contiguous: cooperative order (1, 0) over the (R, G) chunk grid.
+    Returns (r, g) or None for an inactive tail lane."""
+    lin = t + i * T
+    if lin >= R * G:
+        return None
+    return coop_coordinate((R, G), (1, 0), lin)
+
+
+def copy_mncontig(R, G, T, t, i):
+    """8x8 block moved by thread t at iteration i when the operand is stored
+    with rows (M or N) contiguous: cooperative order (0, 1) over the
+    (R/8, G) grid of blocks.  Block (rb, g) covers rows 8rb..8rb+7 and
+    k = 8g..8g+7.  Returns (rb, g) or None."""
+    lin = t + i * T
+    if lin >= (R // 8) * G:
+        return None
+    return coop_coordinate((R // 8, G), (0, 1), lin)

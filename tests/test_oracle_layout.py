@@ -1,0 +1,282 @@
+"""Pins of the layout oracle: the values the pages print, and invariants.
+
+Every fixture under tests/golden/ names the page and section it comes from.
+"""
+import itertools
+
+import pytest
+
+from oracle import layout_ref as L
+
+
+# ---- Part 12: cooperative traversal ---------------------------------------
+
+@pytest.mark.parametrize("name", ["coop_a_4x16.json", "coop_b_16x8.json"])
+def test_cooperative_examples(golden, name):
+    g = golden(name)
+    shape, T, order = tuple(g["logical_shape"]), g["threads"], tuple(g["order"])
+    assert L.coop_iterations(shape, T) == g["iterations"]
+    for t, i, lin, coord in g["visits"]:
+        assert L.coop_linear(shape, T, t, i) == lin
+        assert L.coop_coordinate(shape, order, lin) == tuple(coord)
+    # every element covered exactly once
+    seen = [L.coop_coordinate(shape, order, L.coop_linear(shape, T, t, i))
+            for t in range(T) for i in range(g["iterations"])
+            if L.coop_contains(shape, T, t, i)]
+    assert len(seen) == len(set(seen)) == g["size"]
+
+
+def test_cooperative_tail_lanes_inactive():
+    # a tile smaller than the block: only the first `size` threads are active
+    shape, T = (3, 5), 32
+    assert L.coop_iterations(shape, T) == 1
+    active = [t for t in range(T) if L.coop_contains(shape, T, t, 0)]
+    assert active == list(range(15))
+
+
+def test_cooperative_order_column_major():
+    # order (0, 1): axis 0 changes fastest
+    assert L.coop_coordinate((4, 16), (0, 1), 1) == (1, 0)
+    assert L.coop_coordinate((4, 16), (0, 1), 4) == (0, 1)
+
+
+@pytest.mark.parametrize("bad", [
+    lambda: L.coop_iterations((4, 16), 0),
+    lambda: L.coop_iterations((4, 16), 1025),
+    lambda: L.coop_linear((4, 16), 32, 32, 0),
+    lambda: L.coop_linear((4, 16), 32, 0, 2),
+    lambda: L.coop_coordinate((4, 16), (1, 1), 0),
+    lambda: L.coop_coordinate((4, 16), (1, 0), 64),
+    lambda: L.coop_coordinate((4, 0), (1, 0), 0),
+    lambda: L.coop_coordinate((1, 2, 3), (0, 1, 2), 0),
+])
+def test_cooperative_validation(bad):
+    with pytest.raises(ValueError):
+        bad()
+
+
+# ---- Part 12: kernel layouts and projections --------------------------------
+
+def test_kernel_layouts(golden):
+    g = golden("kernel_layouts.json")
+    for c in g["kernel_layouts"]:
+        kl = L.kernel_layout(tuple(c["output"]), tuple(c["thread"]))
+        assert kl == {"rank": c["rank"], "is_rank2": c["is_rank2"],
+                      "threads_per_block": c["threads_per_block"]}
+    for c in g["projections"]:
+        got = L.tile_layout(tuple(c["thread"]), tuple(c["logical"]),
+                            tuple(c["broadcast_axes"]))
+        assert got == tuple(c["thread_axes"])
+    for c in g["rejected_projections"]:
+        with pytest.raises(ValueError):
+            L.tile_layout(tuple(c["thread"]), tuple(c["logical"]))
+
+
+@pytest.mark.parametrize("out,thr", [((4, 8), (4,)), ((64, 64), (32, 64)),
+                                     ((0, 8), (4, 8)), ((4, 8), (4, -8))])
+def test_kernel_layout_rejects(out, thr):
+    with pytest.raises(ValueError):
+        L.kernel_layout(out, thr)
+
+
+# ---- Part 16: register tiles ---------------------------------------------------
+
+def test_regtile_examples(golden):
+    for c in golden("regtile_examples.json")["cases"]:
+        lg, th = tuple(c["logical"]), tuple(c["thread"])
+        assert L.register_shape(lg, th) == tuple(c["register_shape"])
+        assert L.registers_per_thread(lg, th) == c["registers_per_thread"]
+        for reg, logical in c["owns"]:
+            assert L.regtile_coordinate(lg, th, tuple(c["thread_coord"]),
+                                        tuple(reg)) == tuple(logical)
+
+
+@pytest.mark.parametrize("lg,th", [((8, 8), (4, 8)), ((16, 16), (4, 8)),
+                                   ((16, 32), (4, 8)), ((3, 17), (1, 17))])
+def test_regtile_exactly_once(lg, th):
+    rs = L.register_shape(lg, th)
+    owned = [L.regtile_coordinate(lg, th, (ti, tj), (ri, rj))
+             for ti in range(th[0]) for tj in range(th[1])
+             for ri in range(rs[0]) for rj in range(rs[1])]
+    assert len(owned) == len(set(owned)) == lg[0] * lg[1]
+
+
+def test_regtile_rejects():
+    with pytest.raises(ValueError):
+        L.register_shape((8, 8), (3, 8))
+    with pytest.raises(ValueError):
+        L.register_shape((8,), (4,))
+    with pytest.raises(ValueError):
+        L.regtile_coordinate((8, 8), (4, 8), (4, 0), (0, 0))
+    with pytest.raises(ValueError):
+        L.regtile_coordinate((8, 8), (4, 8), (0, 0), (2, 0))
+
+
+def test_dot_policy_table(golden):
+    g = golden("dot_policy.json")
+    for out, threads, regs in g["table"]:
+        th = L.dot_thread_shape(tuple(out), g["max_threads"])
+        assert th == tuple(threads)
+        assert L.register_shape(tuple(out), th) == tuple(regs)
+
+
+# ---- Triton LinearLayout: GF(2) maps ----------------------------------------
+
+def test_gf2_lane_warp_example(golden):
+    g = golden("gf2_examples.json")["lane_warp"]
+    bases = {k: [tuple(v) for v in vs] for k, vs in g["bases"].items()}
+    for ins, out in g["apply"]:
+        assert L.gf2_apply(bases, ins) == tuple(out)
+    # closed form over the whole 4x4 input space
+    for lane, warp in itertools.product(range(4), range(4)):
+        assert L.gf2_apply(bases, {"lane": lane, "warp": warp}) == (lane, lane ^ warp)
+    assert L.gf2_is_injective(bases, g["out_bits"])
+    assert L.gf2_is_surjective(bases, g["out_bits"])
+
+
+def test_gf2_blocked_example(golden):
+    g = golden("gf2_examples.json")["blocked"]
+    bases = {k: [tuple(v) for v in vs] for k, vs in g["bases"].items()}
+    for ins, out in g["apply"]:
+        assert L.gf2_apply(bases, ins) == tuple(out)
+    outs = {L.gf2_apply(bases, {"register": r, "lane": l, "warp": w})
+            for r in range(8) for l in range(32) for w in range(4)}
+    assert len(outs) == g["coverage"]
+    assert L.gf2_rank(bases, g["out_bits"]) == 10
+
+
+def test_gf2_rank_detects_broadcast():
+    # a zero basis is a broadcast: not injective; duplicated basis: rank drops
+    bases = {"lane": [(1, 0), (2, 0)], "warp": [(0, 0)]}
+    assert not L.gf2_is_injective(bases, [2, 1])
+    assert not L.gf2_is_surjective(bases, [2, 1])
+    dup = {"lane": [(1, 1), (1, 1)]}
+    assert L.gf2_rank(dup, [1, 1]) == 1
+
+
+def test_gf2_rank_brute_force():
+    # rank == log2(|image|) on random small layouts
+    import random
+    rnd = random.Random(7)
+    for _ in range(200):
+        n_in = rnd.randint(1, 6)
+        vecs = [(rnd.randrange(8), rnd.randrange(4)) for _ in range(n_in)]
+        bases = {"x": vecs}
+        image = {L.gf2_apply(bases, {"x": v}) for v in range(1 << n_in)}
+        assert 1 << L.gf2_rank(bases, [3, 2]) == len(image)
+
+
+# ---- MI355X maps ---------------------------------------------------------------
+
+def test_mfma16_maps_are_bijections():
+    a = {L.mfma16_a(l, e) for l in range(64) for e in range(8)}
+    b = {L.mfma16_b(l, e) for l in range(64) for e in range(8)}
+    c = {L.mfma16_c(l, r) for l in range(64) for r in range(4)}
+    assert a == {(i, k) for i in range(16) for k in range(32)}
+    assert b == {(k, j) for k in range(32) for j in range(16)}
+    assert c == {(i, j) for i in range(16) for j in range(16)}
+    # A and B pair the same k in the same (lane group, element) slot
+    for l in range(64):
+        for e in range(8):
+            assert L.mfma16_a(l, e)[1] == L.mfma16_b(l, e)[0]
+
+
+TILE_CONFIGS = [(16, 64, 32, 1, 1), (64, 64, 64, 2, 2), (128, 128, 64, 2, 2),
+                (256, 256, 64, 2, 2), (256, 128, 64, 2, 2), (128, 256, 64, 2, 2),
+                (256, 256, 64, 2, 4)]
+
+
+@pytest.mark.parametrize("cfg", TILE_CONFIGS)
+def test_gemm_c_owner_exactly_once(cfg):
+    BM, BN, BK, WM, WN = cfg
+    regs = L.gemm_regs_per_lane(cfg)
+    owned = [L.gemm_c_owner(cfg, r, l, w)
+             for w in range(WM * WN) for l in range(64) for r in range(regs)]
+    assert len(owned) == len(set(owned)) == BM * BN
+    assert all(0 <= i < BM and 0 <= j < BN for i, j in owned)
+
+
+@pytest.mark.parametrize("cfg", TILE_CONFIGS)
+def test_gemm_c_owner_is_gf2_linear(cfg):
+    BM, BN, BK, WM, WN = cfg
+    bases = L.gemm_c_bases(cfg)
+    out_bits = [L.log2_exact(BM), L.log2_exact(BN)]
+    assert L.gf2_is_injective(bases, out_bits) and L.gf2_is_surjective(bases, out_bits)
+    regs = L.gemm_regs_per_lane(cfg)
+    for w in range(WM * WN):
+        for l in range(64):
+            for r in range(regs):
+                assert L.gemm_c_owner(cfg, r, l, w) == L.gf2_apply(
+                    bases, {"reg": r, "lane": l, "wave": w})
+
+
+def test_tiny_tile_owner_values():
+    # the 16x64 tile over one wave: lane 17 (row 1, column group 1), reg 6
+    # (fragment 1, register 2) -> C(1, 16 + 4 + 2)
+    assert L.gemm_c_owner((16, 64, 32, 1, 1), 6, 17, 0) == (1, 22)
+    assert L.gemm_regs_per_lane((16, 64, 32, 1, 1)) == 16
+
+
+@pytest.mark.parametrize("R,G", [(16, 4), (64, 4), (64, 8), (256, 8), (128, 8)])
+def test_lds_slot_bijective(R, G):
+    slots = {L.lds_slot(r, g, G) for r in range(R) for g in range(G)}
+    assert slots == set(range(R * G))
+
+
+def _conflicts(addresses, banks=32):
+    """Worst number of distinct 16-byte chunks sharing a bank group among
+    lanes that a 16-byte-per-lane LDS access serves in one cycle."""
+    worst = 1
+    lanes_per_cycle = banks * 4 // 16
+    for base in range(0, len(addresses), lanes_per_cycle):
+        grp = addresses[base:base + lanes_per_cycle]
+        col = {}
+        for a in grp:
+            col.setdefault((a // 16) % lanes_per_cycle, set()).add(a)
+        worst = max(worst, max(len(v) for v in col.values()))
+    return worst
+
+
+@pytest.mark.parametrize("R,G", [(64, 4), (256, 8), (128, 8)])
+def test_lds_swizzle_conflict_free_reads(R, G):
+    # fragment read: 16 consecutive rows, one k chunk, per 16 lanes
+    for r0 in range(0, R, 16):
+        for g in range(G):
+            addrs = [16 * L.lds_slot(r0 + (l % 16), g, G) for l in range(16)]
+            assert _conflicts(addrs, 32) == 1
+
+
+@pytest.mark.parametrize("R,G,T", [(256, 8, 256), (64, 4, 64), (128, 8, 256)])
+def test_lds_swizzle_conflict_free_writes(R, G, T):
+    # k-contiguous copy: each thread writes its chunk (r, g)
+    for i in range(-(-R * G // T)):
+        addrs = []
+        for t in range(T):
+            c = L.copy_kcontig(R, G, T, t, i)
+            if c is not None:
+                addrs.append(16 * L.lds_slot(c[0], c[1], G))
+        assert _conflicts(addrs, 32) == 1
+    # row-contiguous copy: block (rb, g), write j lands on row 8rb + j.  With
+    # four chunks per row (64-byte rows) a bank window holds two rows, and the
+    # eight lanes of a cycle all write rows of one parity: two-way at best.
+    worst = 1 if G == 8 else 2
+    for i in range(-(-(R // 8) * G // T)):
+        for j in range(8):
+            addrs = []
+            for t in range(T):
+                c = L.copy_mncontig(R, G, T, t, i)
+                if c is not None:
+                    addrs.append(16 * L.lds_slot(8 * c[0] + j, c[1], G))
+            assert _conflicts(addrs, 32) <= worst
+
+
+def test_copy_maps_cover_tile():
+    for R, G, T in [(256, 8, 256), (16, 4, 64), (64, 4, 64)]:
+        it = -(-R * G // T)
+        got = [L.copy_kcontig(R, G, T, t, i) for t in range(T) for i in range(it)]
+        got = [x for x in got if x is not None]
+        assert sorted(got) == [(r, g) for r in range(R) for g in range(G)]
+        it = -(-(R // 8) * G // T)
+        got = [L.copy_mncontig(R, G, T, t, i) for t in range(T) for i in range(it)]
+        got = [x for x in got if x is not None]
+        assert sorted(got) == [(rb, g) for rb in range(R // 8) for g in range(G)]

@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no arithmetic of the method: it only names the workloads
+(shapes, strides, storage order, value distribution, epilogue flags) and
+draws their raw 16-bit operand buffers from a seeded generator.  Both the
+oracle and the HIP path are fed these same bytes.
+
+Recipe (one generator per tensor): numpy PCG64 seeded with
+[config_seed, tensor_id]; tensor ids A=0, B=1, bias=2, residual=3.  Values are
+drawn in float64 in *storage* order (A^T order when A is stored transposed),
+rounded to the 16-bit type (float16: numpy's float64->float16 conversion;
+bfloat16: float64->float32, then round-to-nearest-even on the float32 bits)
+and written into a padded buffer whose leading-dimension padding holds NaN,
+so that any read of the padding poisons the result.
+"""
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+F16 = 1
+BF16 = 2
+DTYPE_NAMES = {F16: "f16", BF16: "bf16"}
+
+TENSOR_A, TENSOR_B, TENSOR_BIAS, TENSOR_R = 0, 1, 2, 3
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    opA: int = 0            # 0: A stored [M][lda], 1: A stored as A^T [K][lda]
+    opB: int = 0            # 0: B stored [K][ldb], 1: B stored as B^T [N][ldb]
+    lda: Optional[int] = None
+    ldb: Optional[int] = None
+    ldc: Optional[int] = None
+    dtype: int = F16
+    bias: bool = False
+    relu: bool = False
+    residual: bool = False
+    dist: str = "uniform"   # uniform | normal | ternary (exact-arithmetic mode)
+    scale: float = 1.0      # half-width for uniform, divisor for normal
+    seed: int = 0
+    tile: Optional[tuple] = None  # explicit (BM, BN, BK) tile, or None
+
+    @property
+    def a_rows(self):
+        return self.K if self.opA else self.M
+
+    @property
+    def a_cols(self):
+        return self.M if self.opA else self.K
+
+    @property
+    def b_rows(self):
+        return self.N if self.opB else self.K
+
+    @property
+    def b_cols(self):
+        return self.K if self.opB else self.N
+
+    @property
+    def lda_(self):
+        return self.lda if self.lda is not None else self.a_cols
+
+    @property
+    def ldb_(self):
+        return self.ldb if self.ldb is not None else self.b_cols
+
+    @property
+    def ldc_(self):
+        return self.ldc if self.ldc is not None else self.N
+
+    @property
+    def ldr_(self):
+        return self.N
+
+    @property
+    def flops(self):
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self):
+        b = 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
+        if self.bias:
+            b += 2 * self.N
+        if self.residual:
+            b += 2 * self.M * self.N
+        return b
+
+
+# The five workloads of the spec configuration sheet.
+TINY = Workload("tiny", 64, 64, 32, dtype=F16, dist="uniform", scale=1.0,
+                seed=1, tile=(16, 64, 32))
+SQUARE = Workload("square", 4096, 4096, 4096, dtype=F16, dist="normal",
+                  scale=8.0, seed=2)
+EPILOGUE = Workload("epilogue", 8192, 8192, 4096, dtype=BF16, bias=True,
+                    relu=True, residual=True, dist="uniform", scale=1.0, seed=3)
+RAGGED = Workload("ragged", 4000, 3072, 5000, opA=1, lda=5064, ldb=3136,
+                  dtype=F16, dist="uniform", scale=0.5, seed=4)
+SKINNY = Workload("skinny", 16, 16384, 16384, dtype=F16, dist="normal",
+                  scale=128.0, seed=5)
+
+CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY)}
+
+
+def shrink(w: Workload, M=None, N=None, K=None, **kw) -> Workload:
+    """A smaller workload with the same storage scheme, dtype, epilogue and
+    distribution; leading dimensions keep the same padding beyond the
+    contiguous extent as the original."""
+    M = M or w.M
+    N = N or w.N
+    K = K or w.K
+    new = replace(w, M=M, N=N, K=K, lda=None, ldb=None, ldc=None, **kw)
+    pad_a = (w.lda_ - w.a_cols) if w.lda is not None else 0
+    pad_b = (w.ldb_ - w.b_cols) if w.ldb is not None else 0
+    return replace(new, lda=new.a_cols + pad_a if pad_a else None,
+                   ldb=new.b_cols + pad_b if pad_b else None)
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 bits, to nearest with ties to even."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x32)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def to_bits(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == F16:
+        return np.ascontiguousarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32))
+
+
+NAN_BITS = {F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0)}
+
+
+def _draw(w: Workload, tensor_id: int, rows: int, cols: int) -> np.ndarray:
+    rng = np.random.default_rng([w.seed, tensor_id])
+    shape = (rows, cols)
+    if w.dist == "uniform":
+        x = rng.uniform(-w.scale, w.scale, size=shape)
+    elif w.dist == "normal":
+        x = rng.standard_normal(size=shape) / w.scale
+    elif w.dist == "ternary":
+        # exact-arithmetic mode: operands in {-1, 0, 1}, epilogue terms in {-2..2}
+        lim = 2 if tensor_id in (TENSOR_BIAS, TENSOR_R) else 1
+        x = rng.integers(-lim, lim + 1, size=shape).astype(np.float64)
+    else:
+        raise ValueError(w.dist)
+    return x
+
+
+def _padded(w: Workload, tensor_id: int, rows: int, cols: int, ld: int) -> np.ndarray:
+    bits = to_bits(_draw(w, tensor_id, rows, cols), w.dtype)
+    buf = np.full((rows, ld), NAN_BITS[w.dtype], dtype=np.uint16)
+    buf[:, :cols] = bits
+    return buf.reshape(-1)
+
+
+def make_inputs(w: Workload) -> dict:
+    """Raw host buffers (flat uint16) for a workload: A, B and, if enabled,
+    bias [N] and residual [M, N] (leading dimension N)."""
+    out = {
+        "A": _padded(w, TENSOR_A, w.a_rows, w.a_cols, w.lda_),
+        "B": _padded(w, TENSOR_B, w.b_rows, w.b_cols, w.ldb_),
+        "bias": None,
+        "R": None,
+    }
+    if w.bias:
+        out["bias"] = _padded(w, TENSOR_BIAS, 1, w.N, w.N)
+    if w.residual:
+        out["R"] = _padded(w, TENSOR_R, w.M, w.N, w.N)
+    return out
