@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the register-tile GEMM on one MI355X.
+
+A step is one call of the whole hot path -- validation, tile selection and
+the single fused GEMM kernel -- on the workload's operands, already resident
+in HBM.  The default workload is the 4096^3 fp16 GEMM (fp32 accumulation,
+fp16 output) with inputs N(0,1)/8.  Prints ONE JSON line:
+
+  value        whole-job TFLOP/s = 2*M*N*K / average step time
+  roofline     the GEMM kernel against the dense fp16 matrix-core peak
+               (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk), with
+               HBM traffic from committed rocprofv3 counters when they were
+               taken on the current kernel source
+  cpu_baseline the oracle (plain fp64 C, all host cores) timed on a bounded
+               row sample of the same workload, scaled to TFLOP/s
+  parity       the GPU result on the same sampled rows against the oracle
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (fp16→fp32 acc) at 4096³ + % of MFMA peak (rocprof)"
+PEAK_TFLOPS = {1: 2516.6, 2: 2516.6}   # dense f16 / bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def csrc_digest():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "thread_register_tile_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per launch from committed counter runs, only if they were
+    taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("csrc_digest") != csrc_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square")
+    ap.add_argument("--tile", default=None, help="BM,BN,BK")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "the path has no multi-GPU sharding.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import thread_register_tile_amd as trt
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    trt.lib()  # fail loudly if the HIP library is missing
+
+    w = W.CONFIGS[args.workload]
+    tile = tuple(int(x) for x in args.tile.split(",")) if args.tile else w.tile
+    host = W.make_inputs(w)
+    dev = lambda b: None if b is None else torch.from_numpy(b.view(np.int16)).cuda()
+    A, B, bias, R = dev(host["A"]), dev(host["B"]), dev(host["bias"]), dev(host["R"])
+    C = torch.empty(w.M * w.ldc_, dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step():
+        trt.gemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, w.opA, B.data_ptr(), w.ldb_, w.opB,
+                     C.data_ptr(), w.ldc_, w.dtype, w.dtype,
+                     bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
+                     residual=R.data_ptr() if R is not None else 0,
+                     ldr=w.ldr_ if R is not None else 0, tile=tile, stream=sptr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: events on the launch stream bracket exactly `steps` calls
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-launch durations on the same stream, for the kernel average
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(args.steps, 20))]
+    for a, b in evs:
+        a.record(stream); step(); b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    achieved = w.flops / (kern_ms * 1e-3) / 1e12
+    traffic = committed_traffic(w.name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
+                "traffic": traffic,
+                "algorithmic_bytes": w.algorithmic_bytes,
+                "kernel_ms": round(kern_ms, 5)}
+    if w.name == "skinny":
+        gbs = w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9
+        roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        # calibrate on a few rows, then size the sample to the time budget
+        t0 = time.perf_counter()
+        oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_, w.opB,
+                          w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
+                          ldr=w.ldr_ if host["R"] is not None else 0,
+                          m_range=(0, min(threads, w.M)), threads=threads)
+        t_cal = time.perf_counter() - t0
+        rows = int(min(w.M, max(threads, min(threads, w.M) * args.cpu_seconds / max(t_cal, 1e-3))))
+        rows = max(1, rows - rows % max(1, min(threads, rows)))
+        t0 = time.perf_counter()
+        ref = oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,
+                                w.opB, w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
+                                ldr=w.ldr_ if host["R"] is not None else 0,
+                                m_range=(0, rows), threads=threads)
+        t_cpu = time.perf_counter() - t0
+        cpu_tflops = 2.0 * rows * w.N * w.K / t_cpu / 1e12
+        cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, fp64 oracle incl. "
+                         f"epilogue), {t_cpu:.1f} s"}
+        Cg = C.cpu().numpy().view(np.uint16).reshape(w.M, w.ldc_)[:rows, :w.N]
+        rep = oracle.accept(np.ascontiguousarray(Cg), ref, w.dtype)
+        parity = {"rows": rows, "ok": rep["ok"], "max_abs": rep["max_abs"],
+                  "frob_rel": rep["frob_rel"], "bit_match": rep["bit_match"]}
+
+    name = {"square": "square 4096x4096x4096 f16 -> f16, fp32 accumulate"}.get(
+        w.name, f"{w.name} {w.M}x{w.N}x{w.K}")
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W.DTYPE_NAMES[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "opA": w.opA,
+                   "opB": w.opB, "lda": w.lda_, "ldb": w.ldb_, "ldc": w.ldc_,
+                   "epilogue": {"bias": w.bias, "relu": w.relu, "residual": w.residual},
+                   "tile": list(tile) if tile else "auto", "csrc_digest": csrc_digest()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

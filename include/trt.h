@@ -1,0 +1,214 @@
+/*
+ * trt.h -- C ABI of the MI355X (gfx950) register-tile GEMM library, libtrt.so.
+ *
+ * One operation, as defined by the NineToothed page "Named layouts" (the GEMM
+ * arrangement at the top of the page, and sections "Contract" and "Runtime
+ * and compilation"):
+ *
+ *     C[M,N] = epilogue( A[M,K] . B[K,N] )
+ *
+ * computed by a grid of workgroups, each owning one logical [BM,BN] tile of C
+ * and consuming [BM,BK] / [BK,BN] operand tiles per K step.  Products are
+ * accumulated in fp32 and cast once, at the end, to the output dtype.  The
+ * epilogue, when requested, is  y = relu(acc + bias[n]) + R[m,n]  with each
+ * term optional, evaluated in fp32 before the single cast.
+ *
+ * The library has no global mutable state and never allocates: all buffers
+ * belong to the caller.  Every call validates its arguments on the host
+ * before any device work (an error leaves C untouched) and then enqueues
+ * exactly one kernel on the caller's stream; the result is valid once that
+ * stream has synchronised.  No pointer is kept after a call returns.
+ */
+#ifndef TRT_H
+#define TRT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRT_ABI_VERSION 1
+
+/* Status codes.  Every entry point returns one of these. */
+typedef enum {
+  TRT_OK = 0,
+  TRT_ERR_SIZE = 1,        /* M, N or K < 1, or an extent that overflows int64 */
+  TRT_ERR_STRIDE = 2,      /* an input leading dimension < 1, or ldc < N       */
+  TRT_ERR_NULL = 3,        /* A, B or C is NULL (or a required output buffer)  */
+  TRT_ERR_ALIGN = 4,       /* a pointer not aligned to its 2-byte element      */
+  TRT_ERR_OVERLAP = 5,     /* C's byte range meets an input's byte range       */
+  TRT_ERR_DTYPE = 6,       /* unsupported input/output dtype combination       */
+  TRT_ERR_UNSUPPORTED = 7, /* no compiled kernel for the requested tile / map  */
+  TRT_ERR_HIP = 8,         /* the HIP runtime reported an error (see message)  */
+  TRT_ERR_ARG = 9          /* any other invalid argument (op flag, map id...)  */
+} trt_status;
+
+/* Element types.  Inputs and outputs are IEEE binary16 or bfloat16. */
+typedef enum { TRT_F16 = 1, TRT_BF16 = 2 } trt_dtype;
+
+/* Storage of an operand.  An operand is never transposed implicitly
+ * ("Named layouts", section "Contract": a transpose is explicit):
+ *   A, TRT_OP_N: A(m,k) = A[m*lda + k]   (row-major [M][lda])
+ *   A, TRT_OP_T: A(m,k) = A[k*lda + m]   (A^T stored row-major [K][lda])
+ *   B, TRT_OP_N: B(k,n) = B[k*ldb + n]   (row-major [K][ldb])
+ *   B, TRT_OP_T: B(k,n) = B[n*ldb + k]   (B^T stored row-major [N][ldb])
+ * C(m,n) = C[m*ldc + n] and R(m,n) = R[m*ldr + n].  Leading dimensions are
+ * in elements, not bytes. */
+typedef enum { TRT_OP_N = 0, TRT_OP_T = 1 } trt_op;
+
+/* Optional same-output-domain postprocessing ("Named layouts", section
+ * "Contract": bias / ReLU / residual on the output's own domain; a column
+ * bias spans the n axis only and broadcasts over m).  bias: [N] elements of
+ * out_dtype, or NULL.  residual: R(m,n) = residual[m*ldr + n] of out_dtype, or
+ * NULL.  relu != 0 applies max(y, 0) after the bias and before the
+ * residual.  Passing NULL for the whole struct means a plain GEMM. */
+typedef struct {
+  const void* bias;
+  int32_t relu;
+  const void* residual;
+  int64_t ldr;
+} trt_epilogue;
+
+/* A workgroup tile: the logical [bm, bn] output tile and the K step bk.
+ * The physical thread shape (wavefronts of 64 lanes) and the per-lane
+ * register shape of each compiled tile are reported by trt_tile_at(). */
+typedef struct {
+  int32_t bm, bn, bk;
+} trt_tile;
+
+/*
+ * trt_gemm -- C = epilogue(A . B) with a tile chosen by the library.
+ *
+ * M, N, K >= 1 ("Named layouts", section "Runtime and compilation": logical
+ * sizes are positive).  lda, ldb and (when a residual is given) ldr >= 1:
+ * input strides are positive; input rows may overlap.  ldc >= N: output
+ * writes never overlap each other.  C's byte range must not meet the byte
+ * range of A, B, bias or residual -- an in-place residual is rejected, since
+ * safety that cannot be proven is an error.  A, B, C must be non-NULL and all
+ * pointers 2-byte aligned.  in_dtype must equal out_dtype (TRT_F16 or
+ * TRT_BF16).  Elements of C outside [0,M) x [0,N) (the ldc padding) are never
+ * written, and elements of A and B outside the logical operands (the lda/ldb
+ * padding) are never read.
+ *
+ * stream: a hipStream_t (NULL = the default stream).  The call enqueues one
+ * kernel and returns; TRT_ERR_HIP means the launch failed, with the runtime's
+ * message in trt_last_error().  Pointers are device (or device-accessible)
+ * addresses owned by the caller.
+ */
+trt_status trt_gemm(int64_t M, int64_t N, int64_t K,
+                    const void* A, int64_t lda, int32_t opA,
+                    const void* B, int64_t ldb, int32_t opB,
+                    void* C, int64_t ldc,
+                    int32_t in_dtype, int32_t out_dtype,
+                    const trt_epilogue* epi, void* stream);
+
+/*
+ * trt_gemm_tiled -- trt_gemm with an explicit workgroup tile.  tile must name
+ * a compiled instance (see trt_tile_at); otherwise TRT_ERR_UNSUPPORTED and
+ * nothing is enqueued.  tile == NULL behaves as trt_gemm.
+ */
+trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, int32_t opA,
+                          const void* B, int64_t ldb, int32_t opB,
+                          void* C, int64_t ldc,
+                          int32_t in_dtype, int32_t out_dtype,
+                          const trt_epilogue* epi, const trt_tile* tile,
+                          void* stream);
+
+/*
+ * trt_validate -- the host-side checks of trt_gemm_tiled, alone: returns the
+ * status the call would return before any device work.  Makes no HIP call,
+ * dereferences no pointer, and is safe on a machine without a GPU.
+ */
+trt_status trt_validate(int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda, int32_t opA,
+                        const void* B, int64_t ldb, int32_t opB,
+                        const void* C, int64_t ldc,
+                        int32_t in_dtype, int32_t out_dtype,
+                        const trt_epilogue* epi, const trt_tile* tile);
+
+/* Number of compiled workgroup tiles. */
+int32_t trt_tile_count(void);
+
+/*
+ * trt_tile_at -- describe compiled tile i (0 <= i < trt_tile_count()):
+ * its logical tile, its physical thread shape as waves_m x waves_n
+ * wavefronts of 64 lanes, and the accumulator registers each lane owns
+ * ("My Triton From Scratch, Part 16: Register Tiles", section "Three
+ * coordinate spaces": logical shape vs. thread shape vs. register shape).
+ * Any output pointer may be NULL.  TRT_ERR_ARG if i is out of range.
+ */
+trt_status trt_tile_at(int32_t i, trt_tile* tile, int32_t* waves_m,
+                       int32_t* waves_n, int32_t* regs_per_lane);
+
+/* Maps that trt_layout_dump can enumerate. */
+typedef enum {
+  /* C ownership: input index x = (wave*64 + lane)*REGS + reg, output
+   * (row, col) of the tile element that accumulator register holds. */
+  TRT_MAP_C_OWNER = 0,
+  /* LDS operand slot: x = row*G + g (G = bk/8 chunks of 8 k per row),
+   * output (slot, 0): the swizzled 16-byte chunk slot of chunk (row, g). */
+  TRT_MAP_LDS_SLOT_A = 1,
+  TRT_MAP_LDS_SLOT_B = 2,
+  /* Cooperative copy, k-contiguous operand rows of the A tile:
+   * x = iteration*THREADS + thread, output (row, g) of the 16-byte chunk
+   * it moves, or (-1, -1) for an inactive tail lane. */
+  TRT_MAP_COPY_KCONTIG_A = 3,
+  /* Cooperative copy, row-contiguous storage of the A tile: output (rb, g)
+   * of the 8x8 block it moves (rows 8rb..8rb+7, k = 8g..8g+7), or (-1,-1). */
+  TRT_MAP_COPY_MNCONTIG_A = 4,
+  TRT_MAP_COPY_KCONTIG_B = 5,
+  TRT_MAP_COPY_MNCONTIG_B = 6
+} trt_map;
+
+/*
+ * trt_layout_dump -- evaluate map `map_id` of compiled tile `tile` on the
+ * device, with the very device functions the GEMM kernel uses, for inputs
+ * x = 0..n-1, writing rows[x] and cols[x] (device buffers of n int32, owned
+ * by the caller).  n must equal trt_layout_size(map_id, tile).  Enqueued on
+ * `stream`.
+ */
+trt_status trt_layout_dump(int32_t map_id, const trt_tile* tile,
+                           int32_t* rows, int32_t* cols, int64_t n,
+                           void* stream);
+
+/* The same maps evaluated on the host (no HIP call; host buffers). */
+trt_status trt_layout_dump_host(int32_t map_id, const trt_tile* tile,
+                                int32_t* rows, int32_t* cols, int64_t n);
+
+/* Number of inputs of map `map_id` for tile `tile`, or -1 if unsupported. */
+int64_t trt_layout_size(int32_t map_id, const trt_tile* tile);
+
+/*
+ * trt_layout_rank -- GF(2) rank of the C ownership map of a compiled tile
+ * (the rank of its (register, lane, wave) -> (row, col) basis matrix), and
+ * the number of its input and output bits.  Exactly-once ownership means
+ * rank == in_bits == out_bits ("Triton LinearLayout", section
+ * "Surjectivity, injectivity, and broadcasts").  Host only.
+ */
+trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank,
+                           int32_t* in_bits, int32_t* out_bits);
+
+/*
+ * trt_mfma_probe -- run one 16x16x32 matrix-core instruction on one wave:
+ * lane l passes a[l*8 .. l*8+7] as its A-operand register and b[l*8 ..] as
+ * its B-operand register (raw 16-bit values of `dtype`), starting from a zero
+ * accumulator, and writes its 4 result registers to c[l*4 .. l*4+3] (fp32).
+ * a, b, c are device buffers of 512, 512 and 256 elements.  Used to confirm
+ * the hardware fragment layout the ownership map is built on.
+ */
+trt_status trt_mfma_probe(int32_t dtype, const void* a, const void* b,
+                          float* c, void* stream);
+
+/* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
+int32_t trt_abi_version(void);
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char* trt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRT_H */

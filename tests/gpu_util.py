@@ -1,0 +1,100 @@
+"""Test helpers: move seeded host buffers to the GPU, call the library through
+its C ABI, read results back with guard bands, and judge them with the oracle.
+"""
+import numpy as np
+import torch
+
+import oracle
+import thread_register_tile_amd as trt
+import workloads as W
+
+GUARD = 2048            # elements of sentinel before and after C
+SENTINEL = 0x7BAD       # a finite f16/bf16 pattern the kernel never writes by chance
+
+
+def to_dev(bits):
+    if bits is None:
+        return None
+    return torch.from_numpy(bits.view(np.int16)).to("cuda")
+
+
+class Run:
+    """One GEMM call on device copies of a workload's host buffers."""
+
+    def __init__(self, w: W.Workload, inputs=None, ldc=None):
+        self.w = w
+        self.host = inputs if inputs is not None else W.make_inputs(w)
+        self.A = to_dev(self.host["A"])
+        self.B = to_dev(self.host["B"])
+        self.bias = to_dev(self.host["bias"])
+        self.R = to_dev(self.host["R"])
+        self.ldc = ldc or w.ldc_
+        n_c = (w.M - 1) * self.ldc + w.N
+        self.Cbuf = torch.full((n_c + 2 * GUARD,), SENTINEL, dtype=torch.int16, device="cuda")
+
+    def c_ptr(self):
+        return self.Cbuf.data_ptr() + 2 * GUARD
+
+    def launch(self, tile=None):
+        w = self.w
+        trt.gemm_raw(w.M, w.N, w.K, self.A.data_ptr(), w.lda_, w.opA, self.B.data_ptr(),
+                     w.ldb_, w.opB, self.c_ptr(), self.ldc, w.dtype, w.dtype,
+                     bias=self.bias.data_ptr() if self.bias is not None else 0,
+                     relu=w.relu,
+                     residual=self.R.data_ptr() if self.R is not None else 0,
+                     ldr=w.ldr_ if self.R is not None else 0,
+                     tile=tile if tile is not None else w.tile,
+                     stream=torch.cuda.current_stream().cuda_stream)
+
+    def result(self):
+        """C as an (M, N) uint16 array; asserts guards and ldc padding intact."""
+        torch.cuda.synchronize()
+        buf = self.Cbuf.cpu().numpy().view(np.uint16)
+        w = self.w
+        assert (buf[:GUARD] == SENTINEL).all(), "write before C"
+        assert (buf[-GUARD:] == SENTINEL).all(), "write after C"
+        body = buf[GUARD:-GUARD]
+        full = np.full(w.M * self.ldc, SENTINEL, dtype=np.uint16)
+        full[:body.size] = body
+        full = full.reshape(w.M, self.ldc)
+        if self.ldc > w.N:
+            pad = full[:-1, w.N:] if w.M > 1 else full[:0, w.N:]
+            assert (pad == SENTINEL).all(), "write into ldc padding"
+        return np.ascontiguousarray(full[:, :w.N])
+
+
+def oracle_args(w: W.Workload, host):
+    return dict(M=w.M, N=w.N, K=w.K, A=host["A"], lda=w.lda_, opA=w.opA, B=host["B"],
+                ldb=w.ldb_, opB=w.opB, in_dtype=w.dtype, bias=host["bias"], relu=w.relu,
+                R=host["R"], ldr=w.ldr_ if host["R"] is not None else 0)
+
+
+def reference_block(w, host, m_range=None, n_range=None):
+    return oracle.gemm_block(**oracle_args(w, host), m_range=m_range, n_range=n_range)
+
+
+def reference_cells(w, host, ms, ns):
+    return oracle.gemm_cells(**oracle_args(w, host), ms=ms, ns=ns)
+
+
+def assert_accept(C_bits, Cref, dtype, exact=False, what=""):
+    rep = oracle.accept(C_bits, Cref, dtype)
+    assert rep["ok"], f"{what}: {rep}"
+    if exact:
+        assert rep["bit_match"] == 1.0, f"{what}: exact mode not bit-exact: {rep}"
+    return rep
+
+
+def sample_cells(w, n_random, seed=0):
+    """Random cells plus every corner and the last row / column of the domain."""
+    rng = np.random.default_rng(seed)
+    ms = list(rng.integers(0, w.M, n_random))
+    ns = list(rng.integers(0, w.N, n_random))
+    for m in (0, w.M - 1):
+        for n in (0, w.N - 1):
+            ms.append(m); ns.append(n)
+    for i in range(min(w.N, 64)):
+        ms.append(w.M - 1); ns.append(w.N - 1 - i)
+    for i in range(min(w.M, 64)):
+        ms.append(w.M - 1 - i); ns.append(w.N - 1)
+    return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)

@@ -1,0 +1,179 @@
+"""CPU tests of the C ABI: exports, host-side validation, host layout maps.
+
+No compute call reaches the GPU here: trt_validate, trt_layout_dump_host,
+trt_layout_rank and the error paths of trt_gemm all return before any HIP
+call.  The layout maps of the library are compared element by element with
+the layout oracle.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import thread_register_tile_amd as trt
+from oracle import layout_ref as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "trt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(trt_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "trt_gemm" in names and "trt_validate" in names and len(names) >= 12
+    lib = trt.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    hdr = open(os.path.join(ROOT, "include", "trt.h")).read()
+    v = int(re.search(r"#define TRT_ABI_VERSION (\d+)", hdr).group(1))
+    assert trt.abi_version() == v
+
+
+# ---- validation (NineToothed "Named layouts", "Runtime and compilation") ---------
+
+BASE = 1 << 20     # fake, well-separated 256-byte aligned addresses: never dereferenced
+
+
+def args(**kw):
+    a = dict(M=64, N=64, K=32, A=BASE, lda=32, opA=0, B=BASE * 2, ldb=64, opB=0,
+             C=BASE * 3, ldc=64, in_dtype=trt.F16, out_dtype=trt.F16)
+    a.update(kw)
+    return a
+
+
+def status(tile=None, bias=0, relu=False, residual=0, ldr=0, **kw):
+    a = args(**kw)
+    return trt.validate_raw(a["M"], a["N"], a["K"], a["A"], a["lda"], a["opA"], a["B"],
+                            a["ldb"], a["opB"], a["C"], a["ldc"], a["in_dtype"],
+                            a["out_dtype"], bias=bias, relu=relu, residual=residual,
+                            ldr=ldr, tile=tile)
+
+
+def test_valid_call():
+    assert status() == trt.OK
+    assert status(bias=BASE * 4, relu=True, residual=BASE * 5, ldr=64) == trt.OK
+    assert status(opA=1, lda=64, opB=1, ldb=32) == trt.OK
+    assert status(tile=(16, 64, 32)) == trt.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), trt.ERR_SIZE), (dict(N=-1), trt.ERR_SIZE), (dict(K=0), trt.ERR_SIZE),
+    (dict(M=1 << 31), trt.ERR_SIZE),
+    (dict(lda=0), trt.ERR_STRIDE), (dict(ldb=-5), trt.ERR_STRIDE),
+    (dict(ldc=63), trt.ERR_STRIDE),
+    (dict(A=0), trt.ERR_NULL), (dict(B=0), trt.ERR_NULL), (dict(C=0), trt.ERR_NULL),
+    (dict(A=BASE + 1), trt.ERR_ALIGN), (dict(C=BASE * 3 + 1), trt.ERR_ALIGN),
+    (dict(in_dtype=3, out_dtype=3), trt.ERR_DTYPE),
+    (dict(in_dtype=trt.F16, out_dtype=trt.BF16), trt.ERR_DTYPE),
+    (dict(opA=2), trt.ERR_ARG), (dict(opB=-1), trt.ERR_ARG),
+    # C overlapping an input: any byte in common is an error
+    (dict(C=BASE + 64 * 2), trt.ERR_OVERLAP),
+    (dict(C=BASE * 2 - 2), trt.ERR_OVERLAP),
+])
+def test_rejections(kw, code):
+    assert status(**kw) == code
+    assert trt.last_error() != ""
+
+
+def test_overlap_boundaries_are_exact():
+    # A spans [BASE, BASE + 2*(63*32 + 32)) = [BASE, BASE + 4096)
+    assert status(C=BASE + 4096) == trt.OK
+    assert status(C=BASE + 4094) == trt.ERR_OVERLAP
+    # C spans 2*(63*ldc + 64) bytes; ending exactly at A's start is fine
+    c_bytes = 2 * (63 * 64 + 64)
+    assert status(C=BASE - c_bytes) == trt.OK
+    assert status(C=BASE - c_bytes + 2) == trt.ERR_OVERLAP
+    # transposed A spans (K-1)*lda + M elements
+    assert status(opA=1, lda=64, C=BASE + 2 * (31 * 64 + 64)) == trt.OK
+    assert status(opA=1, lda=64, C=BASE + 2 * (31 * 64 + 64) - 2) == trt.ERR_OVERLAP
+
+
+def test_in_place_residual_rejected():
+    assert status(residual=BASE * 3, ldr=64) == trt.ERR_OVERLAP
+    assert status(bias=BASE * 3 + 2) == trt.ERR_OVERLAP
+    assert status(residual=BASE * 5, ldr=0) == trt.ERR_STRIDE
+
+
+def test_overlapping_input_rows_are_legal():
+    # lda smaller than the row: rows overlap, which is fine for inputs
+    assert status(lda=1) == trt.OK
+
+
+def test_unknown_tile_rejected():
+    assert status(tile=(48, 64, 32)) == trt.ERR_UNSUPPORTED
+
+
+def test_gemm_errors_return_before_device_work():
+    # invalid calls never reach HIP, so they are safe without a GPU
+    with pytest.raises(trt.TrtError) as e:
+        trt.gemm_raw(0, 64, 32, BASE, 32, 0, BASE * 2, 64, 0, BASE * 3, 64, trt.F16, trt.F16)
+    assert e.value.status == trt.ERR_SIZE
+    with pytest.raises(trt.TrtError) as e:
+        trt.gemm_raw(64, 64, 32, BASE, 32, 0, BASE * 2, 64, 0, BASE, 64, trt.F16, trt.F16)
+    assert e.value.status == trt.ERR_OVERLAP
+
+
+# ---- tiles and layout maps --------------------------------------------------------
+
+def tile_configs():
+    return [(bm, bn, bk, wm, wn) for bm, bn, bk, wm, wn, _ in trt.tiles()]
+
+
+def test_tile_table():
+    tiles = trt.tiles()
+    assert (16, 64, 32, 1, 1, 16) in tiles      # the named GEMM's tile, one wave
+    for bm, bn, bk, wm, wn, regs in tiles:
+        kl = L.kernel_layout((bm, bn), (wm, 64 * wn))
+        assert kl["threads_per_block"] <= 1024
+        assert regs * 64 * wm * wn == bm * bn
+
+
+@pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (64, 64, 64, 2, 2),
+                                 (128, 128, 64, 2, 2), (256, 256, 64, 2, 2)])
+def test_c_owner_matches_oracle(cfg):
+    assert cfg in tile_configs()
+    tile = cfg[:3]
+    rows, cols = trt.layout_dump_host(trt.MAP_C_OWNER, tile)
+    regs = L.gemm_regs_per_lane(cfg)
+    x = np.arange(rows.size)
+    reg, lane, wave = x % regs, (x // regs) % 64, x // (regs * 64)
+    exp = np.array([L.gemm_c_owner(cfg, int(r), int(l), int(w))
+                    for r, l, w in zip(reg, lane, wave)], dtype=np.int32)
+    assert np.array_equal(rows, exp[:, 0]) and np.array_equal(cols, exp[:, 1])
+    # exactly once over the tile
+    assert len(set(zip(rows.tolist(), cols.tolist()))) == cfg[0] * cfg[1]
+    rank, ib, ob = trt.layout_rank(tile)
+    assert rank == ib == ob == L.log2_exact(cfg[0] * cfg[1])
+
+
+@pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (256, 256, 64, 2, 2),
+                                 (128, 128, 64, 2, 2)])
+def test_lds_and_copy_maps_match_oracle(cfg):
+    BM, BN, BK, WM, WN = cfg
+    tile, G, T = cfg[:3], BK // 8, 64 * WM * WN
+    for mid, R in [(trt.MAP_LDS_SLOT_A, BM), (trt.MAP_LDS_SLOT_B, BN)]:
+        slot, _ = trt.layout_dump_host(mid, tile)
+        exp = [L.lds_slot(r, g, G) for r in range(R) for g in range(G)]
+        assert slot.tolist() == exp
+    for mid, R, fn in [(trt.MAP_COPY_KCONTIG_A, BM, L.copy_kcontig),
+                       (trt.MAP_COPY_KCONTIG_B, BN, L.copy_kcontig),
+                       (trt.MAP_COPY_MNCONTIG_A, BM, L.copy_mncontig),
+                       (trt.MAP_COPY_MNCONTIG_B, BN, L.copy_mncontig)]:
+        r, c = trt.layout_dump_host(mid, tile)
+        n = r.size
+        exp = [fn(R, G, T, x % T, x // T) or (-1, -1) for x in range(n)]
+        assert list(zip(r.tolist(), c.tolist())) == [tuple(e) for e in exp]
+
+
+def test_layout_dump_host_errors():
+    with pytest.raises(trt.TrtError):
+        trt.layout_dump_host(99, (16, 64, 32))
+    assert trt.layout_size(trt.MAP_C_OWNER, (48, 64, 32)) == -1

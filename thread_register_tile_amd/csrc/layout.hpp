@@ -1,0 +1,207 @@
+// layout.hpp -- the layout module: who owns, moves and stores which element.
+//
+// Three shapes are kept apart ("My Triton From Scratch, Part 16: Register
+// Tiles", section "Three coordinate spaces"):
+//   * the logical tile   [BM, BN]  -- the C elements one workgroup produces;
+//   * the thread shape   WM x WN wavefronts of 64 lanes (physical);
+//   * the register shape FM x FN fragments x 4 fp32 registers per lane.
+//
+// Every map is GF(2)-linear in the bits of its inputs ("Triton LinearLayout",
+// sections "Linear Layout" and "Basis-vector representation"): a value is
+// the XOR of the basis vectors its set input bits select.  The C ownership
+// (register, lane, wave) -> (row, col) is stated twice -- as the arithmetic
+// the kernel evaluates and as GF(2) bases -- and a compile-time check proves
+// the two agree everywhere and that the basis matrix is square with full
+// rank, i.e. every output element is owned exactly once ("Triton
+// LinearLayout", section "Surjectivity, injectivity, and broadcasts").
+//
+// Matrix-core fragments (v_mfma_f32_16x16x32_{f16,bf16}, one wave):
+//   operand 0 (16 x 32): lane l holds row l%16, k = 8*(l/16) + e, e = 0..7
+//   operand 1 (32 x 16): lane l holds column l%16, the same k rule
+//   result    (16 x 16): lane l, register r holds row 4*(l/16) + r, col l%16
+// The kernel feeds the B tile (rows = n) to operand 0 and the A tile
+// (rows = m) to operand 1, so a fragment result is a C^T fragment: lane l,
+// register r holds C(l%16, 4*(l/16) + r) -- four consecutive columns per
+// lane, which the epilogue stores as one 8-byte vector.
+#pragma once
+
+#include <stdint.h>
+
+#define TRT_HD __host__ __device__ __forceinline__ constexpr
+
+namespace trt {
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
+constexpr bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// One basis vector: the (row, col) image of one input bit.
+struct Basis {
+  int32_t row, col;
+};
+
+// A GF(2)-linear map from NIN input bits to (row, col).
+template <int NIN>
+struct Gf2Map {
+  Basis b[NIN];
+  int row_bits, col_bits;
+
+  // XOR of the bases selected by the set bits of x ("Triton LinearLayout",
+  // section "LinearLayout::apply").
+  constexpr Basis apply(uint32_t x) const {
+    Basis out{0, 0};
+    for (int i = 0; i < NIN; ++i)
+      if ((x >> i) & 1u) {
+        out.row ^= b[i].row;
+        out.col ^= b[i].col;
+      }
+    return out;
+  }
+
+  // Rank over GF(2) of the matrix whose columns are the bases, by Gaussian
+  // elimination on packed (row | col << row_bits) words.
+  constexpr int rank() const {
+    uint32_t w[NIN] = {};
+    for (int i = 0; i < NIN; ++i)
+      w[i] = uint32_t(b[i].row) | (uint32_t(b[i].col) << row_bits);
+    int r = 0;
+    for (int bit = 0; bit < row_bits + col_bits; ++bit) {
+      int p = -1;
+      for (int i = r; i < NIN; ++i)
+        if ((w[i] >> bit) & 1u) { p = i; break; }
+      if (p < 0) continue;
+      uint32_t t = w[p]; w[p] = w[r]; w[r] = t;
+      for (int i = 0; i < NIN; ++i)
+        if (i != r && ((w[i] >> bit) & 1u)) w[i] ^= w[r];
+      ++r;
+    }
+    return r;
+  }
+
+  // Injective and surjective: a square basis matrix of full rank.
+  constexpr bool bijective() const {
+    return NIN == row_bits + col_bits && rank() == NIN;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// A workgroup tile: logical shape, thread shape, register shape.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Tile {
+  // logical tile and K step
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  // physical thread shape
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = 64 * WAVES;
+  // per-wave sub-tile, in 16 x 16 fragments
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  // register shape: accumulator registers per lane
+  static constexpr int REGS = FM * FN * 4;
+  // operand tiles in LDS: G chunks of 8 k (16 bytes) per row
+  static constexpr int G = BK / 8;
+  static constexpr int KSUB = BK / 32;  // matrix-core k steps per K step
+
+  static_assert(is_pow2(BM) && is_pow2(BN) && is_pow2(BK), "power-of-two tiles");
+  static_assert(is_pow2(WM) && is_pow2(WN), "power-of-two wave grid");
+  static_assert(WTM >= 16 && WTN >= 16 && WTM % 16 == 0 && WTN % 16 == 0,
+                "each wave owns whole 16x16 fragments");
+  static_assert(BK >= 32 && BK % 32 == 0 && G <= 8, "K step: 32 or 64");
+  static_assert(THREADS <= 1024, "1024 work-items per workgroup at most");
+  static_assert(BM % 8 == 0 && BN % 8 == 0, "8x8 transpose blocks");
+
+  // ---- C ownership, as the kernel evaluates it ----------------------------
+  // Register index reg = 4*(fm*FN + fn) + r.
+  TRT_HD static int owner_row(int reg, int lane, int wave) {
+    const int fm = (reg >> 2) / FN;
+    return (wave / WN) * WTM + 16 * fm + (lane & 15);
+  }
+  TRT_HD static int owner_col(int reg, int lane, int wave) {
+    const int fn = (reg >> 2) % FN;
+    return (wave % WN) * WTN + 16 * fn + 4 * (lane >> 4) + (reg & 3);
+  }
+
+  // ---- the same ownership as GF(2) bases -----------------------------------
+  // Input bits, low to high: register bits, 6 lane bits, wave bits.
+  static constexpr int REG_BITS = ilog2(REGS);
+  static constexpr int WAVE_BITS = ilog2(WAVES);
+  static constexpr int C_IN_BITS = REG_BITS + 6 + WAVE_BITS;
+
+  static constexpr Gf2Map<C_IN_BITS> c_map() {
+    Gf2Map<C_IN_BITS> m{};
+    m.row_bits = ilog2(BM);
+    m.col_bits = ilog2(BN);
+    int i = 0;
+    m.b[i++] = {0, 1};                                  // r bit 0
+    m.b[i++] = {0, 2};                                  // r bit 1
+    for (int s = 0; s < ilog2(FN); ++s) m.b[i++] = {0, 16 << s};   // fn
+    for (int s = 0; s < ilog2(FM); ++s) m.b[i++] = {16 << s, 0};   // fm
+    m.b[i++] = {1, 0}; m.b[i++] = {2, 0};               // lane bits 0-3: row
+    m.b[i++] = {4, 0}; m.b[i++] = {8, 0};
+    m.b[i++] = {0, 4}; m.b[i++] = {0, 8};               // lane bits 4-5: col
+    for (int s = 0; s < ilog2(WN); ++s) m.b[i++] = {0, WTN << s};  // wave col
+    for (int s = 0; s < ilog2(WM); ++s) m.b[i++] = {WTM << s, 0};  // wave row
+    return m;
+  }
+
+  // Exhaustive agreement of the arithmetic form with the bases.
+  static constexpr bool owner_matches_bases() {
+    constexpr auto m = c_map();
+    for (int w = 0; w < WAVES; ++w)
+      for (int l = 0; l < 64; ++l)
+        for (int r = 0; r < REGS; ++r) {
+          const uint32_t x = uint32_t(r) | (uint32_t(l) << REG_BITS) |
+                             (uint32_t(w) << (REG_BITS + 6));
+          const Basis v = m.apply(x);
+          if (v.row != owner_row(r, l, w) || v.col != owner_col(r, l, w)) return false;
+        }
+    return true;
+  }
+
+  static_assert(c_map().bijective(),
+                "C ownership must cover every tile element exactly once");
+  static_assert(owner_matches_bases(),
+                "kernel ownership arithmetic must equal its GF(2) bases");
+
+  // ---- LDS operand tiles ----------------------------------------------------
+  // Chunk (r, g) of a tile with R rows lives in 16-byte slot
+  // r*G + (g XOR s(r)),  s(r) = ((r >> (3 - log2 G)) XOR (r >> 3)) mod G.
+  // s is linear in the bits of r, so the slot map is a GF(2) bijection.  A
+  // fragment read (16 consecutive rows, one g) and a copy write (8 lanes on
+  // one row, or 8 lanes on rows 8 apart) both touch distinct 16-byte bank
+  // groups within each 128-byte LDS cycle.
+  TRT_HD static int lds_swz(int r) {
+    return ((r >> (3 - ilog2(G))) ^ (r >> 3)) & (G - 1);
+  }
+  TRT_HD static int lds_slot(int r, int g) { return r * G + (g ^ lds_swz(r)); }
+
+  // ---- cooperative copies ---------------------------------------------------
+  // "My Triton From Scratch, Part 12: CUDA Tile Layouts", section
+  // "Cooperative tile layouts": thread t handles linear items t + i*THREADS,
+  // ceil(items / THREADS) iterations, the tail lanes of the last one idle.
+  // k-contiguous storage: items are 16-byte chunks of the (R, G) grid in
+  // order (1, 0) -- g fastest, so 8 neighbouring lanes read one 128-byte
+  // run of a row.
+  template <int R>
+  struct KContig {
+    static constexpr int ITEMS = R * G;
+    static constexpr int ITERS = (ITEMS + THREADS - 1) / THREADS;
+    TRT_HD static bool active(int t, int i) { return t + i * THREADS < ITEMS; }
+    TRT_HD static int row(int t, int i) { return (t + i * THREADS) / G; }
+    TRT_HD static int g(int t, int i) { return (t + i * THREADS) % G; }
+  };
+  // Row-contiguous storage (A^T, or row-major B): items are 8x8 blocks of
+  // the (R/8, G) grid in order (0, 1) -- the row block fastest, so
+  // neighbouring lanes read neighbouring 16-byte runs of one k row.
+  template <int R>
+  struct MNContig {
+    static constexpr int ITEMS = (R / 8) * G;
+    static constexpr int ITERS = (ITEMS + THREADS - 1) / THREADS;
+    TRT_HD static bool active(int t, int i) { return t + i * THREADS < ITEMS; }
+    TRT_HD static int rb(int t, int i) { return (t + i * THREADS) % (R / 8); }
+    TRT_HD static int g(int t, int i) { return (t + i * THREADS) / (R / 8); }
+  };
+};
+
+}  // namespace trt

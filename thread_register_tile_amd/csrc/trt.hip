@@ -1,0 +1,337 @@
+// trt.hip -- the C ABI of libtrt.so: validation, tile selection, launches,
+// layout introspection and the matrix-core probe.  Declarations and the
+// contract of every entry point are in include/trt.h.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/trt.h"
+#include "gemm_kernel.hpp"
+#include "validate.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+trt_status fail(trt_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+trt_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(TRT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  g_err.clear();
+  return TRT_OK;
+}
+
+using trt::GemmArgs;
+
+// ---- compiled tiles ------------------------------------------------------------
+
+using TileTiny = trt::Tile<16, 64, 32, 1, 1>;    // one wave, the named GEMM's tile
+using Tile64 = trt::Tile<64, 64, 64, 2, 2>;      // 4 waves, 32x32 each
+using Tile128 = trt::Tile<128, 128, 64, 2, 2>;   // 4 waves, 64x64 each
+using Tile256 = trt::Tile<256, 256, 64, 2, 2>;   // 4 waves, 128x128 each
+
+template <class TL, int DT, bool AKC, bool BKC>
+void launch_vec(const GemmArgs& a, bool vec, dim3 grid, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((trt::gemm_kernel<TL, DT, AKC, BKC, true>), grid, dim3(TL::THREADS), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((trt::gemm_kernel<TL, DT, AKC, BKC, false>), grid, dim3(TL::THREADS), 0,
+                       s, a);
+}
+
+template <class TL, int DT>
+void launch_ops(const GemmArgs& a, int opA, int opB, bool vec, dim3 grid, hipStream_t s) {
+  const bool akc = opA == TRT_OP_N, bkc = opB == TRT_OP_T;
+  if (akc && bkc) launch_vec<TL, DT, true, true>(a, vec, grid, s);
+  else if (akc) launch_vec<TL, DT, true, false>(a, vec, grid, s);
+  else if (bkc) launch_vec<TL, DT, false, true>(a, vec, grid, s);
+  else launch_vec<TL, DT, false, false>(a, vec, grid, s);
+}
+
+template <class TL>
+void launch_tile(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
+  a.tiles_m = (a.M + TL::BM - 1) / TL::BM;
+  a.tiles_n = (a.N + TL::BN - 1) / TL::BN;
+  const dim3 grid(a.tiles_m * a.tiles_n);
+  if (dt == TRT_F16) launch_ops<TL, trt::DT_F16>(a, opA, opB, vec, grid, s);
+  else launch_ops<TL, trt::DT_BF16>(a, opA, opB, vec, grid, s);
+}
+
+// ---- layout maps (host and device evaluate the same functions) ---------------
+
+template <class TL>
+TRT_HD int64_t map_size(int map) {
+  using KA = typename TL::template KContig<TL::BM>;
+  using MA = typename TL::template MNContig<TL::BM>;
+  using KB = typename TL::template KContig<TL::BN>;
+  using MB = typename TL::template MNContig<TL::BN>;
+  switch (map) {
+    case TRT_MAP_C_OWNER: return (int64_t)TL::WAVES * 64 * TL::REGS;
+    case TRT_MAP_LDS_SLOT_A: return (int64_t)TL::BM * TL::G;
+    case TRT_MAP_LDS_SLOT_B: return (int64_t)TL::BN * TL::G;
+    case TRT_MAP_COPY_KCONTIG_A: return (int64_t)KA::ITERS * TL::THREADS;
+    case TRT_MAP_COPY_MNCONTIG_A: return (int64_t)MA::ITERS * TL::THREADS;
+    case TRT_MAP_COPY_KCONTIG_B: return (int64_t)KB::ITERS * TL::THREADS;
+    case TRT_MAP_COPY_MNCONTIG_B: return (int64_t)MB::ITERS * TL::THREADS;
+    default: return -1;
+  }
+}
+
+template <class TL, class Map>
+TRT_HD void eval_kcontig(int64_t x, int& r, int& c) {
+  const int t = (int)(x % TL::THREADS), i = (int)(x / TL::THREADS);
+  if (Map::active(t, i)) { r = Map::row(t, i); c = Map::g(t, i); }
+  else { r = -1; c = -1; }
+}
+
+template <class TL, class Map>
+TRT_HD void eval_mncontig(int64_t x, int& r, int& c) {
+  const int t = (int)(x % TL::THREADS), i = (int)(x / TL::THREADS);
+  if (Map::active(t, i)) { r = Map::rb(t, i); c = Map::g(t, i); }
+  else { r = -1; c = -1; }
+}
+
+template <class TL>
+TRT_HD void eval_map(int map, int64_t x, int& r, int& c) {
+  switch (map) {
+    case TRT_MAP_C_OWNER: {
+      const int reg = (int)(x % TL::REGS);
+      const int lane = (int)((x / TL::REGS) % 64);
+      const int wave = (int)(x / (TL::REGS * 64));
+      r = TL::owner_row(reg, lane, wave);
+      c = TL::owner_col(reg, lane, wave);
+      return;
+    }
+    case TRT_MAP_LDS_SLOT_A:
+    case TRT_MAP_LDS_SLOT_B:
+      r = TL::lds_slot((int)(x / TL::G), (int)(x % TL::G));
+      c = 0;
+      return;
+    case TRT_MAP_COPY_KCONTIG_A: eval_kcontig<TL, typename TL::template KContig<TL::BM>>(x, r, c); return;
+    case TRT_MAP_COPY_MNCONTIG_A: eval_mncontig<TL, typename TL::template MNContig<TL::BM>>(x, r, c); return;
+    case TRT_MAP_COPY_KCONTIG_B: eval_kcontig<TL, typename TL::template KContig<TL::BN>>(x, r, c); return;
+    case TRT_MAP_COPY_MNCONTIG_B: eval_mncontig<TL, typename TL::template MNContig<TL::BN>>(x, r, c); return;
+    default: r = c = -1; return;
+  }
+}
+
+template <class TL>
+__global__ void dump_kernel(int map, int32_t* rows, int32_t* cols, int64_t n) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= n) return;
+  int r, c;
+  eval_map<TL>(map, x, r, c);
+  rows[x] = r;
+  cols[x] = c;
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void probe_kernel(const trt::u32x4* a, const trt::u32x4* b,
+                                                    trt::f32x4* c) {
+  const int l = threadIdx.x;
+  c[l] = trt::mfma16<DT>(a[l], b[l], trt::f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
+// ---- tile registry ---------------------------------------------------------------
+
+struct TileEntry {
+  int bm, bn, bk, wm, wn, regs;
+  void (*launch)(GemmArgs, int, int, int, bool, hipStream_t);
+  int64_t (*size)(int);
+  void (*eval)(int, int64_t, int&, int&);
+  void (*dump)(int, int32_t*, int32_t*, int64_t, hipStream_t);
+  int rank, in_bits, out_bits;
+};
+
+template <class TL>
+void dump_launch(int map, int32_t* rows, int32_t* cols, int64_t n, hipStream_t s) {
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL((dump_kernel<TL>), dim3((unsigned)blocks), dim3(256), 0, s, map, rows, cols,
+                     n);
+}
+
+template <class TL>
+int64_t size_host(int map) { return map_size<TL>(map); }
+
+template <class TL>
+void eval_host(int map, int64_t x, int& r, int& c) { eval_map<TL>(map, x, r, c); }
+
+template <class TL>
+constexpr TileEntry entry() {
+  return TileEntry{TL::BM, TL::BN, TL::BK, TL::WM, TL::WN, TL::REGS,
+                   &launch_tile<TL>, &size_host<TL>, &eval_host<TL>, &dump_launch<TL>,
+                   TL::c_map().rank(), TL::C_IN_BITS, trt::ilog2(TL::BM * TL::BN)};
+}
+
+const TileEntry kTiles[] = {entry<TileTiny>(), entry<Tile64>(), entry<Tile128>(),
+                            entry<Tile256>()};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+const TileEntry* find_tile(const trt_tile* t) {
+  for (const TileEntry& e : kTiles)
+    if (e.bm == t->bm && e.bn == t->bn && e.bk == t->bk) return &e;
+  return nullptr;
+}
+
+// Tile choice when the caller names none: the largest tile that still gives
+// the 256 compute units a full wave of workgroups; a 16-row tile when M is
+// that small.
+const TileEntry* choose_tile(int64_t M, int64_t N) {
+  auto count = [&](const TileEntry& e) { return ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn); };
+  if (M <= 16) return &kTiles[0];
+  if (count(kTiles[3]) >= 192) return &kTiles[3];
+  if (count(kTiles[2]) >= 128) return &kTiles[2];
+  return &kTiles[1];
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+trt_status trt_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
+                        const void* B, int64_t ldb, int32_t opB, const void* C, int64_t ldc,
+                        int32_t in_dtype, int32_t out_dtype, const trt_epilogue* epi,
+                        const trt_tile* tile) {
+  std::string msg;
+  const trt_status s = trt::validate_gemm(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
+                                          out_dtype, epi, msg);
+  if (s != TRT_OK) return fail(s, msg);
+  if (tile && !find_tile(tile))
+    return fail(TRT_ERR_UNSUPPORTED, "no compiled kernel for the requested tile");
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                          int32_t opA, const void* B, int64_t ldb, int32_t opB, void* C,
+                          int64_t ldc, int32_t in_dtype, int32_t out_dtype,
+                          const trt_epilogue* epi, const trt_tile* tile, void* stream) {
+  const trt_status s =
+      trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, tile);
+  if (s != TRT_OK) return s;
+  const TileEntry* e = tile ? find_tile(tile) : choose_tile(M, N);
+
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.C = static_cast<uint16_t*>(C);
+  a.bias = epi ? static_cast<const uint16_t*>(epi->bias) : nullptr;
+  a.R = epi ? static_cast<const uint16_t*>(epi->residual) : nullptr;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.ldr = (epi && epi->residual) ? epi->ldr : 0;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.relu = (epi && epi->relu) ? 1 : 0;
+  // 16-byte operand vectors need 16-byte aligned bases and rows.
+  const bool vec = aligned(A, 16) && aligned(B, 16) && lda % 8 == 0 && ldb % 8 == 0;
+  // 8-byte epilogue vectors need 8-byte aligned C, bias, residual rows.
+  a.epi_vec = aligned(C, 8) && ldc % 4 == 0 && (!a.bias || aligned(a.bias, 8)) &&
+              (!a.R || (aligned(a.R, 8) && a.ldr % 4 == 0));
+  e->launch(a, in_dtype, opA, opB, vec, static_cast<hipStream_t>(stream));
+  return check_launch("gemm launch");
+}
+
+trt_status trt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
+                    const void* B, int64_t ldb, int32_t opB, void* C, int64_t ldc,
+                    int32_t in_dtype, int32_t out_dtype, const trt_epilogue* epi, void* stream) {
+  return trt_gemm_tiled(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi,
+                        nullptr, stream);
+}
+
+int32_t trt_tile_count(void) { return kNumTiles; }
+
+trt_status trt_tile_at(int32_t i, trt_tile* tile, int32_t* waves_m, int32_t* waves_n,
+                       int32_t* regs_per_lane) {
+  if (i < 0 || i >= kNumTiles) return fail(TRT_ERR_ARG, "tile index out of range");
+  const TileEntry& e = kTiles[i];
+  if (tile) *tile = trt_tile{e.bm, e.bn, e.bk};
+  if (waves_m) *waves_m = e.wm;
+  if (waves_n) *waves_n = e.wn;
+  if (regs_per_lane) *regs_per_lane = e.regs;
+  g_err.clear();
+  return TRT_OK;
+}
+
+int64_t trt_layout_size(int32_t map_id, const trt_tile* tile) {
+  if (!tile) return -1;
+  const TileEntry* e = find_tile(tile);
+  return e ? e->size(map_id) : -1;
+}
+
+trt_status trt_layout_dump_host(int32_t map_id, const trt_tile* tile, int32_t* rows,
+                                int32_t* cols, int64_t n) {
+  if (!tile) return fail(TRT_ERR_NULL, "tile must be non-null");
+  const TileEntry* e = find_tile(tile);
+  if (!e) return fail(TRT_ERR_UNSUPPORTED, "no compiled kernel for the requested tile");
+  const int64_t size = e->size(map_id);
+  if (size < 0) return fail(TRT_ERR_ARG, "unknown map id");
+  if (n != size) return fail(TRT_ERR_SIZE, "n must equal trt_layout_size(map_id, tile)");
+  if (!rows || !cols) return fail(TRT_ERR_NULL, "rows and cols must be non-null");
+  for (int64_t x = 0; x < n; ++x) {
+    int r, c;
+    e->eval(map_id, x, r, c);
+    rows[x] = r;
+    cols[x] = c;
+  }
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_layout_dump(int32_t map_id, const trt_tile* tile, int32_t* rows, int32_t* cols,
+                           int64_t n, void* stream) {
+  if (!tile) return fail(TRT_ERR_NULL, "tile must be non-null");
+  const TileEntry* e = find_tile(tile);
+  if (!e) return fail(TRT_ERR_UNSUPPORTED, "no compiled kernel for the requested tile");
+  const int64_t size = e->size(map_id);
+  if (size < 0) return fail(TRT_ERR_ARG, "unknown map id");
+  if (n != size) return fail(TRT_ERR_SIZE, "n must equal trt_layout_size(map_id, tile)");
+  if (!rows || !cols) return fail(TRT_ERR_NULL, "rows and cols must be non-null");
+  e->dump(map_id, rows, cols, n, static_cast<hipStream_t>(stream));
+  return check_launch("layout dump launch");
+}
+
+trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank, int32_t* in_bits,
+                           int32_t* out_bits) {
+  if (!tile) return fail(TRT_ERR_NULL, "tile must be non-null");
+  const TileEntry* e = find_tile(tile);
+  if (!e) return fail(TRT_ERR_UNSUPPORTED, "no compiled kernel for the requested tile");
+  if (rank) *rank = e->rank;
+  if (in_bits) *in_bits = e->in_bits;
+  if (out_bits) *out_bits = e->out_bits;
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_mfma_probe(int32_t dtype, const void* a, const void* b, float* c, void* stream) {
+  if (!a || !b || !c) return fail(TRT_ERR_NULL, "a, b and c must be non-null");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
+    return fail(TRT_ERR_ALIGN, "a, b and c must be 16-byte aligned");
+  const auto* av = static_cast<const trt::u32x4*>(a);
+  const auto* bv = static_cast<const trt::u32x4*>(b);
+  auto* cv = reinterpret_cast<trt::f32x4*>(c);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == TRT_F16)
+    hipLaunchKernelGGL((probe_kernel<trt::DT_F16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+  else if (dtype == TRT_BF16)
+    hipLaunchKernelGGL((probe_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+  else
+    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16 or TRT_BF16");
+  return check_launch("probe launch");
+}
+
+int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }
+
+const char* trt_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"
