@@ -64,6 +64,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before the "
+                         "GEMM steps (a known-size kernel to scale HBM counters by)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -97,6 +100,15 @@ def main():
                      bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
                      residual=R.data_ptr() if R is not None else 0,
                      ldr=w.ldr_ if R is not None else 0, tile=tile, stream=sptr)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -140,14 +152,21 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = oracle.default_threads()
-        # calibrate on a few rows, then size the sample to the time budget
-        t0 = time.perf_counter()
-        oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_, w.opB,
-                          w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
-                          ldr=w.ldr_ if host["R"] is not None else 0,
-                          m_range=(0, min(threads, w.M)), threads=threads)
-        t_cal = time.perf_counter() - t0
-        rows = int(min(w.M, max(threads, min(threads, w.M) * args.cpu_seconds / max(t_cal, 1e-3))))
+        # calibrate: the per-call cost (decoding B once) and the per-row
+        # cost, from two short runs; then size the sample to the budget
+        def run_rows(r):
+            t0 = time.perf_counter()
+            oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,
+                              w.opB, w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
+                              ldr=w.ldr_ if host["R"] is not None else 0,
+                              m_range=(0, r), threads=threads)
+            return time.perf_counter() - t0
+        r1 = min(threads, w.M)
+        r2 = min(4 * threads, w.M)
+        t1, t2 = run_rows(r1), run_rows(r2)
+        per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
+        fixed = max(t1 - r1 * per_row, 0.0)
+        rows = int(min(w.M, max(r1, (args.cpu_seconds - fixed) / per_row)))
         rows = max(1, rows - rows % max(1, min(threads, rows)))
         t0 = time.perf_counter()
         ref = oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,

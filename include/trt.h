@@ -88,8 +88,9 @@ typedef struct {
  * safety that cannot be proven is an error.  A, B, C must be non-NULL and all
  * pointers 2-byte aligned.  in_dtype must equal out_dtype (TRT_F16 or
  * TRT_BF16).  Elements of C outside [0,M) x [0,N) (the ldc padding) are never
- * written, and elements of A and B outside the logical operands (the lda/ldb
- * padding) are never read.
+ * written.  Elements of A and B outside the logical operands (the lda/ldb
+ * padding) never influence C, and no byte outside an operand's extent
+ * ((rows-1)*ld + cols elements from its base) is ever read.
  *
  * stream: a hipStream_t (NULL = the default stream).  The call enqueues one
  * kernel and returns; TRT_ERR_HIP means the launch failed, with the runtime's
@@ -134,13 +135,14 @@ int32_t trt_tile_count(void);
 /*
  * trt_tile_at -- describe compiled tile i (0 <= i < trt_tile_count()):
  * its logical tile, its physical thread shape as waves_m x waves_n
- * wavefronts of 64 lanes, and the accumulator registers each lane owns
- * ("My Triton From Scratch, Part 16: Register Tiles", section "Three
- * coordinate spaces": logical shape vs. thread shape vs. register shape).
- * Any output pointer may be NULL.  TRT_ERR_ARG if i is out of range.
+ * wavefronts of 64 lanes, the accumulator registers each lane owns, and the
+ * edge (16 or 32) of the square matrix-core fragments those registers are
+ * grouped in ("My Triton From Scratch, Part 16: Register Tiles", section
+ * "Three coordinate spaces": logical shape vs. thread shape vs. register
+ * shape).  Any output pointer may be NULL.  TRT_ERR_ARG if i is out of range.
  */
 trt_status trt_tile_at(int32_t i, trt_tile* tile, int32_t* waves_m,
-                       int32_t* waves_n, int32_t* regs_per_lane);
+                       int32_t* waves_n, int32_t* regs_per_lane, int32_t* frag);
 
 /* Maps that trt_layout_dump can enumerate. */
 typedef enum {
@@ -159,7 +161,16 @@ typedef enum {
    * of the 8x8 block it moves (rows 8rb..8rb+7, k = 8g..8g+7), or (-1,-1). */
   TRT_MAP_COPY_MNCONTIG_A = 4,
   TRT_MAP_COPY_KCONTIG_B = 5,
-  TRT_MAP_COPY_MNCONTIG_B = 6
+  TRT_MAP_COPY_MNCONTIG_B = 6,
+  /* Direct-to-LDS tiles of the pipelined kernel (tiles with bk == 32).
+   * k-contiguous operand tile: x = r*4 + g (chunk g of 8 k of row r),
+   * output (slot, 0).  Rows-contiguous operand tile: x = k*(R/8) + c
+   * (chunk c of 8 rows of k row k), output (slot, 0).  R = bm for A, bn
+   * for B; the rows-contiguous maps need R >= 128. */
+  TRT_MAP_DMA_KC_SLOT_A = 7,
+  TRT_MAP_DMA_KC_SLOT_B = 8,
+  TRT_MAP_DMA_MN_SLOT_A = 9,
+  TRT_MAP_DMA_MN_SLOT_B = 10
 } trt_map;
 
 /*
@@ -191,15 +202,16 @@ trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank,
                            int32_t* in_bits, int32_t* out_bits);
 
 /*
- * trt_mfma_probe -- run one 16x16x32 matrix-core instruction on one wave:
- * lane l passes a[l*8 .. l*8+7] as its A-operand register and b[l*8 ..] as
- * its B-operand register (raw 16-bit values of `dtype`), starting from a zero
- * accumulator, and writes its 4 result registers to c[l*4 .. l*4+3] (fp32).
- * a, b, c are device buffers of 512, 512 and 256 elements.  Used to confirm
- * the hardware fragment layout the ownership map is built on.
+ * trt_mfma_probe -- run one matrix-core instruction on one wave, shape 16
+ * (16x16x32) or 32 (32x32x16): lane l passes a[l*8 .. l*8+7] as its first
+ * operand register and b[l*8 ..] as its second (raw 16-bit values of
+ * `dtype`), starting from a zero accumulator, and writes its R result
+ * registers to c[l*R .. l*R+R-1] (fp32), R = 4 (shape 16) or 16 (shape 32).
+ * a, b are device buffers of 512 elements, c of 64*R.  Used to confirm the
+ * hardware fragment layouts the ownership maps are built on.
  */
-trt_status trt_mfma_probe(int32_t dtype, const void* a, const void* b,
-                          float* c, void* stream);
+trt_status trt_mfma_probe(int32_t dtype, int32_t shape, const void* a,
+                          const void* b, float* c, void* stream);
 
 /* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
 int32_t trt_abi_version(void);

@@ -248,44 +248,74 @@ def mfma16_c(lane, reg):
     return (4 * (lane // 16) + reg, lane % 16)           # (row, col)
 
 
+# v_mfma_f32_32x32x16_{f16,bf16}: operand 0 (32 rows x 16 k): lane l holds
+# row l % 32, k = 8*(l // 32) + e; operand 1 (16 k x 32 cols): column l % 32,
+# same k rule; result (32 x 32): lane l, register r holds row
+# 8*(r // 4) + 4*(l // 32) + r % 4, column l % 32.
+
+def mfma32_a(lane, elem):
+    return (lane % 32, 8 * (lane // 32) + elem)
+
+
+def mfma32_b(lane, elem):
+    return (8 * (lane // 32) + elem, lane % 32)
+
+
+def mfma32_c(lane, reg):
+    return (8 * (reg // 4) + 4 * (lane // 32) + reg % 4, lane % 32)
+
+
 # --------------------------------------------------------------------------
 # The workgroup tile of the MI355X kernel
 # --------------------------------------------------------------------------
-# A tile config is (BM, BN, BK, WAVES_M, WAVES_N).  Wave w sits at wave row
-# w // WAVES_N, wave column w % WAVES_N, and owns the sub-tile of
-# WTM = BM / WAVES_M rows by WTN = BN / WAVES_N columns, made of
-# (WTM/16) x (WTN/16) fragments.  The kernel feeds the B tile to the matrix
-# core's row operand and the A tile to its column operand, so a fragment's
-# result row is a C column and vice versa: within fragment (fm, fn), lane l,
-# register r holds C(16*fm + l % 16, 16*fn + 4*(l // 16) + r).  The register
-# index of that value is 4*(fm*(WTN/16) + fn) + r.
+# A tile config is (BM, BN, BK, WAVES_M, WAVES_N[, MF]), MF the fragment edge
+# (16 or 32, default 16).  Wave w sits at wave row w // WAVES_N, wave column
+# w % WAVES_N, and owns the sub-tile of WTM = BM / WAVES_M rows by
+# WTN = BN / WAVES_N columns, made of (WTM/MF) x (WTN/MF) fragments.  The
+# kernel feeds the B tile to the matrix core's row operand and the A tile to
+# its column operand, so a fragment's result row is a C column and vice
+# versa: within fragment (fm, fn), the value a lane's register holds at
+# fragment position (i, j) is C(MF*fm + j, MF*fn + i).  The register index of
+# that value is R*(fm*(WTN/MF) + fn) + r with R = MF*MF/64 registers per
+# fragment.
+
+def _cfg(cfg):
+    BM, BN, BK, WM, WN = cfg[:5]
+    MF = cfg[5] if len(cfg) > 5 else 16
+    return BM, BN, BK, WM, WN, MF
+
 
 def gemm_c_owner(cfg, reg, lane, wave):
-    BM, BN, BK, WM, WN = cfg
+    BM, BN, BK, WM, WN, MF = _cfg(cfg)
     WTM, WTN = BM // WM, BN // WN
-    FN = WTN // 16
-    r, f = reg % 4, reg // 4
+    FN = WTN // MF
+    R = MF * MF // 64
+    r, f = reg % R, reg // R
     fm, fn = f // FN, f % FN
-    frag_row, frag_col = mfma16_c(lane, r)       # (C column, C row) when swapped
-    row = (wave // WN) * WTM + 16 * fm + frag_col
-    col = (wave % WN) * WTN + 16 * fn + frag_row
+    frag_row, frag_col = (mfma16_c if MF == 16 else mfma32_c)(lane, r)
+    row = (wave // WN) * WTM + MF * fm + frag_col
+    col = (wave % WN) * WTN + MF * fn + frag_row
     return (row, col)
 
 
 def gemm_regs_per_lane(cfg):
-    BM, BN, BK, WM, WN = cfg
+    BM, BN, BK, WM, WN, MF = _cfg(cfg)
     return (BM // WM) * (BN // WN) // 64
 
 
 def gemm_c_bases(cfg):
     """The same ownership written as GF(2) bases {reg, lane, wave} -> (row, col)."""
-    BM, BN, BK, WM, WN = cfg
+    BM, BN, BK, WM, WN, MF = _cfg(cfg)
     WTM, WTN = BM // WM, BN // WN
-    FM, FN = WTM // 16, WTN // 16
-    reg = [(0, 1), (0, 2)]
-    reg += [(0, 16 << i) for i in range(log2_exact(FN))]
-    reg += [(16 << i, 0) for i in range(log2_exact(FM))]
-    lane = [(1, 0), (2, 0), (4, 0), (8, 0), (0, 4), (0, 8)]
+    FM, FN = WTM // MF, WTN // MF
+    if MF == 16:
+        reg = [(0, 1), (0, 2)]
+        lane = [(1, 0), (2, 0), (4, 0), (8, 0), (0, 4), (0, 8)]
+    else:
+        reg = [(0, 1), (0, 2), (0, 8), (0, 16)]
+        lane = [(1, 0), (2, 0), (4, 0), (8, 0), (16, 0), (0, 4)]
+    reg += [(0, MF << i) for i in range(log2_exact(FN))]
+    reg += [(MF << i, 0) for i in range(log2_exact(FM))]
     wave = [(0, WTN << i) for i in range(log2_exact(WN))]
     wave += [(WTM << i, 0) for i in range(log2_exact(WM))]
     return {"reg": reg, "lane": lane, "wave": wave}
@@ -326,3 +356,25 @@ def copy_mncontig(R, G, T, t, i):
     if lin >= (R // 8) * G:
         return None
     return coop_coordinate((R // 8, G), (0, 1), lin)
+
+
+# --------------------------------------------------------------------------
+# Direct-to-LDS tiles of the pipelined kernel (K step of 32)
+# --------------------------------------------------------------------------
+# k-contiguous operand [R rows][4 chunks of 8 k]: chunk (r, g) in slot
+# 4r + (g XOR sk(r)), sk(r) = (bit1(r) XOR bit3(r)) + 2*bit2(r).
+# Rows-contiguous operand [32 k rows][R/8 chunks of 8 rows]: chunk (k, c) in
+# slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*bit0(k) XOR 12*bit1(k).
+
+def _bit(x, i):
+    return (x >> i) & 1
+
+
+def dma_kc_slot(r, g):
+    sk = (_bit(r, 1) ^ _bit(r, 3)) + 2 * _bit(r, 2)
+    return 4 * r + (g ^ sk)
+
+
+def dma_mn_slot(R, k, c):
+    sm = (6 * _bit(k, 0)) ^ (12 * _bit(k, 1))
+    return k * (R // 8) + (c ^ sm)

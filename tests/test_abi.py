@@ -124,20 +124,28 @@ def test_gemm_errors_return_before_device_work():
 # ---- tiles and layout maps --------------------------------------------------------
 
 def tile_configs():
-    return [(bm, bn, bk, wm, wn) for bm, bn, bk, wm, wn, _ in trt.tiles()]
+    return [(bm, bn, bk, wm, wn, fr) for bm, bn, bk, wm, wn, _, fr in trt.tiles()]
 
 
 def test_tile_table():
     tiles = trt.tiles()
-    assert (16, 64, 32, 1, 1, 16) in tiles      # the named GEMM's tile, one wave
-    for bm, bn, bk, wm, wn, regs in tiles:
+    assert (16, 64, 32, 1, 1, 16, 16) in tiles      # the named GEMM's tile, one wave
+    for bm, bn, bk, wm, wn, regs, fr in tiles:
         kl = L.kernel_layout((bm, bn), (wm, 64 * wn))
         assert kl["threads_per_block"] <= 1024
         assert regs * 64 * wm * wn == bm * bn
+        assert fr in (16, 32) and regs % (fr * fr // 64) == 0
 
 
-@pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (64, 64, 64, 2, 2),
-                                 (128, 128, 64, 2, 2), (256, 256, 64, 2, 2)])
+ALL_TILES = [(16, 64, 32, 1, 1, 16), (64, 64, 64, 2, 2, 16), (128, 128, 64, 2, 2, 16),
+             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 2, 32)]
+
+
+def test_all_tiles_listed():
+    assert sorted(tile_configs()) == sorted(ALL_TILES)
+
+
+@pytest.mark.parametrize("cfg", ALL_TILES)
 def test_c_owner_matches_oracle(cfg):
     assert cfg in tile_configs()
     tile = cfg[:3]
@@ -155,7 +163,7 @@ def test_c_owner_matches_oracle(cfg):
 
 
 @pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (256, 256, 64, 2, 2),
-                                 (128, 128, 64, 2, 2)])
+                                 (128, 128, 64, 2, 2), (256, 256, 32, 2, 2)])
 def test_lds_and_copy_maps_match_oracle(cfg):
     BM, BN, BK, WM, WN = cfg
     tile, G, T = cfg[:3], BK // 8, 64 * WM * WN
@@ -177,3 +185,15 @@ def test_layout_dump_host_errors():
     with pytest.raises(trt.TrtError):
         trt.layout_dump_host(99, (16, 64, 32))
     assert trt.layout_size(trt.MAP_C_OWNER, (48, 64, 32)) == -1
+
+
+def test_dma_slot_maps_match_oracle():
+    tile = (256, 256, 32)
+    for mid, R in [(trt.MAP_DMA_KC_SLOT_A, 256), (trt.MAP_DMA_KC_SLOT_B, 256)]:
+        slot, _ = trt.layout_dump_host(mid, tile)
+        assert slot.tolist() == [L.dma_kc_slot(r, g) for r in range(R) for g in range(4)]
+    for mid, R in [(trt.MAP_DMA_MN_SLOT_A, 256), (trt.MAP_DMA_MN_SLOT_B, 256)]:
+        slot, _ = trt.layout_dump_host(mid, tile)
+        assert slot.tolist() == [L.dma_mn_slot(R, k, c) for k in range(32) for c in range(R // 8)]
+    # not defined for tiles without the 32-wide K step
+    assert trt.layout_size(trt.MAP_DMA_KC_SLOT_A, (256, 256, 64)) == -1

@@ -30,24 +30,30 @@ def _gpu():
 
 # ---- the hardware fragment layout the ownership map is built on ---------------
 
+MAPS = {16: (L.mfma16_a, L.mfma16_b, L.mfma16_c, 16, 32, 4),
+        32: (L.mfma32_a, L.mfma32_b, L.mfma32_c, 32, 16, 16)}
+
+
+@pytest.mark.parametrize("shape", [16, 32])
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
-def test_mfma_probe_fragment_maps(dtype):
+def test_mfma_probe_fragment_maps(dtype, shape):
+    fa, fb, fc, n, kk, regs = MAPS[shape]
     rng = np.random.default_rng(21)
-    X = rng.integers(-3, 4, (16, 32)).astype(np.float64)   # operand 0, rows x k
-    Y = rng.integers(-3, 4, (32, 16)).astype(np.float64)   # operand 1, k x cols
+    X = rng.integers(-3, 4, (n, kk)).astype(np.float64)   # operand 0, rows x k
+    Y = rng.integers(-3, 4, (kk, n)).astype(np.float64)   # operand 1, k x cols
     a = np.zeros((64, 8)); b = np.zeros((64, 8))
     for l in range(64):
         for e in range(8):
-            i, k = L.mfma16_a(l, e); a[l, e] = X[i, k]
-            k, j = L.mfma16_b(l, e); b[l, e] = Y[k, j]
+            i, k = fa(l, e); a[l, e] = X[i, k]
+            k, j = fb(l, e); b[l, e] = Y[k, j]
     D = X @ Y
-    exp = np.zeros((64, 4))
+    exp = np.zeros((64, regs))
     for l in range(64):
-        for r in range(4):
-            i, j = L.mfma16_c(l, r); exp[l, r] = D[i, j]
+        for r in range(regs):
+            i, j = fc(l, r); exp[l, r] = D[i, j]
     ab = torch.from_numpy(W.to_bits(a, dtype).view(np.int16)).cuda()
     bb = torch.from_numpy(W.to_bits(b, dtype).view(np.int16)).cuda()
-    c = trt.mfma_probe(ab, bb, dtype).cpu().numpy()
+    c = trt.mfma_probe(ab, bb, dtype, shape).cpu().numpy()
     assert np.array_equal(c, exp)
 
 
@@ -71,10 +77,12 @@ def test_mfma_probe_one_hot():
 
 # ---- device layout maps == host maps (== oracle, checked on the CPU) ----------
 
-@pytest.mark.parametrize("tile", [t[:3] for t in [(16, 64, 32), (64, 64, 64),
-                                                   (128, 128, 64), (256, 256, 64)]])
+@pytest.mark.parametrize("tile", [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64),
+                                  (256, 256, 32)])
 def test_layout_dump_device_equals_host(tile):
-    for mid in range(7):
+    for mid in range(11):
+        if trt.layout_size(mid, tile) < 0:
+            continue
         hr, hc = trt.layout_dump_host(mid, tile)
         dr, dc = trt.layout_dump(mid, tile)
         torch.cuda.synchronize()
@@ -83,7 +91,7 @@ def test_layout_dump_device_equals_host(tile):
 
 # ---- small shapes, every compiled instance, full comparison ---------------------
 
-TILES = [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64)]
+TILES = [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64), (256, 256, 32)]
 
 
 def small_case(tile, dtype, opA, opB, pad, epi, seed, dist="uniform"):
@@ -91,6 +99,10 @@ def small_case(tile, dtype, opA, opB, pad, epi, seed, dist="uniform"):
     M, N, K = 2 * BM + 37, 2 * BN + 19, 3 * BK + 9
     if BM == 256:
         M, N, K = BM + 37, BN + 19, 2 * BK + 9
+    if BK == 32 and BM == 256:
+        # the pipelined kernel: k-contiguous operands need K % 8 == 0; a
+        # partial last K step and ragged M, N edges remain
+        M, N, K = 2 * BM + 37, BN + 19, 5 * BK + 8
     lda = (M if opA else K) + pad
     ldb = (K if opB else N) + pad
     return W.Workload(f"small{tile}", M, N, K, opA=opA, opB=opB, lda=lda, ldb=ldb,
@@ -136,6 +148,35 @@ def test_brute_force_tiny_shapes():
         run.launch()
         assert_accept(run.result(), reference_block(w, run.host), W.F16, exact=True,
                       what=f"M={M} N={N} K={K} op={opA}{opB}")
+
+
+def test_pipelined_tile_ragged_shapes():
+    # the direct-to-LDS kernel on many small ragged shapes: rows beyond M and
+    # N, partial last K steps, all four storage combinations, both dtypes
+    rng = np.random.default_rng(9)
+    for trial in range(24):
+        M, N = int(rng.integers(1, 600)), int(rng.integers(1, 600))
+        K = 8 * int(rng.integers(1, 40))
+        opA, opB = trial % 2, (trial // 2) % 2
+        # rows-contiguous operands take this kernel when their rows are whole
+        # 16-byte runs; other shapes run the generic kernel on the same tile
+        if opA and trial % 4 != 3:
+            M = max(8, M - M % 8)
+        if not opB and trial % 4 != 3:
+            N = max(8, N - N % 8)
+        dt = W.F16 if trial % 3 else W.BF16
+        a_cols = M if opA else K
+        b_cols = K if opB else N
+        w = W.Workload("dma-bf", M, N, K, opA=opA, opB=opB,
+                       lda=-(-a_cols // 8) * 8 + 8 * (trial % 2),
+                       ldb=-(-b_cols // 8) * 8 + 8 * ((trial // 3) % 2),
+                       dtype=dt, dist="ternary", seed=2000 + trial,
+                       bias=bool(trial % 2), relu=bool(trial % 4 == 1),
+                       residual=bool(trial % 3 == 0), tile=(256, 256, 32))
+        run = Run(w, ldc=N + 4 * (trial % 3))
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
+                      what=f"M={M} N={N} K={K} op={opA}{opB} dt={dt}")
 
 
 def test_deterministic_runs():

@@ -183,12 +183,13 @@ def test_mfma16_maps_are_bijections():
 
 TILE_CONFIGS = [(16, 64, 32, 1, 1), (64, 64, 64, 2, 2), (128, 128, 64, 2, 2),
                 (256, 256, 64, 2, 2), (256, 128, 64, 2, 2), (128, 256, 64, 2, 2),
-                (256, 256, 64, 2, 4)]
+                (256, 256, 64, 2, 4), (256, 256, 32, 2, 2, 32), (128, 128, 32, 2, 2, 32),
+                (64, 64, 32, 2, 2, 32)]
 
 
 @pytest.mark.parametrize("cfg", TILE_CONFIGS)
 def test_gemm_c_owner_exactly_once(cfg):
-    BM, BN, BK, WM, WN = cfg
+    BM, BN, BK, WM, WN = cfg[:5]
     regs = L.gemm_regs_per_lane(cfg)
     owned = [L.gemm_c_owner(cfg, r, l, w)
              for w in range(WM * WN) for l in range(64) for r in range(regs)]
@@ -198,7 +199,7 @@ def test_gemm_c_owner_exactly_once(cfg):
 
 @pytest.mark.parametrize("cfg", TILE_CONFIGS)
 def test_gemm_c_owner_is_gf2_linear(cfg):
-    BM, BN, BK, WM, WN = cfg
+    BM, BN, BK, WM, WN = cfg[:5]
     bases = L.gemm_c_bases(cfg)
     out_bits = [L.log2_exact(BM), L.log2_exact(BN)]
     assert L.gf2_is_injective(bases, out_bits) and L.gf2_is_surjective(bases, out_bits)
@@ -280,3 +281,76 @@ def test_copy_maps_cover_tile():
         got = [L.copy_mncontig(R, G, T, t, i) for t in range(T) for i in range(it)]
         got = [x for x in got if x is not None]
         assert sorted(got) == [(rb, g) for rb in range(R // 8) for g in range(G)]
+
+
+def test_mfma32_maps_are_bijections():
+    a = {L.mfma32_a(l, e) for l in range(64) for e in range(8)}
+    b = {L.mfma32_b(l, e) for l in range(64) for e in range(8)}
+    c = {L.mfma32_c(l, r) for l in range(64) for r in range(16)}
+    assert a == {(i, k) for i in range(32) for k in range(16)}
+    assert b == {(k, j) for k in range(16) for j in range(32)}
+    assert c == {(i, j) for i in range(32) for j in range(32)}
+    for l in range(64):
+        for e in range(8):
+            assert L.mfma32_a(l, e)[1] == L.mfma32_b(l, e)[0]
+
+
+def test_owner_runs_of_four_columns():
+    # every run of four consecutive registers holds four consecutive columns
+    # of one row: the epilogue's 8-byte vector stores rely on it
+    for cfg in [(16, 64, 32, 1, 1), (256, 256, 32, 2, 2, 32)]:
+        for w in range(cfg[3] * cfg[4]):
+            for l in range(64):
+                for r0 in range(0, L.gemm_regs_per_lane(cfg), 4):
+                    pts = [L.gemm_c_owner(cfg, r0 + e, l, w) for e in range(4)]
+                    assert all(p[0] == pts[0][0] for p in pts)
+                    assert [p[1] - pts[0][1] for p in pts] == [0, 1, 2, 3]
+
+
+# ---- direct-to-LDS tiles ---------------------------------------------------------
+
+@pytest.mark.parametrize("R", [128, 256])
+def test_dma_slots_bijective(R):
+    assert sorted(L.dma_kc_slot(r, g) for r in range(R) for g in range(4)) == list(range(4 * R))
+    assert sorted(L.dma_mn_slot(R, k, c) for k in range(32) for c in range(R // 8)) \
+        == list(range(4 * R))
+
+
+def _conflicts_bytes(addr_bytes, window):
+    """Worst count of accesses hitting the same bank among a group of
+    accesses served together; banks are 4 bytes wide, window bytes per cycle.
+    addr_bytes: list of (start, length) per lane."""
+    banks = {}
+    for a, n in addr_bytes:
+        for b in range(a, a + n, 4):
+            banks.setdefault((b % window) // 4, set()).add(b)
+    return max(len(v) for v in banks.values())
+
+
+@pytest.mark.parametrize("R", [128, 256])
+def test_dma_kc_fragment_reads_conflict_free(R):
+    # 32x32x16 operand read: lane l reads row rbase + l%32, chunk g = 2s + l//32
+    for rbase in range(0, R, 32):
+        for s in range(2):
+            lanes = [(16 * L.dma_kc_slot(rbase + l % 32, 2 * s + l // 32), 16) for l in range(64)]
+            for n, window in [(8, 128), (16, 256)]:
+                for q in range(0, 64, n):
+                    assert _conflicts_bytes(lanes[q:q + n], window) == 1
+
+
+@pytest.mark.parametrize("R", [128, 256])
+def test_dma_mn_transposed_reads_conflict_free(R):
+    # transposing read: lane l (group gq = l//16, l16 = l%16) reads 8 bytes at
+    # k row 8*(gq//2) + 4h + l16//4, columns c0 + 16*(gq%2) + 4*(l16%4)
+    for c0 in range(0, R, 32):
+        for h in range(2):
+            lanes = []
+            for l in range(64):
+                gq, l16 = l // 16, l % 16
+                k = 8 * (gq // 2) + 4 * h + l16 // 4
+                col = c0 + 16 * (gq % 2) + 4 * (l16 % 4)
+                slot = L.dma_mn_slot(R, k, col // 8)
+                lanes.append((16 * slot + 2 * (col % 8), 8))
+            for n, window in [(16, 128), (32, 256)]:
+                for q in range(0, 64, n):
+                    assert _conflicts_bytes(lanes[q:q + n], window) == 1

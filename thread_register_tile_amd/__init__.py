@@ -35,6 +35,10 @@ MAP_COPY_KCONTIG_A = 3
 MAP_COPY_MNCONTIG_A = 4
 MAP_COPY_KCONTIG_B = 5
 MAP_COPY_MNCONTIG_B = 6
+MAP_DMA_KC_SLOT_A = 7
+MAP_DMA_KC_SLOT_B = 8
+MAP_DMA_MN_SLOT_A = 9
+MAP_DMA_MN_SLOT_B = 10
 
 
 class TrtError(RuntimeError):
@@ -76,7 +80,7 @@ def lib():
         L.trt_tile_count.argtypes = []
         L.trt_tile_count.restype = i32
         L.trt_tile_at.argtypes = [i32, ctypes.POINTER(TileDesc), ctypes.POINTER(i32),
-                                  ctypes.POINTER(i32), ctypes.POINTER(i32)]
+                                  ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.trt_tile_at.restype = i32
         L.trt_layout_dump.argtypes = [i32, ctypes.POINTER(TileDesc), vp, vp, i64, vp]
         L.trt_layout_dump.restype = i32
@@ -87,7 +91,7 @@ def lib():
         L.trt_layout_rank.argtypes = [ctypes.POINTER(TileDesc), ctypes.POINTER(i32),
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.trt_layout_rank.restype = i32
-        L.trt_mfma_probe.argtypes = [i32, vp, vp, vp, vp]
+        L.trt_mfma_probe.argtypes = [i32, i32, vp, vp, vp, vp]
         L.trt_mfma_probe.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
@@ -140,14 +144,15 @@ def validate_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
 
 
 def tiles():
-    """Compiled tiles: [(bm, bn, bk, waves_m, waves_n, regs_per_lane), ...]."""
+    """Compiled tiles: [(bm, bn, bk, waves_m, waves_n, regs_per_lane, frag), ...]
+    where frag is the edge (16 or 32) of the matrix-core fragments."""
     out = []
     for i in range(lib().trt_tile_count()):
         t = TileDesc()
-        wm, wn, regs = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        wm, wn, regs, fr = (ctypes.c_int32() for _ in range(4))
         _check(lib().trt_tile_at(i, ctypes.byref(t), ctypes.byref(wm), ctypes.byref(wn),
-                                 ctypes.byref(regs)))
-        out.append((t.bm, t.bn, t.bk, wm.value, wn.value, regs.value))
+                                 ctypes.byref(regs), ctypes.byref(fr)))
+        out.append((t.bm, t.bn, t.bk, wm.value, wn.value, regs.value, fr.value))
     return out
 
 
@@ -258,13 +263,14 @@ def layout_dump(map_id, tile, device="cuda"):
     return rows, cols
 
 
-def mfma_probe(a_regs, b_regs, dtype=F16):
-    """Run one 16x16x32 matrix-core instruction: a_regs, b_regs are [64, 8]
-    16-bit tensors (lane-major operand registers); returns [64, 4] fp32."""
+def mfma_probe(a_regs, b_regs, dtype=F16, shape=16):
+    """Run one matrix-core instruction (shape 16: 16x16x32, 32: 32x32x16):
+    a_regs, b_regs are [64, 8] 16-bit tensors (lane-major operand registers);
+    returns [64, 4] (shape 16) or [64, 16] (shape 32) fp32."""
     torch = _torch()
-    c = torch.empty((64, 4), dtype=torch.float32, device=a_regs.device)
+    c = torch.empty((64, 4 if shape == 16 else 16), dtype=torch.float32, device=a_regs.device)
     a = a_regs.contiguous()
     b = b_regs.contiguous()
-    _check(lib().trt_mfma_probe(dtype, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+    _check(lib().trt_mfma_probe(dtype, shape, a.data_ptr(), b.data_ptr(), c.data_ptr(),
                                 _stream(a.device)))
     return c

@@ -1,0 +1,376 @@
+// gemm_dma.hpp -- the pipelined main-path GEMM kernel for gfx950.
+//
+// Same contract as the generic kernel in gemm_kernel.hpp, with 32x32x16
+// matrix-core fragments (the tile's ownership map is stated in layout.hpp).
+// It differs in how operand tiles reach the matrix cores:
+//
+//   * Direct-to-LDS copies.  Each 16-byte chunk goes from global memory
+//     straight into LDS (buffer_load ... lds): no staging registers, no LDS
+//     store instructions.  A wave instruction fills 64 consecutive LDS slots,
+//     so each lane fetches the chunk its slot holds under the XOR swizzle.
+//   * Hardware bounds.  Each operand is read through a buffer descriptor whose
+//     record count is the operand's byte extent, rebased every K step: a copy
+//     reaching past the extent returns zero and never faults.  The check
+//     covers a 16-byte copy as a whole, so the caller guarantees that no copy
+//     straddles the extent's end (K % 8 == 0 for k-contiguous operands, rows
+//     % 8 == 0 for rows-contiguous ones).  Rows beyond M or N are read (or
+//     zero) but only feed accumulators the epilogue never stores; k beyond K
+//     reads zero for rows-contiguous operands and is forced out of range for
+//     k-contiguous chunks on the last, partial K step.
+//   * Transposing fragment reads.  A rows-contiguous operand (row-major B, or
+//     A^T) keeps its natural [k][rows] layout in LDS and reaches the matrix
+//     core through ds_read_b64_tr_b16: within each 16 lanes, output lane i,
+//     element v is input lane 4v + i/4, element i%4.  Lanes 4v..4v+3 read k row
+//     k0+v at columns c0, c0+4, c0+8, c0+12, so output lane i holds k0..k0+3
+//     of column c0+i -- the matrix-core operand layout, two reads per 8 k.
+//   * Four LDS stages of one 32-wide K step each (4 x 32 KiB), copies issued
+//     three steps ahead, one barrier per step.
+//
+// Per K step kt, per wave (S0 / S1: the fragments of the step's two 16-wide
+// k halves, each in its own registers):
+//   issue the copies of step kt+3 into stage (kt+3)%4;
+//   read S1(kt) while the products on S0(kt) run;
+//   wait for this wave's copies of step kt+1; workgroup barrier;
+//   read S0(kt+1) while the products on S1(kt) run.
+// Stage (kt+3)%4 was last read (S0(kt-1) in step kt-2, S1(kt-1) in step kt-1)
+// before the barrier of step kt-1, which precedes the copies of step kt; the
+// copies of step kt+1 are complete and visible once every wave has waited
+// for its own and passed the barrier of step kt.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace trt {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define TRT_LDS __attribute__((address_space(3)))
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
+// operations (or n LDS operations) of this wave are outstanding.
+constexpr int waitcnt_vm(int n) { return ((n >> 4) & 3) << 14 | 0x0F70 | (n & 15); }
+constexpr int waitcnt_lgkm(int n) { return 0xC07F | ((n & 15) << 8); }
+
+// One 16-byte direct-to-LDS copy per lane: global (buffer) byte offset voff
+// -> LDS byte address lds_addr + 16 * lane.  lds_addr is wave-uniform (it
+// travels in M0).  Written as inline assembly so that the compiler does not
+// treat the copy as a pending LDS store that every later LDS read must wait
+// for: the kernel orders copies and reads itself with s_waitcnt vmcnt and
+// barriers.  M0 is saved and restored around the copy.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr,
+                                      uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rs));
+}
+
+enum : int {
+  SG_VALU = 0x002,
+  SG_SALU = 0x004,
+  SG_MFMA = 0x008,
+  SG_VMEM_READ = 0x020,
+  SG_DS_READ = 0x100,
+};
+
+// One operand's copies and fragment reads.  R: tile rows (m for A, n for B);
+// KC: k-contiguous storage.
+template <class TL, int R, bool KC>
+struct DmaOperand {
+  static constexpr int CHUNKS = R * 32 * 2 / 16;         // 16-byte chunks per stage
+  static constexpr int NCH = CHUNKS / TL::THREADS;       // per thread per stage
+  static constexpr int BYTES = R * 64;                   // one stage of this operand
+  static_assert(CHUNKS % TL::THREADS == 0, "whole copy iterations");
+  static_assert(KC || R >= 128, "the rows-contiguous swizzle needs 16 chunks per k row");
+
+  const char* base;      // operand base address
+  int64_t extent;        // operand extent in bytes
+  int64_t step_bytes;    // bytes per K step of 32
+  uint32_t voff[NCH];    // byte offset of each chunk this thread copies, at step 0
+  int kchunk;            // k offset (elements) of this thread's chunks (KC only)
+
+  __device__ __forceinline__ void init(const uint16_t* X, int64_t ld, int64_t ext, int row0,
+                                       int t) {
+    base = reinterpret_cast<const char*>(X);
+    extent = ext;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int s = i * TL::THREADS + t;  // LDS slot this lane fills
+      if (KC) {
+        const int r = TL::kc_slot_row(s), g = TL::kc_slot_g(s);
+        voff[i] = (uint32_t)(((int64_t)(row0 + r) * ld + 8 * g) * 2);
+        kchunk = 8 * g;  // the same for every i: rows advance by THREADS/4
+      } else {
+        const int k = TL::template mn_slot_k<R>(s), c = TL::template mn_slot_c<R>(s);
+        voff[i] = (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2);
+      }
+    }
+    step_bytes = KC ? 64 : 64 * ld;
+  }
+
+  // Buffer descriptor of K step `step`: based at the step's first byte, its
+  // record count what is left of the operand (zero past the end).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int step) const {
+    const int64_t adv = (int64_t)step * step_bytes;
+    int64_t left = extent - adv;
+    left = left < 0 ? 0 : left;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (adv < extent ? adv : 0)),
+                                             (short)0, (int)left, 0x00020000);
+  }
+  // Copy i (0 <= i < NCH) of K step `step` into LDS region `dst` (this
+  // operand's part of one stage).  last_partial: K % 32 != 0 and `step` is
+  // the last step, whose chunks at k >= K are forced out of range.
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int step, uint32_t dst,
+                                            int wave, int K, bool last_partial, int i) const {
+    const bool drop = KC && last_partial && (step * 32 + kchunk >= K);
+    const uint32_t off = drop ? 0x80000000u : voff[i];
+    dma16(rs, __builtin_amdgcn_readfirstlane(dst + (i * TL::THREADS + 64 * wave) * 16), off);
+  }
+};
+
+// Fragment addressing of one operand tile inside a stage.  F: fragments per
+// wave along this operand (FM or FN); rbase: the wave's first row.
+template <class TL, int R, bool KC, int F>
+struct FragReader {
+  // k-contiguous: one base per k half (the chunk XOR differs), fragments at
+  // +2048 bytes (32 rows of 64 bytes).  rows-contiguous: one base per
+  // fragment (the chunk XOR differs), k half at +32R bytes (16 k rows),
+  // second read of 4 k rows at +8R bytes.
+  int addr[KC ? 2 : F];
+
+  __device__ __forceinline__ void init(int rbase, int lane, int region) {
+    if (KC) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        addr[s] = region + 16 * TL::kc_slot(rbase + (lane & 31), 2 * s + (lane >> 5));
+    } else {
+      const int l16 = lane & 15, gq = lane >> 4;
+      const int k = 8 * (gq >> 1) + (l16 >> 2);
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int c = (rbase + 32 * f) / 8 + 2 * (gq & 1) + ((l16 & 3) >> 1);
+        addr[f] = region + 16 * (k * (R / 8) + (c ^ TL::mn_swz(k))) + 8 * (l16 & 1);
+      }
+    }
+  }
+
+  __device__ __forceinline__ u32x4 read(TRT_LDS char* st, int s, int f) const {
+    if (KC) return *(TRT_LDS u32x4*)(st + addr[s] + 2048 * f);
+    TRT_LDS char* p = st + addr[f] + s * 32 * R;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TRT_LDS i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TRT_LDS i16x4*)(p + 8 * R));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+  static constexpr int DS_PER_FRAG = KC ? 1 : 2;
+};
+
+// Fused epilogue of a pipelined tile, restaged through LDS.  The tile is
+// written in two passes of half its fragment rows: each wave stores its raw
+// fp32 accumulators of the pass into an LDS staging array (rows padded by 16
+// bytes so the 32 rows a fragment store touches fall on distinct banks);
+// then every thread takes four consecutive columns of successive rows, adds
+// the bias it read once for those columns, applies ReLU, adds the residual,
+// rounds once to the output type and stores 8 bytes -- a wave covers 512
+// contiguous bytes of a row ("My Triton From Scratch, Part 16: Register
+// Tiles", sections "Masks and stores" and "Broadcasts cannot be treated as
+// full register tiles": per-element masks, bias held once per owned column).
+template <class TL, int DT>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&acc)[TL::FM][TL::FN],
+                                             float* stage, int m0, int n0, int t) {
+  constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
+  constexpr int PITCH = BN + 4;                       // floats per staged row
+  constexpr int HALF_ROWS = TL::BM / 2;               // rows per pass
+  constexpr int COLS_PER_T = 4;
+  constexpr int T_PER_ROW = BN / COLS_PER_T;          // threads across a row
+  constexpr int ROWS_PER_IT = TL::THREADS / T_PER_ROW;
+  static_assert(FM % 2 == 0 && TL::WM == 2, "two passes over the wave rows");
+  const int lane = t & 63, wave = t >> 6;
+  const int wr = wave / TL::WN, wc = wave % TL::WN;
+  const int col = COLS_PER_T * (t % T_PER_ROW);       // this thread's 4 columns
+  const int n = n0 + col;
+  const bool vec = p.epi_vec && n + 4 <= p.N;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.bias) {
+    if (vec) {
+      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+      bias[0] = to_f32<DT>(bb[0] & 0xFFFFu); bias[1] = to_f32<DT>(bb[0] >> 16);
+      bias[2] = to_f32<DT>(bb[1] & 0xFFFFu); bias[3] = to_f32<DT>(bb[1] >> 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) bias[e] = to_f32<DT>(p.bias[n + e]);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    // accumulators of fragment rows fm = 2*pass, 2*pass+1 -> staged rows
+    // prow = 64*wr + 32*(fm - 2*pass) + lane%32
+#pragma unroll
+    for (int f = 0; f < FM / 2; ++f) {
+      const int fm = (FM / 2) * pass + f;
+      const int prow = (HALF_ROWS / TL::WM) * wr + TL::MF * f + (lane & 31);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wc * TL::WTN + TL::MF * fn + 8 * q + 4 * (lane >> 5);
+          *reinterpret_cast<f32x4*>(stage + prow * PITCH + c) =
+              f32x4{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                    acc[fm][fn][4 * q + 3]};
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < HALF_ROWS / ROWS_PER_IT; ++it) {
+      const int prow = it * ROWS_PER_IT + t / T_PER_ROW;
+      // staged row -> tile row: wave row block, then the pass's half of it
+      const int mt = (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
+                     prow % (HALF_ROWS / TL::WM);
+      const int m = m0 + mt;
+      if (m >= p.M) continue;
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow * PITCH + col);
+      float y[4] = {a4[0] + bias[0], a4[1] + bias[1], a4[2] + bias[2], a4[3] + bias[3]};
+      if (p.relu) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
+      }
+      if (p.R) {
+        const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
+        if (vec) {
+          const u32x2 rr = *reinterpret_cast<const u32x2*>(rp);
+          y[0] += to_f32<DT>(rr[0] & 0xFFFFu); y[1] += to_f32<DT>(rr[0] >> 16);
+          y[2] += to_f32<DT>(rr[1] & 0xFFFFu); y[3] += to_f32<DT>(rr[1] >> 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
+        }
+      }
+      uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
+      if (vec) {
+        u32x2 o;
+        o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
+        o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
+        *reinterpret_cast<u32x2*>(cp) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <class TL, int DT, bool A_KC, bool B_KC>
+__global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
+  static_assert(TL::BK == 32 && TL::MF == 32, "32-wide K steps of 32x32x16 fragments");
+  constexpr int BM = TL::BM, BN = TL::BN, FM = TL::FM, FN = TL::FN;
+  using OpA = DmaOperand<TL, BM, A_KC>;
+  using OpB = DmaOperand<TL, BN, B_KC>;
+  constexpr int STAGE = OpA::BYTES + OpB::BYTES;
+  constexpr int NS = 4;
+  constexpr int LOADS = OpA::NCH + OpB::NCH;
+  constexpr int EPI_BYTES = (BM / 2) * (BN + 4) * 4;
+  constexpr int LDS_BYTES = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
+  static_assert(LOADS <= FM * FN && FM + FN <= FM * FN, "one copy / read per product");
+  __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
+  TRT_LDS char* lds = (TRT_LDS char*)lds_raw;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  int tm, tn;
+  tile_of<8>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  OpA a;
+  OpB b;
+  a.init(p.A, p.lda, p.a_bytes, m0, t);
+  b.init(p.B, p.ldb, p.b_bytes, n0, t);
+
+  const int nk = (p.K + 31) / 32;
+  const bool partial = (p.K & 31) != 0;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  FragReader<TL, BM, A_KC, FM> ra;
+  FragReader<TL, BN, B_KC, FN> rb;
+  ra.init((wave / TL::WN) * TL::WTM, lane, 0);
+  rb.init((wave % TL::WN) * TL::WTN, lane, OpA::BYTES);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
+
+  // prologue: steps 0..2 in flight, S0(0) in registers
+#pragma unroll
+  for (int step = 0; step < 3; ++step) {
+    const uint32_t st = lds_base + step * STAGE;
+    const bool lp = partial && step == nk - 1;
+    const auto rsa = a.rsrc(step), rsb = b.rsrc(step);
+#pragma unroll
+    for (int i = 0; i < OpA::NCH; ++i) a.issue_one(rsa, step, st, wave, p.K, lp, i);
+#pragma unroll
+    for (int i = 0; i < OpB::NCH; ++i) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, i);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < FN; ++j) b0[j] = rb.read(lds, 0, j);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a0[i] = ra.read(lds, 0, i);
+
+  // Main loop, in an explicit instruction order: after each of the first
+  // products of a half comes one copy of step kt+3 and one fragment read of
+  // the other half, so copies and reads are issued early and their latency
+  // is covered by the remaining products.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int step = kt + 3;
+    const uint32_t st = lds_base + (step & (NS - 1)) * STAGE;
+    const bool lp = partial && step == nk - 1;
+    const auto rsa = a.rsrc(step), rsb = b.rsrc(step);
+    TRT_LDS char* cur = lds + (kt & (NS - 1)) * STAGE;
+    TRT_LDS char* nxt = lds + ((kt + 1) & (NS - 1)) * STAGE;
+#pragma unroll
+    for (int q = 0; q < FM * FN; ++q) {
+      acc[q / FN][q % FN] = mfma32<DT>(b0[q % FN], a0[q / FN], acc[q / FN][q % FN]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < OpA::NCH) a.issue_one(rsa, step, st, wave, p.K, lp, q);
+      else if (q < LOADS) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, q - OpA::NCH);
+      if (q < FN) b1[q] = rb.read(cur, 1, q);
+      else if (q < FN + FM) a1[q - FN] = ra.read(cur, 1, q - FN);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < FM * FN; ++q) {
+      acc[q / FN][q % FN] = mfma32<DT>(b1[q % FN], a1[q / FN], acc[q / FN][q % FN]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < FN) b0[q] = rb.read(nxt, 0, q);
+      else if (q < FN + FM) a0[q - FN] = ra.read(nxt, 0, q - FN);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // drain the copies issued past the end (they read nothing) and all LDS
+  // reads before the staging area reuses the stages
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+  __syncthreads();
+
+  epilogue_lds<TL, DT>(p, acc, reinterpret_cast<float*>(lds_raw), m0, n0, t);
+}
+
+}  // namespace trt

@@ -33,6 +33,7 @@ namespace trt {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -78,6 +79,19 @@ __device__ __forceinline__ f32x4 mfma16<DT_BF16>(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // ---- kernel arguments --------------------------------------------------------------
 
 struct GemmArgs {
@@ -91,6 +105,7 @@ struct GemmArgs {
   int32_t relu;
   int32_t epi_vec;       // 8-byte vector epilogue allowed (alignment holds)
   int32_t tiles_m, tiles_n;
+  int64_t a_bytes, b_bytes;  // byte extents of the A and B operands
 };
 
 // Workgroup id -> (tile row, tile column).  Consecutive workgroup ids are
@@ -221,6 +236,74 @@ template <class TL, int R, bool KC, bool VEC>
 using Operand = typename std::conditional<KC, KContigOperand<TL, R, VEC>,
                                           MNContigOperand<TL, R, VEC>>::type;
 
+// ---- fused epilogue --------------------------------------------------------------
+// Per accumulator register ("My Triton From Scratch, Part 16: Register Tiles",
+// sections "Pointer tiles" and "Masks and stores"): the register's (row, col)
+// comes from the tile's ownership map, the bias is read once per owned column
+// (it is broadcast along m), y = relu(acc + bias) + R is evaluated in fp32,
+// rounded once to the output type, and stored under its own mask.  A lane
+// owns four consecutive columns of a row per fragment, stored as one 8-byte
+// vector when the whole run is in range and the buffers are aligned.
+template <class TL, int DT, class AccT>
+__device__ __forceinline__ void epilogue_store(const GemmArgs& p,
+                                               const AccT (&acc)[TL::FM][TL::FN], int m0,
+                                               int n0, int lane, int wave) {
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < TL::FRAG_REGS / 4; ++q) {
+        const int reg = TL::FRAG_REGS * (i * TL::FN + j) + 4 * q;
+        const int m = m0 + TL::owner_row(reg, lane, wave);
+        const int n = n0 + TL::owner_col(reg, lane, wave);  // this run: n..n+3
+        if (m >= p.M) continue;
+        float y[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+        const bool vec = p.epi_vec && (n + 4 <= p.N);
+        if (p.bias) {
+          if (vec) {
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+            y[0] += to_f32<DT>(bb[0] & 0xFFFFu); y[1] += to_f32<DT>(bb[0] >> 16);
+            y[2] += to_f32<DT>(bb[1] & 0xFFFFu); y[3] += to_f32<DT>(bb[1] >> 16);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) y[e] += to_f32<DT>(p.bias[n + e]);
+          }
+        }
+        if (p.relu) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
+        }
+        if (p.R) {
+          const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
+          if (vec) {
+            const u32x2 rr = *reinterpret_cast<const u32x2*>(rp);
+            y[0] += to_f32<DT>(rr[0] & 0xFFFFu); y[1] += to_f32<DT>(rr[0] >> 16);
+            y[2] += to_f32<DT>(rr[1] & 0xFFFFu); y[3] += to_f32<DT>(rr[1] >> 16);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
+          }
+        }
+        uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
+        if (vec) {
+          u32x2 o;
+          o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
+          o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
+          *reinterpret_cast<u32x2*>(cp) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+        }
+      }
+    }
+  }
+}
+
 // ---- the kernel -------------------------------------------------------------------
 
 // A_KC: A stored with k contiguous (op N); otherwise A^T (op T).
@@ -228,6 +311,7 @@ using Operand = typename std::conditional<KC, KContigOperand<TL, R, VEC>,
 // VEC:  16-byte aligned operand rows, so chunks load as one vector.
 template <class TL, int DT, bool A_KC, bool B_KC, bool VEC>
 __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs p) {
+  static_assert(TL::MF == 16, "the generic kernel runs 16x16x32 fragments");
   constexpr int G = TL::G;
   __shared__ u32x4 lds[2][(TL::BM + TL::BN) * G];
 
@@ -296,57 +380,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- fused epilogue: per register, y = relu(acc + bias) + R, one cast ----
-#pragma unroll
-  for (int i = 0; i < TL::FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int reg = 4 * (i * TL::FN + j);
-      const int m = m0 + TL::owner_row(reg, lane, wave);
-      const int n = n0 + TL::owner_col(reg, lane, wave);  // this lane's 4 columns n..n+3
-      if (m >= p.M) continue;
-      float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      const bool vec = p.epi_vec && (n + 4 <= p.N);
-      if (p.bias) {
-        if (vec) {
-          const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-          y[0] += to_f32<DT>(bb[0] & 0xFFFFu); y[1] += to_f32<DT>(bb[0] >> 16);
-          y[2] += to_f32<DT>(bb[1] & 0xFFFFu); y[3] += to_f32<DT>(bb[1] >> 16);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) y[e] += to_f32<DT>(p.bias[n + e]);
-        }
-      }
-      if (p.relu) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
-      }
-      if (p.R) {
-        const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
-        if (vec) {
-          const u32x2 rr = *reinterpret_cast<const u32x2*>(rp);
-          y[0] += to_f32<DT>(rr[0] & 0xFFFFu); y[1] += to_f32<DT>(rr[0] >> 16);
-          y[2] += to_f32<DT>(rr[1] & 0xFFFFu); y[3] += to_f32<DT>(rr[1] >> 16);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
-        }
-      }
-      uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
-      if (vec) {
-        u32x2 o;
-        o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
-        o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
-        *reinterpret_cast<u32x2*>(cp) = o;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
-      }
-    }
-  }
+  epilogue_store<TL, DT>(p, acc, m0, n0, lane, wave);
 }
 
 }  // namespace trt

@@ -15,14 +15,21 @@
 // rank, i.e. every output element is owned exactly once ("Triton
 // LinearLayout", section "Surjectivity, injectivity, and broadcasts").
 //
-// Matrix-core fragments (v_mfma_f32_16x16x32_{f16,bf16}, one wave):
-//   operand 0 (16 x 32): lane l holds row l%16, k = 8*(l/16) + e, e = 0..7
-//   operand 1 (32 x 16): lane l holds column l%16, the same k rule
-//   result    (16 x 16): lane l, register r holds row 4*(l/16) + r, col l%16
-// The kernel feeds the B tile (rows = n) to operand 0 and the A tile
-// (rows = m) to operand 1, so a fragment result is a C^T fragment: lane l,
-// register r holds C(l%16, 4*(l/16) + r) -- four consecutive columns per
-// lane, which the epilogue stores as one 8-byte vector.
+// Matrix-core fragments, one wave of 64 lanes (AMD's documented register
+// layouts of v_mfma_f32_16x16x32_* and v_mfma_f32_32x32x16_*):
+//   16x16x32: operand 0 (16 x 32): lane l holds row l%16, k = 8*(l/16) + e;
+//             operand 1 (32 x 16): column l%16, the same k rule;
+//             result (16 x 16): lane l, register r is row 4*(l/16) + r, col l%16.
+//   32x32x16: operand 0 (32 x 16): lane l holds row l%32, k = 8*(l/32) + e;
+//             operand 1 (16 x 32): column l%32, the same k rule;
+//             result (32 x 32): lane l, register r is row 8*(r/4) + 4*(l/32) + r%4,
+//             col l%32.
+// The k rule only has to agree between the two operands (the instruction
+// sums over k slots).  The kernels feed the B tile (rows = n) to operand 0
+// and the A tile (rows = m) to operand 1, so a fragment result is a C^T
+// fragment: every run of four consecutive registers of a lane holds four
+// consecutive columns of one C row, which the epilogue stores as one 8-byte
+// vector.
 #pragma once
 
 #include <stdint.h>
@@ -86,7 +93,7 @@ struct Gf2Map {
 // ---------------------------------------------------------------------------
 // A workgroup tile: logical shape, thread shape, register shape.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MF_ = 16>
 struct Tile {
   // logical tile and K step
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
@@ -94,32 +101,38 @@ struct Tile {
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
-  // per-wave sub-tile, in 16 x 16 fragments
+  // per-wave sub-tile, in MF x MF matrix-core fragments (MF = 16 or 32)
+  static constexpr int MF = MF_;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  static constexpr int FM = WTM / MF, FN = WTN / MF;
   // register shape: accumulator registers per lane
-  static constexpr int REGS = FM * FN * 4;
+  static constexpr int FRAG_REGS = MF * MF / 64;
+  static constexpr int REGS = FM * FN * FRAG_REGS;
   // operand tiles in LDS: G chunks of 8 k (16 bytes) per row
   static constexpr int G = BK / 8;
   static constexpr int KSUB = BK / 32;  // matrix-core k steps per K step
 
   static_assert(is_pow2(BM) && is_pow2(BN) && is_pow2(BK), "power-of-two tiles");
   static_assert(is_pow2(WM) && is_pow2(WN), "power-of-two wave grid");
-  static_assert(WTM >= 16 && WTN >= 16 && WTM % 16 == 0 && WTN % 16 == 0,
-                "each wave owns whole 16x16 fragments");
+  static_assert(MF == 16 || MF == 32, "16x16 or 32x32 fragments");
+  static_assert(WTM >= MF && WTN >= MF && WTM % MF == 0 && WTN % MF == 0,
+                "each wave owns whole fragments");
   static_assert(BK >= 32 && BK % 32 == 0 && G <= 8, "K step: 32 or 64");
   static_assert(THREADS <= 1024, "1024 work-items per workgroup at most");
   static_assert(BM % 8 == 0 && BN % 8 == 0, "8x8 transpose blocks");
 
   // ---- C ownership, as the kernel evaluates it ----------------------------
-  // Register index reg = 4*(fm*FN + fn) + r.
+  // Register index reg = FRAG_REGS*(fm*FN + fn) + r.
   TRT_HD static int owner_row(int reg, int lane, int wave) {
-    const int fm = (reg >> 2) / FN;
-    return (wave / WN) * WTM + 16 * fm + (lane & 15);
+    const int fm = (reg / FRAG_REGS) / FN;
+    return (wave / WN) * WTM + MF * fm + (lane & (MF - 1));
   }
   TRT_HD static int owner_col(int reg, int lane, int wave) {
-    const int fn = (reg >> 2) % FN;
-    return (wave % WN) * WTN + 16 * fn + 4 * (lane >> 4) + (reg & 3);
+    const int fn = (reg / FRAG_REGS) % FN;
+    const int r = reg % FRAG_REGS;
+    const int in_frag = MF == 16 ? 4 * (lane >> 4) + r
+                                 : 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    return (wave % WN) * WTN + MF * fn + in_frag;
   }
 
   // ---- the same ownership as GF(2) bases -----------------------------------
@@ -135,11 +148,19 @@ struct Tile {
     int i = 0;
     m.b[i++] = {0, 1};                                  // r bit 0
     m.b[i++] = {0, 2};                                  // r bit 1
-    for (int s = 0; s < ilog2(FN); ++s) m.b[i++] = {0, 16 << s};   // fn
-    for (int s = 0; s < ilog2(FM); ++s) m.b[i++] = {16 << s, 0};   // fm
-    m.b[i++] = {1, 0}; m.b[i++] = {2, 0};               // lane bits 0-3: row
-    m.b[i++] = {4, 0}; m.b[i++] = {8, 0};
-    m.b[i++] = {0, 4}; m.b[i++] = {0, 8};               // lane bits 4-5: col
+    if (MF == 32) {
+      m.b[i++] = {0, 8};                                // r bit 2
+      m.b[i++] = {0, 16};                               // r bit 3
+    }
+    for (int s = 0; s < ilog2(FN); ++s) m.b[i++] = {0, MF << s};   // fn
+    for (int s = 0; s < ilog2(FM); ++s) m.b[i++] = {MF << s, 0};   // fm
+    for (int s = 0; s < ilog2(MF); ++s) m.b[i++] = {1 << s, 0};    // lane: row
+    if (MF == 16) {
+      m.b[i++] = {0, 4};                                // lane bits 4-5: col
+      m.b[i++] = {0, 8};
+    } else {
+      m.b[i++] = {0, 4};                                // lane bit 5: col
+    }
     for (int s = 0; s < ilog2(WN); ++s) m.b[i++] = {0, WTN << s};  // wave col
     for (int s = 0; s < ilog2(WM); ++s) m.b[i++] = {WTM << s, 0};  // wave row
     return m;
@@ -161,8 +182,8 @@ struct Tile {
 
   static_assert(c_map().bijective(),
                 "C ownership must cover every tile element exactly once");
-  static_assert(owner_matches_bases(),
-                "kernel ownership arithmetic must equal its GF(2) bases");
+  // The exhaustive owner_matches_bases() check runs once per compiled tile,
+  // in the library's tile registry.
 
   // ---- LDS operand tiles ----------------------------------------------------
   // Chunk (r, g) of a tile with R rows lives in 16-byte slot
@@ -175,6 +196,36 @@ struct Tile {
     return ((r >> (3 - ilog2(G))) ^ (r >> 3)) & (G - 1);
   }
   TRT_HD static int lds_slot(int r, int g) { return r * G + (g ^ lds_swz(r)); }
+
+  // ---- direct-to-LDS operand tiles (K step of 32) ---------------------------
+  // The pipelined kernel copies global memory straight into LDS, 16 bytes per
+  // lane: the lanes of one wave instruction fill 64 consecutive 16-byte slots,
+  // so the swizzle is applied on the global side -- each lane fetches the
+  // chunk that belongs in its slot (the inverse maps below).
+  //
+  // k-contiguous operand, [R rows][4 chunks of 8 k]: chunk (r, g) in slot
+  // 4r + (g XOR sk(r)), sk(r) = (r1 XOR r3) | r2 << 1 in the bits of r.  A
+  // fragment read (16 consecutive rows, one g, 16 bytes per lane) covers every
+  // bank once per 8 rows (128-byte window) and per 16 rows (256-byte window);
+  // sk only uses bits 1-3 of r, so fragments 16 rows apart differ by a
+  // constant address offset.
+  TRT_HD static int kc_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+  TRT_HD static int kc_slot(int r, int g) { return 4 * r + (g ^ kc_swz(r)); }
+  TRT_HD static int kc_slot_row(int s) { return s >> 2; }
+  TRT_HD static int kc_slot_g(int s) { return (s & 3) ^ kc_swz(s >> 2); }
+  // rows-contiguous operand, [32 k rows][R/8 chunks of 8 rows]: chunk (k, c)
+  // in slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*k0 XOR 12*k1 in the bits of k.
+  // A transposing fragment read covers 4 consecutive k rows: 32 bytes of each
+  // per 16 lanes, 64 bytes of each per 32 lanes.  sm sends the four rows to
+  // four distinct 32-byte slots of a 128-byte window (bits 1-2) and four
+  // distinct 64-byte slots of a 256-byte window (bits 2-3).
+  TRT_HD static int mn_swz(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 12 : 0); }
+  template <int R>
+  TRT_HD static int mn_slot(int k, int c) { return k * (R / 8) + (c ^ mn_swz(k)); }
+  template <int R>
+  TRT_HD static int mn_slot_k(int s) { return s / (R / 8); }
+  template <int R>
+  TRT_HD static int mn_slot_c(int s) { return (s % (R / 8)) ^ mn_swz(s / (R / 8)); }
 
   // ---- cooperative copies ---------------------------------------------------
   // "My Triton From Scratch, Part 12: CUDA Tile Layouts", section

@@ -1,0 +1,26 @@
+// tiles.hpp -- the compiled workgroup tiles and their launch entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_kernel.hpp"
+
+namespace trt {
+
+using TileTiny = Tile<16, 64, 32, 1, 1>;       // one wave, the named GEMM's tile
+using Tile64 = Tile<64, 64, 64, 2, 2>;         // 4 waves, 32x32 each
+using Tile128 = Tile<128, 128, 64, 2, 2>;      // 4 waves, 64x64 each
+using Tile256 = Tile<256, 256, 64, 2, 2>;      // 4 waves, 128x128 each
+using Tile256D = Tile<256, 256, 32, 2, 2, 32>; // pipelined, 32x32x16 fragments
+using Tile256F = Tile<256, 256, 32, 2, 2, 16>; // generic kernel on the pipelined tile
+
+// Launch the generic kernel of tile TL (defined, and explicitly instantiated
+// per tile, in the kern_*.hip translation units).
+template <class TL>
+void launch_generic(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s);
+
+// Launch the pipelined direct-to-LDS kernel of tile TL.
+template <class TL>
+void launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s);
+
+}  // namespace trt

@@ -7,6 +7,7 @@
 
 #include "../../include/trt.h"
 #include "gemm_kernel.hpp"
+#include "tiles.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -30,43 +31,41 @@ using trt::GemmArgs;
 
 // ---- compiled tiles ------------------------------------------------------------
 
-using TileTiny = trt::Tile<16, 64, 32, 1, 1>;    // one wave, the named GEMM's tile
-using Tile64 = trt::Tile<64, 64, 64, 2, 2>;      // 4 waves, 32x32 each
-using Tile128 = trt::Tile<128, 128, 64, 2, 2>;   // 4 waves, 64x64 each
-using Tile256 = trt::Tile<256, 256, 64, 2, 2>;   // 4 waves, 128x128 each
+using trt::Tile256;
+using trt::Tile256D;
+using trt::Tile64;
+using trt::Tile128;
+using trt::TileTiny;
 
-template <class TL, int DT, bool AKC, bool BKC>
-void launch_vec(const GemmArgs& a, bool vec, dim3 grid, hipStream_t s) {
-  if (vec)
-    hipLaunchKernelGGL((trt::gemm_kernel<TL, DT, AKC, BKC, true>), grid, dim3(TL::THREADS), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((trt::gemm_kernel<TL, DT, AKC, BKC, false>), grid, dim3(TL::THREADS), 0,
-                       s, a);
-}
-
-template <class TL, int DT>
-void launch_ops(const GemmArgs& a, int opA, int opB, bool vec, dim3 grid, hipStream_t s) {
-  const bool akc = opA == TRT_OP_N, bkc = opB == TRT_OP_T;
-  if (akc && bkc) launch_vec<TL, DT, true, true>(a, vec, grid, s);
-  else if (akc) launch_vec<TL, DT, true, false>(a, vec, grid, s);
-  else if (bkc) launch_vec<TL, DT, false, true>(a, vec, grid, s);
-  else launch_vec<TL, DT, false, false>(a, vec, grid, s);
+// Whether the pipelined direct-to-LDS kernel applies: aligned 16-byte operand
+// rows; every 16-byte copy wholly inside or wholly outside its operand's
+// extent (the buffer record check drops a copy that straddles the end as a
+// whole), i.e. K % 8 == 0 for a k-contiguous operand and M (N) % 8 == 0 for
+// a rows-contiguous A (B); operand extents addressable by 32-bit offsets.
+bool dma_ok(const GemmArgs& a, int opA, int opB, bool vec) {
+  const bool a_kc = opA == TRT_OP_N, b_kc = opB == TRT_OP_T;
+  return vec && (a_kc ? a.K % 8 == 0 : a.M % 8 == 0) && (b_kc ? a.K % 8 == 0 : a.N % 8 == 0) &&
+         a.a_bytes < (int64_t(1) << 31) && a.b_bytes < (int64_t(1) << 31);
 }
 
 template <class TL>
 void launch_tile(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
-  a.tiles_m = (a.M + TL::BM - 1) / TL::BM;
-  a.tiles_n = (a.N + TL::BN - 1) / TL::BN;
-  const dim3 grid(a.tiles_m * a.tiles_n);
-  if (dt == TRT_F16) launch_ops<TL, trt::DT_F16>(a, opA, opB, vec, grid, s);
-  else launch_ops<TL, trt::DT_BF16>(a, opA, opB, vec, grid, s);
+  trt::launch_generic<TL>(a, dt, opA, opB, vec, s);
+}
+
+// The pipelined tile: the direct-to-LDS kernel when it applies, otherwise the
+// generic kernel on the same logical tile (with 16x16 fragments).
+template <class TL>
+void launch_tile_dma(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
+  if (!dma_ok(a, opA, opB, vec)) return trt::launch_generic<trt::Tile256F>(a, dt, opA, opB, vec, s);
+  trt::launch_pipelined<TL>(a, dt, opA, opB, s);
 }
 
 // ---- layout maps (host and device evaluate the same functions) ---------------
 
 template <class TL>
 TRT_HD int64_t map_size(int map) {
+  constexpr bool dma = TL::BK == 32;
   using KA = typename TL::template KContig<TL::BM>;
   using MA = typename TL::template MNContig<TL::BM>;
   using KB = typename TL::template KContig<TL::BN>;
@@ -79,6 +78,10 @@ TRT_HD int64_t map_size(int map) {
     case TRT_MAP_COPY_MNCONTIG_A: return (int64_t)MA::ITERS * TL::THREADS;
     case TRT_MAP_COPY_KCONTIG_B: return (int64_t)KB::ITERS * TL::THREADS;
     case TRT_MAP_COPY_MNCONTIG_B: return (int64_t)MB::ITERS * TL::THREADS;
+    case TRT_MAP_DMA_KC_SLOT_A: return dma ? (int64_t)TL::BM * 4 : -1;
+    case TRT_MAP_DMA_KC_SLOT_B: return dma ? (int64_t)TL::BN * 4 : -1;
+    case TRT_MAP_DMA_MN_SLOT_A: return dma && TL::BM >= 128 ? (int64_t)32 * (TL::BM / 8) : -1;
+    case TRT_MAP_DMA_MN_SLOT_B: return dma && TL::BN >= 128 ? (int64_t)32 * (TL::BN / 8) : -1;
     default: return -1;
   }
 }
@@ -117,6 +120,19 @@ TRT_HD void eval_map(int map, int64_t x, int& r, int& c) {
     case TRT_MAP_COPY_MNCONTIG_A: eval_mncontig<TL, typename TL::template MNContig<TL::BM>>(x, r, c); return;
     case TRT_MAP_COPY_KCONTIG_B: eval_kcontig<TL, typename TL::template KContig<TL::BN>>(x, r, c); return;
     case TRT_MAP_COPY_MNCONTIG_B: eval_mncontig<TL, typename TL::template MNContig<TL::BN>>(x, r, c); return;
+    case TRT_MAP_DMA_KC_SLOT_A:
+    case TRT_MAP_DMA_KC_SLOT_B:
+      r = TL::kc_slot((int)(x / 4), (int)(x % 4));
+      c = 0;
+      return;
+    case TRT_MAP_DMA_MN_SLOT_A:
+      r = TL::template mn_slot<TL::BM>((int)(x / (TL::BM / 8)), (int)(x % (TL::BM / 8)));
+      c = 0;
+      return;
+    case TRT_MAP_DMA_MN_SLOT_B:
+      r = TL::template mn_slot<TL::BN>((int)(x / (TL::BN / 8)), (int)(x % (TL::BN / 8)));
+      c = 0;
+      return;
     default: r = c = -1; return;
   }
 }
@@ -138,10 +154,17 @@ __global__ __launch_bounds__(64) void probe_kernel(const trt::u32x4* a, const tr
   c[l] = trt::mfma16<DT>(a[l], b[l], trt::f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
+template <int DT>
+__global__ __launch_bounds__(64) void probe32_kernel(const trt::u32x4* a, const trt::u32x4* b,
+                                                      trt::f32x16* c) {
+  const int l = threadIdx.x;
+  c[l] = trt::mfma32<DT>(a[l], b[l], trt::f32x16{});
+}
+
 // ---- tile registry ---------------------------------------------------------------
 
 struct TileEntry {
-  int bm, bn, bk, wm, wn, regs;
+  int bm, bn, bk, wm, wn, regs, frag;
   void (*launch)(GemmArgs, int, int, int, bool, hipStream_t);
   int64_t (*size)(int);
   void (*eval)(int, int64_t, int&, int&);
@@ -162,15 +185,24 @@ int64_t size_host(int map) { return map_size<TL>(map); }
 template <class TL>
 void eval_host(int map, int64_t x, int& r, int& c) { eval_map<TL>(map, x, r, c); }
 
-template <class TL>
+template <class TL, bool DMA>
+constexpr auto launcher() {
+  if constexpr (DMA) return &launch_tile_dma<TL>;
+  else return &launch_tile<TL>;
+}
+
+template <class TL, bool DMA = false>
 constexpr TileEntry entry() {
-  return TileEntry{TL::BM, TL::BN, TL::BK, TL::WM, TL::WN, TL::REGS,
-                   &launch_tile<TL>, &size_host<TL>, &eval_host<TL>, &dump_launch<TL>,
+  static_assert(TL::owner_matches_bases(),
+                "kernel ownership arithmetic must equal its GF(2) bases");
+  return TileEntry{TL::BM, TL::BN, TL::BK, TL::WM, TL::WN, TL::REGS, TL::MF,
+                   launcher<TL, DMA>(), &size_host<TL>,
+                   &eval_host<TL>, &dump_launch<TL>,
                    TL::c_map().rank(), TL::C_IN_BITS, trt::ilog2(TL::BM * TL::BN)};
 }
 
 const TileEntry kTiles[] = {entry<TileTiny>(), entry<Tile64>(), entry<Tile128>(),
-                            entry<Tile256>()};
+                            entry<Tile256>(), entry<Tile256D, true>()};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 const TileEntry* find_tile(const trt_tile* t) {
@@ -185,7 +217,7 @@ const TileEntry* find_tile(const trt_tile* t) {
 const TileEntry* choose_tile(int64_t M, int64_t N) {
   auto count = [&](const TileEntry& e) { return ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn); };
   if (M <= 16) return &kTiles[0];
-  if (count(kTiles[3]) >= 192) return &kTiles[3];
+  if (count(kTiles[4]) >= 192) return &kTiles[4];
   if (count(kTiles[2]) >= 128) return &kTiles[2];
   return &kTiles[1];
 }
@@ -233,6 +265,11 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   a.N = (int32_t)N;
   a.K = (int32_t)K;
   a.relu = (epi && epi->relu) ? 1 : 0;
+  int64_t sa = 0, sb = 0;
+  trt::span_bytes(opA ? K : M, opA ? M : K, lda, sa);
+  trt::span_bytes(opB ? N : K, opB ? K : N, ldb, sb);
+  a.a_bytes = sa;
+  a.b_bytes = sb;
   // 16-byte operand vectors need 16-byte aligned bases and rows.
   const bool vec = aligned(A, 16) && aligned(B, 16) && lda % 8 == 0 && ldb % 8 == 0;
   // 8-byte epilogue vectors need 8-byte aligned C, bias, residual rows.
@@ -252,13 +289,14 @@ trt_status trt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 int32_t trt_tile_count(void) { return kNumTiles; }
 
 trt_status trt_tile_at(int32_t i, trt_tile* tile, int32_t* waves_m, int32_t* waves_n,
-                       int32_t* regs_per_lane) {
+                       int32_t* regs_per_lane, int32_t* frag) {
   if (i < 0 || i >= kNumTiles) return fail(TRT_ERR_ARG, "tile index out of range");
   const TileEntry& e = kTiles[i];
   if (tile) *tile = trt_tile{e.bm, e.bn, e.bk};
   if (waves_m) *waves_m = e.wm;
   if (waves_n) *waves_n = e.wn;
   if (regs_per_lane) *regs_per_lane = e.regs;
+  if (frag) *frag = e.frag;
   g_err.clear();
   return TRT_OK;
 }
@@ -313,20 +351,30 @@ trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank, int32_t* in_bits
   return TRT_OK;
 }
 
-trt_status trt_mfma_probe(int32_t dtype, const void* a, const void* b, float* c, void* stream) {
+trt_status trt_mfma_probe(int32_t dtype, int32_t shape, const void* a, const void* b, float* c,
+                          void* stream) {
   if (!a || !b || !c) return fail(TRT_ERR_NULL, "a, b and c must be non-null");
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
     return fail(TRT_ERR_ALIGN, "a, b and c must be 16-byte aligned");
+  if (dtype != TRT_F16 && dtype != TRT_BF16)
+    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16 or TRT_BF16");
+  if (shape != 16 && shape != 32) return fail(TRT_ERR_ARG, "shape must be 16 or 32");
   const auto* av = static_cast<const trt::u32x4*>(a);
   const auto* bv = static_cast<const trt::u32x4*>(b);
-  auto* cv = reinterpret_cast<trt::f32x4*>(c);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == TRT_F16)
-    hipLaunchKernelGGL((probe_kernel<trt::DT_F16>), dim3(1), dim3(64), 0, s, av, bv, cv);
-  else if (dtype == TRT_BF16)
-    hipLaunchKernelGGL((probe_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
-  else
-    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16 or TRT_BF16");
+  if (shape == 16) {
+    auto* cv = reinterpret_cast<trt::f32x4*>(c);
+    if (dtype == TRT_F16)
+      hipLaunchKernelGGL((probe_kernel<trt::DT_F16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+    else
+      hipLaunchKernelGGL((probe_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+  } else {
+    auto* cv = reinterpret_cast<trt::f32x16*>(c);
+    if (dtype == TRT_F16)
+      hipLaunchKernelGGL((probe32_kernel<trt::DT_F16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+    else
+      hipLaunchKernelGGL((probe32_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+  }
   return check_launch("probe launch");
 }
 
