@@ -57,8 +57,9 @@ def committed_traffic(workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the clock settles under sustained load")
     ap.add_argument("--workload", default="square")
     ap.add_argument("--tile", default=None, help="BM,BN,BK")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,

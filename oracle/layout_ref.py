@@ -378,3 +378,14 @@ def dma_kc_slot(r, g):
 def dma_mn_slot(R, k, c):
     sm = (6 * _bit(k, 0)) ^ (12 * _bit(k, 1))
     return k * (R // 8) + (c ^ sm)
+
+
+# --------------------------------------------------------------------------
+# The streaming tile for M <= 16 ([16, 64], 8 waves)
+# --------------------------------------------------------------------------
+# After the waves' partial tiles are summed, thread t = 64*wave + lane owns
+# the two consecutive columns 2*(t % 32), 2*(t % 32) + 1 of row t // 32.
+
+def skinny_c_owner(reg, lane, wave):
+    t = 64 * wave + lane
+    return (t // 32, 2 * (t % 32) + reg)

@@ -134,11 +134,14 @@ def test_tile_table():
         kl = L.kernel_layout((bm, bn), (wm, 64 * wn))
         assert kl["threads_per_block"] <= 1024
         assert regs * 64 * wm * wn == bm * bn
-        assert fr in (16, 32) and regs % (fr * fr // 64) == 0
+        assert fr in (16, 32)
+        if bk != 256:   # the streaming tile owns reduced outputs, not fragments
+            assert regs % (fr * fr // 64) == 0
 
 
 ALL_TILES = [(16, 64, 32, 1, 1, 16), (64, 64, 64, 2, 2, 16), (128, 128, 64, 2, 2, 16),
-             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 2, 32)]
+             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 2, 32), (16, 64, 256, 8, 1, 16)]
+SKINNY = (16, 64, 256, 8, 1, 16)
 
 
 def test_all_tiles_listed():
@@ -150,10 +153,12 @@ def test_c_owner_matches_oracle(cfg):
     assert cfg in tile_configs()
     tile = cfg[:3]
     rows, cols = trt.layout_dump_host(trt.MAP_C_OWNER, tile)
-    regs = L.gemm_regs_per_lane(cfg)
+    regs = 2 if cfg == SKINNY else L.gemm_regs_per_lane(cfg)
+    owner = (lambda r, l, w: L.skinny_c_owner(r, l, w)) if cfg == SKINNY else \
+        (lambda r, l, w: L.gemm_c_owner(cfg, r, l, w))
     x = np.arange(rows.size)
     reg, lane, wave = x % regs, (x // regs) % 64, x // (regs * 64)
-    exp = np.array([L.gemm_c_owner(cfg, int(r), int(l), int(w))
+    exp = np.array([owner(int(r), int(l), int(w))
                     for r, l, w in zip(reg, lane, wave)], dtype=np.int32)
     assert np.array_equal(rows, exp[:, 0]) and np.array_equal(cols, exp[:, 1])
     # exactly once over the tile
@@ -197,3 +202,6 @@ def test_dma_slot_maps_match_oracle():
         assert slot.tolist() == [L.dma_mn_slot(R, k, c) for k in range(32) for c in range(R // 8)]
     # not defined for tiles without the 32-wide K step
     assert trt.layout_size(trt.MAP_DMA_KC_SLOT_A, (256, 256, 64)) == -1
+    # the streaming tile has only its ownership map
+    assert trt.layout_size(trt.MAP_C_OWNER, (16, 64, 256)) == 1024
+    assert all(trt.layout_size(m, (16, 64, 256)) == -1 for m in range(1, 11))

@@ -78,7 +78,7 @@ def test_mfma_probe_one_hot():
 # ---- device layout maps == host maps (== oracle, checked on the CPU) ----------
 
 @pytest.mark.parametrize("tile", [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64),
-                                  (256, 256, 32)])
+                                  (256, 256, 32), (16, 64, 256)])
 def test_layout_dump_device_equals_host(tile):
     for mid in range(11):
         if trt.layout_size(mid, tile) < 0:
@@ -177,6 +177,37 @@ def test_pipelined_tile_ragged_shapes():
         run.launch()
         assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
                       what=f"M={M} N={N} K={K} op={opA}{opB} dt={dt}")
+
+
+def test_streaming_tile_shapes():
+    # the M <= 16 streaming kernel: every M up to 16, K and N edges, split-K
+    # slices of unequal length, epilogue combinations, both dtypes
+    rng = np.random.default_rng(13)
+    for trial in range(30):
+        M = 1 + trial % 16
+        N = 4 * int(rng.integers(1, 200))
+        K = 8 * int(rng.integers(1, 300))
+        dt = W.F16 if trial % 3 else W.BF16
+        w = W.Workload("skinny-bf", M, N, K, lda=K + 8 * (trial % 2), ldb=N + 4 * (trial % 3),
+                       dtype=dt, dist="ternary", seed=3000 + trial, bias=bool(trial % 2),
+                       relu=bool(trial % 4 == 1), residual=bool(trial % 3 == 0),
+                       tile=(16, 64, 256))
+        run = Run(w, ldc=N + (trial % 5))
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
+                      what=f"M={M} N={N} K={K} dt={dt}")
+
+
+def test_streaming_tile_falls_back():
+    # shapes the streaming kernel does not take still compute correctly on
+    # the same logical tile (generic kernel)
+    for M, N, K, opA, opB in [(5, 70, 30, 0, 0), (16, 64, 64, 1, 0), (16, 64, 64, 0, 1)]:
+        w = W.Workload("skinny-fb", M, N, K, opA=opA, opB=opB, dtype=W.F16, dist="ternary",
+                       seed=41, tile=(16, 64, 256))
+        run = Run(w)
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), W.F16, exact=True,
+                      what=f"fallback M={M} N={N} K={K} op={opA}{opB}")
 
 
 def test_deterministic_runs():

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["trt.hip", "kern_tiny.hip", "kern_64.hip", "kern_128.hip", "kern_256.hip",
-           "kern_256f.hip", "kern_dma256.hip"]
+           "kern_256f.hip", "kern_dma256.hip", "kern_skinny.hip"]
 LIB = os.path.join(HERE, "libtrt.so")
 ARCH = "gfx950"
 

@@ -206,8 +206,25 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&a
         if (n + e < p.N) bias[e] = to_f32<DT>(p.bias[n + e]);
     }
   }
+  constexpr int ITERS = HALF_ROWS / ROWS_PER_IT;
+  // staged row -> tile row: the wave row block, then the pass's half of it
+  auto tile_row = [&](int pass, int prow) {
+    return (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
+           prow % (HALF_ROWS / TL::WM);
+  };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
+    // residual loads of the whole pass go out first, so their latency is
+    // paid once per pass and overlaps the staging writes
+    u32x2 rr[ITERS];
+    if (p.R && vec) {
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int m = m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW);
+        rr[it] = m < p.M ? *reinterpret_cast<const u32x2*>(p.R + (int64_t)m * p.ldr + n)
+                         : u32x2{0u, 0u};
+      }
+    }
     // accumulators of fragment rows fm = 2*pass, 2*pass+1 -> staged rows
     // prow = 64*wr + 32*(fm - 2*pass) + lane%32
 #pragma unroll
@@ -225,13 +242,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&a
         }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int it = 0; it < HALF_ROWS / ROWS_PER_IT; ++it) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
       const int prow = it * ROWS_PER_IT + t / T_PER_ROW;
-      // staged row -> tile row: wave row block, then the pass's half of it
-      const int mt = (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
-                     prow % (HALF_ROWS / TL::WM);
-      const int m = m0 + mt;
+      const int m = m0 + tile_row(pass, prow);
       if (m >= p.M) continue;
       const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow * PITCH + col);
       float y[4] = {a4[0] + bias[0], a4[1] + bias[1], a4[2] + bias[2], a4[3] + bias[3]};
@@ -240,12 +254,11 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&a
         for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
       }
       if (p.R) {
-        const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
         if (vec) {
-          const u32x2 rr = *reinterpret_cast<const u32x2*>(rp);
-          y[0] += to_f32<DT>(rr[0] & 0xFFFFu); y[1] += to_f32<DT>(rr[0] >> 16);
-          y[2] += to_f32<DT>(rr[1] & 0xFFFFu); y[3] += to_f32<DT>(rr[1] >> 16);
+          y[0] += to_f32<DT>(rr[it][0] & 0xFFFFu); y[1] += to_f32<DT>(rr[it][0] >> 16);
+          y[2] += to_f32<DT>(rr[it][1] & 0xFFFFu); y[3] += to_f32<DT>(rr[it][1] >> 16);
         } else {
+          const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);

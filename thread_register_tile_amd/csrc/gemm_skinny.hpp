@@ -1,0 +1,167 @@
+// gemm_skinny.hpp -- the GEMM for M <= 16: a pure stream over B.
+//
+// With at most 16 rows of A, each element of B is used by at most 16
+// products: the operation is bound by reading B from HBM once.  One
+// workgroup owns a 64-column panel of C ([16, 64], the tile of the NineToothed
+// "Named layouts" GEMM arrangement) and all of K.  Its 8 waves split K between
+// them; each wave streams its slice of the panel straight from global memory
+// into registers -- no LDS on the way -- keeping DEPTH iterations of loads in
+// flight, and accumulates a partial [16, 64] tile on the 16x16x32 matrix
+// cores.  The 8 partial tiles are summed through LDS in a fixed order
+// (deterministic, no atomics) and the fused epilogue stores the panel.
+//
+// One iteration of a wave covers 32 k x 64 columns of B: lane l loads 8 bytes
+// (4 columns, n = 4*(l%16)) of the 8 k rows 8*(l/16) .. 8*(l/16)+7, and
+// transposes the 8 x 4 block in registers into four operand registers of 8
+// k values, one per column n + j.  Product j then covers the 16 columns
+// {4i + j : i = 0..15} (operand column i is lane l%16 = i).  A's operand (16
+// rows, 8 consecutive k per lane) is one 16-byte load.
+//
+// Requirements (checked by the dispatcher): A stored k-contiguous and B
+// row-major; 16-byte aligned A rows (lda % 8 == 0), 8-byte aligned B rows
+// (ldb % 4 == 0); K % 8 == 0 and N % 4 == 0, so that every vector load is
+// wholly inside or outside the operand.  Loads outside are redirected to the
+// operand's first element and their values replaced by zero.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace trt {
+
+// The workgroup tile of the skinny kernel: logical [16, 64], 8 waves, and
+// after the cross-wave reduction every thread owns 2 consecutive columns of
+// one row: thread t = 64*wave + lane holds C(t / 32, 2*(t % 32) + reg).
+struct SkinnyTile {
+  static constexpr int BM = 16, BN = 64, WAVES = 8, THREADS = 64 * WAVES;
+  static constexpr int KW = 32;      // k per wave iteration
+  static constexpr int DEPTH = 4;    // iterations of loads in flight per wave
+  static constexpr int REGS = 2;     // outputs per thread after the reduction
+  TRT_HD static int owner_row(int reg, int lane, int wave) { return (64 * wave + lane) / 32; }
+  TRT_HD static int owner_col(int reg, int lane, int wave) {
+    return 2 * ((64 * wave + lane) % 32) + reg;
+  }
+  static constexpr int REG_BITS = 1, WAVE_BITS = 3, C_IN_BITS = REG_BITS + 6 + WAVE_BITS;
+  static constexpr Gf2Map<C_IN_BITS> c_map() {
+    Gf2Map<C_IN_BITS> m{};
+    m.row_bits = 4;
+    m.col_bits = 6;
+    int i = 0;
+    m.b[i++] = {0, 1};                                   // reg
+    for (int s = 0; s < 5; ++s) m.b[i++] = {0, 2 << s};  // lane bits 0-4
+    m.b[i++] = {1, 0};                                   // lane bit 5
+    for (int s = 0; s < 3; ++s) m.b[i++] = {2 << s, 0};  // wave bits
+    return m;
+  }
+  static constexpr bool owner_matches_bases() {
+    constexpr auto m = c_map();
+    for (int w = 0; w < WAVES; ++w)
+      for (int l = 0; l < 64; ++l)
+        for (int r = 0; r < REGS; ++r) {
+          const Basis v = m.apply(uint32_t(r) | (uint32_t(l) << 1) | (uint32_t(w) << 7));
+          if (v.row != owner_row(r, l, w) || v.col != owner_col(r, l, w)) return false;
+        }
+    return true;
+  }
+};
+static_assert(SkinnyTile::c_map().bijective(), "C ownership must cover the tile exactly once");
+
+template <int DT>
+__global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmArgs p) {
+  using ST = SkinnyTile;
+  constexpr int D = ST::DEPTH;
+  __shared__ f32x4 part[ST::WAVES][4][64];  // partial tiles: [wave][j][lane]
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int n0 = blockIdx.x * ST::BN;
+  const int c = lane & 15, g = lane >> 4;
+  const int n = n0 + 4 * c;                 // this lane's 4 columns of B
+  const int ma = lane & 15;                 // this lane's row of A
+
+  // the wave's K slice, in whole iterations of 32
+  const int iters_total = (p.K + ST::KW - 1) / ST::KW;
+  const int per_wave = (iters_total + ST::WAVES - 1) / ST::WAVES;
+  const int it0 = wave * per_wave;
+  const int it1 = min(it0 + per_wave, iters_total);
+  const int iters = max(it1 - it0, 0);
+
+  u32x2 bq[D][8];
+  u32x4 aq[D];
+  // Loads of iteration `it` (absolute) into slot s.
+  auto load = [&](int it, int s) {
+    const int kb = it * ST::KW + 8 * g;
+    const bool a_ok = ma < p.M && kb < p.K;
+    const u32x4 av = *reinterpret_cast<const u32x4*>(p.A + (a_ok ? (int64_t)ma * p.lda + kb : 0));
+    aq[s] = a_ok ? av : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = n < p.N && kb + j < p.K;
+      const u32x2 v =
+          *reinterpret_cast<const u32x2*>(p.B + (ok ? (int64_t)(kb + j) * p.ldb + n : 0));
+      bq[s][j] = ok ? v : u32x2{0u, 0u};
+    }
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto consume = [&](int s) {
+    // 8 k rows x 4 columns -> 4 operand registers of 8 k each
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = j >> 1;
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = __builtin_amdgcn_perm(bq[s][2 * q + 1][w], bq[s][2 * q][w], sel);
+      acc[j] = mfma16<DT>(aq[s], f, acc[j]);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < iters) load(it0 + s, s);
+  int i = 0;
+  for (; i + D <= iters; i += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      consume(s);
+      if (i + D + s < iters) load(it0 + i + D + s, s);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (i + s < iters) consume(s);
+
+  // cross-wave reduction: partial (m, n) of wave w sits at part[w][j][lane]
+  // register r with m = 4*(lane/16) + r, n = 4*(lane%16) + j
+#pragma unroll
+  for (int j = 0; j < 4; ++j) part[wave][j][lane] = acc[j];
+  __syncthreads();
+
+  const int m = ST::owner_row(0, lane, wave);
+  const int nl = ST::owner_col(0, lane, wave);  // columns nl, nl + 1
+  float y[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int ncol = nl + e;
+    const int j = ncol & 3, src_lane = 16 * (m >> 2) + (ncol >> 2), r = m & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < ST::WAVES; ++w) sum += part[w][j][src_lane][r];
+    y[e] = sum;
+  }
+  if (m >= p.M) return;
+  const int nc = n0 + nl;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (nc + e >= p.N) continue;
+    if (p.bias) y[e] += to_f32<DT>(p.bias[nc + e]);
+    if (p.relu) y[e] = y[e] > 0.f ? y[e] : 0.f;
+    if (p.R) y[e] += to_f32<DT>(p.R[(int64_t)m * p.ldr + nc + e]);
+    p.C[(int64_t)m * p.ldc + nc + e] = (uint16_t)from_f32<DT>(y[e]);
+  }
+}
+
+}  // namespace trt

@@ -107,6 +107,7 @@ struct Tile {
   static constexpr int FM = WTM / MF, FN = WTN / MF;
   // register shape: accumulator registers per lane
   static constexpr int FRAG_REGS = MF * MF / 64;
+  static constexpr bool COPY_MAPS = true;  // has cooperative copy / LDS maps
   static constexpr int REGS = FM * FN * FRAG_REGS;
   // operand tiles in LDS: G chunks of 8 k (16 bytes) per row
   static constexpr int G = BK / 8;

@@ -23,4 +23,7 @@ void launch_generic(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t 
 template <class TL>
 void launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s);
 
+// Launch the HBM-streaming kernel for M <= 16 (kern_skinny.hip).
+void launch_skinny(GemmArgs a, int dt, hipStream_t s);
+
 }  // namespace trt

@@ -7,6 +7,7 @@
 
 #include "../../include/trt.h"
 #include "gemm_kernel.hpp"
+#include "gemm_skinny.hpp"
 #include "tiles.hpp"
 #include "validate.hpp"
 
@@ -48,6 +49,21 @@ bool dma_ok(const GemmArgs& a, int opA, int opB, bool vec) {
          a.a_bytes < (int64_t(1) << 31) && a.b_bytes < (int64_t(1) << 31);
 }
 
+// Whether the streaming kernel applies (M <= 16, A k-contiguous, B
+// row-major, aligned vector rows, whole vector runs at the K and N edges).
+bool skinny_ok(const GemmArgs& a, int opA, int opB) {
+  auto al = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
+  return a.M <= 16 && opA == TRT_OP_N && opB == TRT_OP_N && al(a.A, 16) && a.lda % 8 == 0 &&
+         al(a.B, 8) && a.ldb % 4 == 0 && a.K % 8 == 0 && a.N % 4 == 0;
+}
+
+// The streaming tile: the skinny kernel when it applies, otherwise the
+// generic kernel on the 16x64 tile.
+void launch_tile_skinny(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
+  if (!skinny_ok(a, opA, opB)) return trt::launch_generic<TileTiny>(a, dt, opA, opB, vec, s);
+  trt::launch_skinny(a, dt, s);
+}
+
 template <class TL>
 void launch_tile(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
   trt::launch_generic<TL>(a, dt, opA, opB, vec, s);
@@ -63,8 +79,16 @@ void launch_tile_dma(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t
 
 // ---- layout maps (host and device evaluate the same functions) ---------------
 
+template <class TL, class = void>
+struct HasCopyMaps : std::false_type {};
+template <class TL>
+struct HasCopyMaps<TL, std::void_t<decltype(TL::COPY_MAPS)>> : std::true_type {};
+
 template <class TL>
 TRT_HD int64_t map_size(int map) {
+  if constexpr (!HasCopyMaps<TL>::value) {
+    return map == TRT_MAP_C_OWNER ? (int64_t)TL::WAVES * 64 * TL::REGS : -1;
+  } else {
   constexpr bool dma = TL::BK == 32;
   using KA = typename TL::template KContig<TL::BM>;
   using MA = typename TL::template MNContig<TL::BM>;
@@ -84,6 +108,7 @@ TRT_HD int64_t map_size(int map) {
     case TRT_MAP_DMA_MN_SLOT_B: return dma && TL::BN >= 128 ? (int64_t)32 * (TL::BN / 8) : -1;
     default: return -1;
   }
+  }
 }
 
 template <class TL, class Map>
@@ -102,6 +127,14 @@ TRT_HD void eval_mncontig(int64_t x, int& r, int& c) {
 
 template <class TL>
 TRT_HD void eval_map(int map, int64_t x, int& r, int& c) {
+  if constexpr (!HasCopyMaps<TL>::value) {
+    const int reg = (int)(x % TL::REGS);
+    const int lane = (int)((x / TL::REGS) % 64);
+    const int wave = (int)(x / (TL::REGS * 64));
+    r = map == TRT_MAP_C_OWNER ? TL::owner_row(reg, lane, wave) : -1;
+    c = map == TRT_MAP_C_OWNER ? TL::owner_col(reg, lane, wave) : -1;
+    return;
+  } else {
   switch (map) {
     case TRT_MAP_C_OWNER: {
       const int reg = (int)(x % TL::REGS);
@@ -134,6 +167,7 @@ TRT_HD void eval_map(int map, int64_t x, int& r, int& c) {
       c = 0;
       return;
     default: r = c = -1; return;
+  }
   }
 }
 
@@ -187,22 +221,46 @@ void eval_host(int map, int64_t x, int& r, int& c) { eval_map<TL>(map, x, r, c);
 
 template <class TL, bool DMA>
 constexpr auto launcher() {
-  if constexpr (DMA) return &launch_tile_dma<TL>;
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return &launch_tile_skinny;
+  else if constexpr (DMA) return &launch_tile_dma<TL>;
   else return &launch_tile<TL>;
+}
+
+template <class TL>
+constexpr int tile_bk() {
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return TL::KW * TL::WAVES;
+  else return TL::BK;
+}
+template <class TL>
+constexpr int tile_wm() {
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return TL::WAVES;
+  else return TL::WM;
+}
+template <class TL>
+constexpr int tile_wn() {
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return 1;
+  else return TL::WN;
+}
+template <class TL>
+constexpr int tile_mf() {
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return 16;
+  else return TL::MF;
 }
 
 template <class TL, bool DMA = false>
 constexpr TileEntry entry() {
   static_assert(TL::owner_matches_bases(),
                 "kernel ownership arithmetic must equal its GF(2) bases");
-  return TileEntry{TL::BM, TL::BN, TL::BK, TL::WM, TL::WN, TL::REGS, TL::MF,
+  return TileEntry{TL::BM, TL::BN, tile_bk<TL>(), tile_wm<TL>(), tile_wn<TL>(), TL::REGS,
+                   tile_mf<TL>(),
                    launcher<TL, DMA>(), &size_host<TL>,
                    &eval_host<TL>, &dump_launch<TL>,
                    TL::c_map().rank(), TL::C_IN_BITS, trt::ilog2(TL::BM * TL::BN)};
 }
 
 const TileEntry kTiles[] = {entry<TileTiny>(), entry<Tile64>(), entry<Tile128>(),
-                            entry<Tile256>(), entry<Tile256D, true>()};
+                            entry<Tile256>(), entry<Tile256D, true>(),
+                            entry<trt::SkinnyTile>()};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 const TileEntry* find_tile(const trt_tile* t) {
@@ -216,7 +274,7 @@ const TileEntry* find_tile(const trt_tile* t) {
 // that small.
 const TileEntry* choose_tile(int64_t M, int64_t N) {
   auto count = [&](const TileEntry& e) { return ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn); };
-  if (M <= 16) return &kTiles[0];
+  if (M <= 16) return &kTiles[5];
   if (count(kTiles[4]) >= 192) return &kTiles[4];
   if (count(kTiles[2]) >= 128) return &kTiles[2];
   return &kTiles[1];
