@@ -179,34 +179,35 @@ struct FragReader {
 // contiguous bytes of a row ("My Triton From Scratch, Part 16: Register
 // Tiles", sections "Masks and stores" and "Broadcasts cannot be treated as
 // full register tiles": per-element masks, bias held once per owned column).
-template <class TL, int DT>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&acc)[TL::FM][TL::FN],
-                                             float* stage, int m0, int n0, int t) {
+//
+// MODE, chosen once per tile: EPI_FAST when the whole tile is inside C and
+// 8-byte vectors are allowed (EPI_FAST_RES with a residual), else
+// EPI_MASKED.  The fast modes have no branch in the store phase: the
+// residual rows of a pass are loaded before its staging writes, and the LDS
+// reads of a batch of rows are all issued before the first of their stores.
+// EPI_MASKED masks and stores every element on its own.
+enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2 };
+
+template <class TL, int DT, int MODE>
+__device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
+                                                const f32x16 (&acc)[TL::FM][TL::FN],
+                                                float* stage, int m0, int n0, int t,
+                                                const float (&bias)[4]) {
   constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
   constexpr int PITCH = BN + 4;                       // floats per staged row
   constexpr int HALF_ROWS = TL::BM / 2;               // rows per pass
   constexpr int COLS_PER_T = 4;
   constexpr int T_PER_ROW = BN / COLS_PER_T;          // threads across a row
   constexpr int ROWS_PER_IT = TL::THREADS / T_PER_ROW;
+  constexpr int ITERS = HALF_ROWS / ROWS_PER_IT;
+  constexpr int BATCH = 8;                            // rows read ahead of their stores
   static_assert(FM % 2 == 0 && TL::WM == 2, "two passes over the wave rows");
+  static_assert(ITERS % BATCH == 0, "whole batches");
   const int lane = t & 63, wave = t >> 6;
   const int wr = wave / TL::WN, wc = wave % TL::WN;
   const int col = COLS_PER_T * (t % T_PER_ROW);       // this thread's 4 columns
   const int n = n0 + col;
-  const bool vec = p.epi_vec && n + 4 <= p.N;
-  float bias[4] = {0.f, 0.f, 0.f, 0.f};
-  if (p.bias) {
-    if (vec) {
-      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-      bias[0] = to_f32<DT>(bb[0] & 0xFFFFu); bias[1] = to_f32<DT>(bb[0] >> 16);
-      bias[2] = to_f32<DT>(bb[1] & 0xFFFFu); bias[3] = to_f32<DT>(bb[1] >> 16);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < p.N) bias[e] = to_f32<DT>(p.bias[n + e]);
-    }
-  }
-  constexpr int ITERS = HALF_ROWS / ROWS_PER_IT;
+  const bool relu = p.relu != 0;
   // staged row -> tile row: the wave row block, then the pass's half of it
   auto tile_row = [&](int pass, int prow) {
     return (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
@@ -214,15 +215,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&a
   };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    // residual loads of the whole pass go out first, so their latency is
-    // paid once per pass and overlaps the staging writes
-    u32x2 rr[ITERS];
-    if (p.R && vec) {
+    u32x2 rr[MODE == EPI_FAST_RES ? ITERS : 1];
+    if constexpr (MODE == EPI_FAST_RES) {
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int m = m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW);
-        rr[it] = m < p.M ? *reinterpret_cast<const u32x2*>(p.R + (int64_t)m * p.ldr + n)
-                         : u32x2{0u, 0u};
+        rr[it] = *reinterpret_cast<const u32x2*>(p.R + (int64_t)m * p.ldr + n);
       }
     }
     // accumulators of fragment rows fm = 2*pass, 2*pass+1 -> staged rows
@@ -242,42 +240,91 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&a
         }
     }
     __syncthreads();
+    if constexpr (MODE != EPI_MASKED) {
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int prow = it * ROWS_PER_IT + t / T_PER_ROW;
-      const int m = m0 + tile_row(pass, prow);
-      if (m >= p.M) continue;
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow * PITCH + col);
-      float y[4] = {a4[0] + bias[0], a4[1] + bias[1], a4[2] + bias[2], a4[3] + bias[3]};
-      if (p.relu) {
+      for (int b0 = 0; b0 < ITERS; b0 += BATCH) {
+        f32x4 v[BATCH];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
+        for (int i = 0; i < BATCH; ++i)
+          v[i] = *reinterpret_cast<const f32x4*>(
+              stage + ((b0 + i) * ROWS_PER_IT + t / T_PER_ROW) * PITCH + col);
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int it = b0 + i;
+          const int m = m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW);
+          float y[4] = {v[i][0] + bias[0], v[i][1] + bias[1], v[i][2] + bias[2],
+                        v[i][3] + bias[3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (relu && !(y[e] > 0.f)) ? 0.f : y[e];
+          if constexpr (MODE == EPI_FAST_RES) {
+            y[0] += to_f32<DT>(rr[it][0] & 0xFFFFu); y[1] += to_f32<DT>(rr[it][0] >> 16);
+            y[2] += to_f32<DT>(rr[it][1] & 0xFFFFu); y[3] += to_f32<DT>(rr[it][1] >> 16);
+          }
+          u32x2 o;
+          o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
+          o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
+          *reinterpret_cast<u32x2*>(p.C + (int64_t)m * p.ldc + n) = o;
+        }
       }
-      if (p.R) {
-        if (vec) {
-          y[0] += to_f32<DT>(rr[it][0] & 0xFFFFu); y[1] += to_f32<DT>(rr[it][0] >> 16);
-          y[2] += to_f32<DT>(rr[it][1] & 0xFFFFu); y[3] += to_f32<DT>(rr[it][1] >> 16);
-        } else {
+    } else {
+      const bool vec = p.epi_vec && n + 4 <= p.N;
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int prow = it * ROWS_PER_IT + t / T_PER_ROW;
+        const int m = m0 + tile_row(pass, prow);
+        if (m >= p.M) continue;
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow * PITCH + col);
+        float y[4] = {a4[0] + bias[0], a4[1] + bias[1], a4[2] + bias[2], a4[3] + bias[3]};
+        if (relu) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
+        }
+        if (p.R) {
           const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
         }
-      }
-      uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
-      if (vec) {
-        u32x2 o;
-        o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
-        o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
-        *reinterpret_cast<u32x2*>(cp) = o;
-      } else {
+        uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
+        if (vec) {
+          u32x2 o;
+          o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
+          o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
+          *reinterpret_cast<u32x2*>(cp) = o;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+        }
       }
     }
     __syncthreads();
   }
+}
+
+template <class TL, int DT>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&acc)[TL::FM][TL::FN],
+                                             float* stage, int m0, int n0, int t) {
+  const int n = n0 + 4 * (t % (TL::BN / 4));          // this thread's 4 columns
+  const bool vec = p.epi_vec && n + 4 <= p.N;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.bias) {
+    if (vec) {
+      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+      bias[0] = to_f32<DT>(bb[0] & 0xFFFFu); bias[1] = to_f32<DT>(bb[0] >> 16);
+      bias[2] = to_f32<DT>(bb[1] & 0xFFFFu); bias[3] = to_f32<DT>(bb[1] >> 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) bias[e] = to_f32<DT>(p.bias[n + e]);
+    }
+  }
+  if (!(p.epi_vec && n0 + TL::BN <= p.N && m0 + TL::BM <= p.M))
+    epilogue_passes<TL, DT, EPI_MASKED>(p, acc, stage, m0, n0, t, bias);
+  else if (p.R)
+    epilogue_passes<TL, DT, EPI_FAST_RES>(p, acc, stage, m0, n0, t, bias);
+  else
+    epilogue_passes<TL, DT, EPI_FAST>(p, acc, stage, m0, n0, t, bias);
 }
 
 template <class TL, int DT, bool A_KC, bool B_KC>
