@@ -8,9 +8,12 @@ fp16 output) with inputs N(0,1)/8.  Prints ONE JSON line:
 
   value        whole-job TFLOP/s = 2*M*N*K / average step time
   roofline     the GEMM kernel against the dense fp16 matrix-core peak
-               (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk), with
-               HBM traffic from committed rocprofv3 counters when they were
-               taken on the current kernel source
+               (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk), or for
+               the M <= 16 workload against the 8 TB/s HBM peak; its HBM
+               GB/s; the read bandwidth of a plain streaming kernel measured
+               in the same run (context); and, when the committed rocprofv3
+               counters were taken on the current kernel source, the HBM
+               traffic and matrix-core figures from those counters
   cpu_baseline the oracle (plain fp64 C, all host cores) timed on a bounded
                row sample of the same workload, scaled to TFLOP/s
   parity       the GPU result on the same sampled rows against the oracle
@@ -28,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s (fp16→fp32 acc) at 4096³ + % of MFMA peak (rocprof)"
 PEAK_TFLOPS = {1: 2516.6, 2: 2516.6}   # dense f16 / bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+WORKLOADS = ("square", "epilogue", "ragged", "skinny")
 
 
 def csrc_digest():
@@ -40,18 +44,105 @@ def csrc_digest():
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload):
-    """HBM bytes per launch from committed counter runs, only if they were
-    taken on the current kernel source."""
+def committed_counters(workload):
+    """Counter figures of `workload` from profiles/counters.json, only if they
+    were taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(workload)
     if not e or e.get("csrc_digest") != csrc_digest():
         return None
-    return e.get("bytes_per_launch")
+    return e
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def ingest_counters(root):
+    """Build profiles/counters.json from rocprofv3 --pmc runs of this script.
+
+    root/pmc_fetch_<w>, root/pmc_write_<w>: FETCH_SIZE and WRITE_SIZE runs with
+    --copy-calibration-mib 256; root/pmc_mfma_<w>: SQ_INSTS_VALU_MFMA_MOPS_*,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE and
+    SQ_LDS_BANK_CONFLICT.  Each counter is scaled by what it reads for the
+    256 MiB device-to-device copy of the same run (read and written bytes
+    known), and the GEMM launches' median is kept."""
+    import workloads as W
+    out = {}
+    for w in WORKLOADS:
+        cfg = W.CONFIGS[w]
+        e = {"csrc_digest": csrc_digest()}
+        for cn, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+            path = os.path.join(root, f"pmc_{cn}_{w}", "run_counter_collection.csv")
+            if not os.path.exists(path):
+                break
+            rows = [r for r in _csv_rows(path) if r["Counter_Name"] == counter]
+            copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+            big = max(int(r["Grid_Size"]) for r in copies)
+            raw_copy = float(next(r["Counter_Value"] for r in copies if int(r["Grid_Size"]) == big))
+            gemm = [r for r in rows if "gemm" in r["Kernel_Name"]]
+            raw = _median([float(r["Counter_Value"]) for r in gemm])
+            factor = 256 * 1024 / raw_copy
+            e["kernel"] = sorted({r["Kernel_Name"] for r in gemm})[0]
+            e[f"{cn}_size_kib_raw"] = raw
+            e[f"{cn}_factor"] = round(factor, 5)
+            e[f"{cn}_bytes_per_launch"] = int(raw * 1024 * factor)
+        if "write_bytes_per_launch" in e:
+            e["bytes_per_launch"] = e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
+        path = os.path.join(root, f"pmc_mfma_{w}", "run_counter_collection.csv")
+        if os.path.exists(path):
+            rows = [r for r in _csv_rows(path) if "gemm" in r["Kernel_Name"]]
+            by = {}
+            for r in rows:
+                by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            med = {k: _median(v) for k, v in by.items()}
+            dur = {}
+            for r in rows:
+                dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            ns = _median(list(dur.values()))
+            mops = sum(v for k, v in med.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+            gui = med.get("GRBM_GUI_ACTIVE", 0.0) / 8          # summed over the 8 XCDs
+            busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            e["mfma"] = {"counters": med, "duration_ns": ns,
+                         "flops_per_launch": mops * 512, "flops_algorithmic": cfg.flops,
+                         "tflops": round(mops * 512 / ns / 1e3, 2),
+                         "frac_of_peak": round(mops * 512 / ns / 1e3 / PEAK_TFLOPS[cfg.dtype], 4),
+                         "clock_ghz": round(gui / ns, 3) if gui else None,
+                         "busy_frac": round(busy / (gui * 1024), 4) if gui else None}
+        out[w] = e
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def stream_read_gbps(trt, torch, nbytes=1 << 30, reps=20):
+    """Read bandwidth of the library's plain streaming-read kernel over a
+    buffer larger than the last-level cache, timed like the GEMM."""
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(trt.READ_PROBE_SINK_BYTES, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        trt.hbm_read_probe(x, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        trt.hbm_read_probe(x, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / reps * 1e-3
+    del x
+    return nbytes / s / 1e9
 
 
 def main():
@@ -68,7 +159,16 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the "
                          "GEMM steps (a known-size kernel to scale HBM counters by)")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the streaming-read bandwidth measurement")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="write profiles/counters.json from rocprofv3 --pmc runs in DIR "
+                         "and exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(args.ingest_counters), indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
@@ -136,17 +236,33 @@ def main():
 
     tflops = w.flops / (ms * 1e-3) / 1e12
     achieved = w.flops / (kern_ms * 1e-3) / 1e12
-    traffic = committed_traffic(w.name)
+    counters = committed_counters(w.name)
+    traffic = counters.get("bytes_per_launch") if counters else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
                 "traffic": traffic,
                 "algorithmic_bytes": w.algorithmic_bytes,
-                "kernel_ms": round(kern_ms, 5)}
+                "algorithmic_flops": w.flops,
+                "kernel_ms": round(kern_ms, 5),
+                "hbm_GBps_algorithmic": round(w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9, 1),
+                "hbm_GBps_traffic": (round(traffic / (kern_ms * 1e-3) / 1e9, 1)
+                                     if traffic else None)}
     if w.name == "skinny":
         gbs = w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9
         roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "tflops": round(achieved, 2)})
+    if counters and "mfma" in counters:
+        m = counters["mfma"]
+        roofline["rocprof_mfma"] = {"tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
+                                    "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
+                                    "flops_counted": m["flops_per_launch"]}
+    if not args.no_stream_read:
+        sr = stream_read_gbps(trt, torch)
+        roofline["stream_read_GBps"] = round(sr, 1)
+        if w.name == "skinny":
+            roofline["frac_of_stream_read"] = round(roofline["achieved"] / sr, 4)
 
     cpu = None
     parity = None

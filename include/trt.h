@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 1
+#define TRT_ABI_VERSION 2
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -212,6 +212,23 @@ trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank,
  */
 trt_status trt_mfma_probe(int32_t dtype, int32_t shape, const void* a,
                           const void* b, float* c, void* stream);
+
+/*
+ * trt_hbm_read_probe -- measurement yardstick, not part of the GEMM: a plain
+ * streaming read of `bytes` bytes at device address x (16-byte aligned,
+ * bytes a positive multiple of 16), enqueued on `stream`.  The kernel runs
+ * TRT_READ_PROBE_SINK_BYTES / 16 workgroups; workgroup w writes the XOR of
+ * the 16-byte words it read to sink[16w .. 16w+15] (device buffer owned by
+ * the caller, at least TRT_READ_PROBE_SINK_BYTES, 16-byte aligned, disjoint
+ * from x), so the XOR of all sink words equals the XOR of all words of x.
+ * Timing it gives the HBM read bandwidth a simple kernel reaches, the
+ * context for the memory-bound (M <= 16) GEMM.  Errors: TRT_ERR_NULL,
+ * TRT_ERR_SIZE, TRT_ERR_ALIGN, TRT_ERR_OVERLAP, before any HIP call;
+ * TRT_ERR_HIP if the launch fails.
+ */
+#define TRT_READ_PROBE_SINK_BYTES 32768
+trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink,
+                              int64_t sink_bytes, void* stream);
 
 /* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
 int32_t trt_abi_version(void);

@@ -205,3 +205,22 @@ def test_dma_slot_maps_match_oracle():
     # the streaming tile has only its ownership map
     assert trt.layout_size(trt.MAP_C_OWNER, (16, 64, 256)) == 1024
     assert all(trt.layout_size(m, (16, 64, 256)) == -1 for m in range(1, 11))
+
+
+# ---- the HBM read yardstick: argument checks (no HIP call on error) ---------------
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), trt.ERR_NULL), (dict(sink=0), trt.ERR_NULL),
+    (dict(nbytes=0), trt.ERR_SIZE), (dict(nbytes=24), trt.ERR_SIZE),
+    (dict(sink_bytes=trt.READ_PROBE_SINK_BYTES - 16), trt.ERR_SIZE),
+    (dict(x=BASE + 8), trt.ERR_ALIGN), (dict(sink=BASE * 2 + 4), trt.ERR_ALIGN),
+    (dict(sink=BASE + 4096), trt.ERR_OVERLAP),
+    (dict(sink=BASE - trt.READ_PROBE_SINK_BYTES + 16), trt.ERR_OVERLAP),
+])
+def test_read_probe_rejections(kw, code):
+    a = dict(x=BASE, nbytes=1 << 16, sink=BASE * 2, sink_bytes=trt.READ_PROBE_SINK_BYTES)
+    a.update(kw)
+    with pytest.raises(trt.TrtError) as e:
+        trt.hbm_read_probe_raw(a["x"], a["nbytes"], a["sink"], a["sink_bytes"])
+    assert e.value.status == code
+    assert trt.last_error() != ""

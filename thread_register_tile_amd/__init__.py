@@ -93,6 +93,8 @@ def lib():
         L.trt_layout_rank.restype = i32
         L.trt_mfma_probe.argtypes = [i32, i32, vp, vp, vp, vp]
         L.trt_mfma_probe.restype = i32
+        L.trt_hbm_read_probe.argtypes = [vp, i64, vp, i64, vp]
+        L.trt_hbm_read_probe.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
         L.trt_last_error.argtypes = []
@@ -274,3 +276,23 @@ def mfma_probe(a_regs, b_regs, dtype=F16, shape=16):
     _check(lib().trt_mfma_probe(dtype, shape, a.data_ptr(), b.data_ptr(), c.data_ptr(),
                                 _stream(a.device)))
     return c
+
+
+READ_PROBE_SINK_BYTES = 32768   # TRT_READ_PROBE_SINK_BYTES
+
+
+def hbm_read_probe_raw(x, nbytes, sink, sink_bytes, stream=0):
+    """trt_hbm_read_probe on raw device addresses; raises TrtError on error."""
+    _check(lib().trt_hbm_read_probe(x, nbytes, sink, sink_bytes, stream))
+
+
+def hbm_read_probe(x, sink=None):
+    """Stream-read the bytes of device tensor x once (a bandwidth yardstick);
+    returns the [2048, 16]-byte digest tensor (uint8), whose XOR over rows is
+    the XOR of x's 16-byte words."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(READ_PROBE_SINK_BYTES, dtype=torch.uint8, device=x.device)
+    hbm_read_probe_raw(x.data_ptr(), x.numel() * x.element_size(), sink.data_ptr(),
+                       sink.numel() * sink.element_size(), _stream(x.device))
+    return sink.view(-1, 16)

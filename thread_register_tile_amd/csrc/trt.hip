@@ -284,6 +284,34 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
+// Plain streaming read of x (n 16-byte words): each workgroup XORs the words
+// it reads (grid-stride, four independent loads in flight per lane, marked
+// non-temporal) and writes one 16-byte digest; the XOR of all digests is the
+// XOR of all words.  A memory-bound yardstick for the streaming GEMM.
+constexpr int kReadProbeBlocks = 2048;
+__global__ __launch_bounds__(256) void hbm_read_kernel(const trt::u32x4* __restrict__ x, int64_t n,
+                                                       trt::u32x4* sink) {
+  __shared__ trt::u32x4 part[4];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  trt::u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    trt::u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&x[i + u * stride]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u];
+  }
+  for (; i < n; i += stride) acc ^= x[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] ^= __shfl_xor(acc[e], off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 extern "C" {
 
 trt_status trt_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
@@ -434,6 +462,25 @@ trt_status trt_mfma_probe(int32_t dtype, int32_t shape, const void* a, const voi
       hipLaunchKernelGGL((probe32_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
   }
   return check_launch("probe launch");
+}
+
+trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink, int64_t sink_bytes,
+                              void* stream) {
+  if (!x || !sink) return fail(TRT_ERR_NULL, "x and sink must be non-null");
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(TRT_ERR_SIZE, "bytes must be a positive multiple of 16");
+  if (sink_bytes < TRT_READ_PROBE_SINK_BYTES)
+    return fail(TRT_ERR_SIZE, "sink must hold TRT_READ_PROBE_SINK_BYTES bytes");
+  if (!aligned(x, 16) || !aligned(sink, 16))
+    return fail(TRT_ERR_ALIGN, "x and sink must be 16-byte aligned");
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), s0 = reinterpret_cast<uintptr_t>(sink);
+  if (x0 < s0 + (uintptr_t)TRT_READ_PROBE_SINK_BYTES && s0 < x0 + (uintptr_t)bytes)
+    return fail(TRT_ERR_OVERLAP, "sink must not overlap x");
+  static_assert(kReadProbeBlocks * 16 == TRT_READ_PROBE_SINK_BYTES, "one digest per workgroup");
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(kReadProbeBlocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const trt::u32x4*>(x),
+                     bytes / 16, static_cast<trt::u32x4*>(sink));
+  return check_launch("read probe launch");
 }
 
 int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }
