@@ -145,6 +145,28 @@ def stream_read_gbps(trt, torch, nbytes=1 << 30, reps=20):
     return nbytes / s / 1e9
 
 
+def mfma_loop_tflops(trt, torch, host_a, dtype, kern_ms, launches):
+    """Rate of the library's matrix-core-only loop on operand words taken from
+    the workload's own A data, each launch sized to last about as long as one
+    GEMM launch and run as many times as the GEMM was (warmup + timed)."""
+    import numpy as np
+    words = np.resize(host_a, trt.MFMA_PROBE_OPERAND_BYTES // 2)   # repeats a short input
+    ops = torch.from_numpy(words.view(np.int16)).cuda()
+    sink = torch.empty(trt.MFMA_PROBE_SINK_BYTES // 4, dtype=torch.float32, device="cuda")
+    iters = max(1, int(kern_ms * 1e-3 * 1.8e9 / (32 * 32)))   # 32 products of 32 cycles per round
+    stream = torch.cuda.current_stream()
+    for _ in range(max(launches - 20, 0)):
+        trt.mfma_loop_probe(ops, iters, dtype, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(20):
+        trt.mfma_loop_probe(ops, iters, dtype, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 20 * 1e-3
+    return trt.mfma_loop_probe_flops(iters) / s / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +183,8 @@ def main():
                          "GEMM steps (a known-size kernel to scale HBM counters by)")
     ap.add_argument("--no-stream-read", action="store_true",
                     help="skip the streaming-read bandwidth measurement")
+    ap.add_argument("--no-mfma-loop", action="store_true",
+                    help="skip the matrix-core-only loop measurement")
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
                     help="write profiles/counters.json from rocprofv3 --pmc runs in DIR "
                          "and exit (no GPU needed)")
@@ -258,6 +282,11 @@ def main():
         roofline["rocprof_mfma"] = {"tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
                                     "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
                                     "flops_counted": m["flops_per_launch"]}
+    if not args.no_mfma_loop and w.name != "skinny":
+        a_rows = host["A"].reshape(w.a_rows, w.lda_)[:, :w.a_cols].reshape(-1)   # no padding
+        ml = mfma_loop_tflops(trt, torch, a_rows, w.dtype, kern_ms, args.warmup + args.steps)
+        roofline["mfma_loop_tflops"] = round(ml, 1)
+        roofline["frac_of_mfma_loop"] = round(achieved / ml, 4)
     if not args.no_stream_read:
         sr = stream_read_gbps(trt, torch)
         roofline["stream_read_GBps"] = round(sr, 1)

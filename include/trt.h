@@ -230,6 +230,27 @@ trt_status trt_mfma_probe(int32_t dtype, int32_t shape, const void* a,
 trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink,
                               int64_t sink_bytes, void* stream);
 
+/*
+ * trt_mfma_loop_probe -- measurement yardstick, not part of the GEMM: 256
+ * workgroups of 4 waves (one wave per SIMD) each run `iters` rounds of 32
+ * v_mfma_f32_32x32x16 (dtype TRT_F16 or TRT_BF16) with 16 independent
+ * accumulators and no other work in the loop: 2^15 * 32 * 1024 * iters
+ * FLOP per launch.  Operand registers come from `operands` (device buffer
+ * of TRT_MFMA_PROBE_OPERAND_BYTES, 16-byte aligned; lane l of every wave
+ * reads 16-byte words l, 64+l, ..., 960+l); thread x of workgroup w writes
+ * the 16 fp32 sums of its accumulators to sink[16*(256w + x) ..] (device
+ * buffer of at least TRT_MFMA_PROBE_SINK_BYTES, 64-byte aligned, disjoint
+ * from the operands).  Timing it gives the matrix-core rate the part
+ * sustains on such data, the context for the GEMM's fraction of peak.
+ * Errors: TRT_ERR_NULL, TRT_ERR_DTYPE, TRT_ERR_ARG (iters < 1), TRT_ERR_SIZE,
+ * TRT_ERR_ALIGN, TRT_ERR_OVERLAP, before any HIP call; TRT_ERR_HIP if the
+ * launch fails.
+ */
+#define TRT_MFMA_PROBE_OPERAND_BYTES 16384
+#define TRT_MFMA_PROBE_SINK_BYTES 4194304
+trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iters,
+                               float* sink, int64_t sink_bytes, void* stream);
+
 /* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
 int32_t trt_abi_version(void);
 

@@ -224,3 +224,19 @@ def test_read_probe_rejections(kw, code):
         trt.hbm_read_probe_raw(a["x"], a["nbytes"], a["sink"], a["sink_bytes"])
     assert e.value.status == code
     assert trt.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ops=0), trt.ERR_NULL), (dict(sink=0), trt.ERR_NULL),
+    (dict(dtype=3), trt.ERR_DTYPE), (dict(iters=0), trt.ERR_ARG),
+    (dict(sink_bytes=trt.MFMA_PROBE_SINK_BYTES - 64), trt.ERR_SIZE),
+    (dict(ops=BASE + 8), trt.ERR_ALIGN), (dict(sink=BASE * 8 + 32), trt.ERR_ALIGN),
+    (dict(sink=BASE + 4096), trt.ERR_OVERLAP),
+])
+def test_mfma_probe_rejections(kw, code):
+    a = dict(dtype=trt.F16, ops=BASE, iters=4, sink=BASE * 8,
+             sink_bytes=trt.MFMA_PROBE_SINK_BYTES)
+    a.update(kw)
+    with pytest.raises(trt.TrtError) as e:
+        trt.mfma_loop_probe_raw(a["dtype"], a["ops"], a["iters"], a["sink"], a["sink_bytes"])
+    assert e.value.status == code

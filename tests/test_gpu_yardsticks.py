@@ -1,0 +1,83 @@
+"""GPU tests of the measurement yardsticks, through the C ABI.
+
+Neither is part of the GEMM; the benchmark reports their rates as context.
+trt_hbm_read_probe (a plain streaming read) is pinned by a property that holds
+at any size: the XOR of the per-workgroup digests equals the XOR of all
+16-byte words read, computed here with numpy.  trt_mfma_loop_probe (matrix
+cores only) is pinned by recomputing every thread's sum of accumulators on
+the host from the operand words and the documented 32x32x16 fragment maps,
+with operands in {-1, 0, 1} so that every fp32 sum is exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import thread_register_tile_amd as trt
+import workloads as W
+from oracle import layout_ref as L
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    trt.lib()
+
+
+@pytest.mark.parametrize("words", [1, 2047, 2048 * 256 * 4 + 5, 3_000_017])
+def test_read_probe_digest(words):
+    rng = np.random.default_rng(words)
+    host = rng.integers(0, 2**32, size=(words, 4), dtype=np.uint32)
+    x = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = trt.hbm_read_probe(x)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    exp = np.bitwise_xor.reduce(host, axis=0)
+    assert np.array_equal(got, exp)
+
+
+def test_read_probe_leaves_x_unchanged():
+    x = torch.arange(1 << 16, dtype=torch.int32, device="cuda")
+    before = x.clone()
+    trt.hbm_read_probe(x)
+    torch.cuda.synchronize()
+    assert torch.equal(x, before)
+
+
+def _fragment_product(r0, r1):
+    """Result registers [64, 16] of one 32x32x16 instruction whose operand 0 /
+    operand 1 registers are r0 / r1 ([64, 8] values)."""
+    X = np.zeros((32, 16)); Y = np.zeros((16, 32))
+    for l in range(64):
+        for e in range(8):
+            X[L.mfma32_a(l, e)] = r0[l, e]
+            Y[L.mfma32_b(l, e)] = r1[l, e]
+    D = X @ Y
+    out = np.zeros((64, 16))
+    for l in range(64):
+        for r in range(16):
+            out[l, r] = D[L.mfma32_c(l, r)]
+    return out
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_mfma_loop_probe_sums(dtype):
+    rng = np.random.default_rng(5 + dtype)
+    vals = rng.integers(-1, 2, size=(1024, 8)).astype(np.float64)   # 1024 words of 8 values
+    ops = torch.from_numpy(W.to_bits(vals, dtype).view(np.int16).reshape(-1)).cuda()
+    iters = 3
+    sums = trt.mfma_loop_probe(ops, iters, dtype).cpu().numpy()
+    reg = lambda base, i: vals[base + 64 * i: base + 64 * i + 64]      # [64 lanes, 8]
+    exp = np.zeros((64, 16))
+    for q in range(16):
+        exp += iters * (_fragment_product(reg(256, q % 4), reg(0, q // 4)) +
+                        _fragment_product(reg(768, q % 4), reg(512, q // 4)))
+    # every wave of every workgroup holds the same sums
+    got = sums.reshape(256 * 4, 64, 16)
+    assert np.array_equal(got, np.broadcast_to(exp, got.shape))
+
+
+def test_mfma_loop_probe_flops():
+    assert trt.mfma_loop_probe_flops(1) == 1024 * 32 * 32768

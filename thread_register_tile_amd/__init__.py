@@ -95,6 +95,8 @@ def lib():
         L.trt_mfma_probe.restype = i32
         L.trt_hbm_read_probe.argtypes = [vp, i64, vp, i64, vp]
         L.trt_hbm_read_probe.restype = i32
+        L.trt_mfma_loop_probe.argtypes = [i32, vp, i32, vp, i64, vp]
+        L.trt_mfma_loop_probe.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
         L.trt_last_error.argtypes = []
@@ -296,3 +298,29 @@ def hbm_read_probe(x, sink=None):
     hbm_read_probe_raw(x.data_ptr(), x.numel() * x.element_size(), sink.data_ptr(),
                        sink.numel() * sink.element_size(), _stream(x.device))
     return sink.view(-1, 16)
+
+
+MFMA_PROBE_OPERAND_BYTES = 16384   # TRT_MFMA_PROBE_OPERAND_BYTES
+MFMA_PROBE_SINK_BYTES = 4194304    # TRT_MFMA_PROBE_SINK_BYTES
+
+
+def mfma_loop_probe_raw(dtype, operands, iters, sink, sink_bytes, stream=0):
+    """trt_mfma_loop_probe on raw device addresses; raises TrtError on error."""
+    _check(lib().trt_mfma_loop_probe(dtype, operands, iters, sink, sink_bytes, stream))
+
+
+def mfma_loop_probe(operands, iters, dtype=F16, sink=None):
+    """Run the matrix-core yardstick on a device tensor of 16 KiB of operand
+    data; returns the [256*256, 16] fp32 sums (one row per thread)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(MFMA_PROBE_SINK_BYTES // 4, dtype=torch.float32,
+                           device=operands.device)
+    mfma_loop_probe_raw(dtype, operands.data_ptr(), iters, sink.data_ptr(),
+                        sink.numel() * sink.element_size(), _stream(operands.device))
+    return sink.view(-1, 16)
+
+
+def mfma_loop_probe_flops(iters):
+    """FLOPs of one trt_mfma_loop_probe launch."""
+    return 256 * 4 * iters * 32 * 2 * 32 * 32 * 16

@@ -312,6 +312,40 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const trt::u32x4* __restr
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Matrix-core yardstick: every wave of 256 workgroups x 4 waves (one per
+// SIMD) runs `iters` rounds of 32 v_mfma_f32_32x32x16 on operand registers
+// taken from caller data, 16 independent accumulators, nothing else in the
+// loop; each thread then writes the sum of its accumulators (so no product
+// is dead).  Timing it gives the rate the matrix cores sustain on this part
+// under the same data and power conditions as the GEMM.
+constexpr int kMfmaProbeBlocks = 256;
+template <int DT>
+__global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const trt::u32x4* __restrict__ src,
+                                                           int iters, trt::f32x16* sink) {
+  const int t = threadIdx.x, lane = t & 63;
+  trt::u32x4 a[4], b[4], a1[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = src[i * 64 + lane];
+    b[i] = src[256 + i * 64 + lane];
+    a1[i] = src[512 + i * 64 + lane];
+    b1[i] = src[768 + i * 64 + lane];
+  }
+  trt::f32x16 acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = trt::f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = trt::mfma32<DT>(b[q % 4], a[q / 4], acc[q]);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = trt::mfma32<DT>(b1[q % 4], a1[q / 4], acc[q]);
+  }
+  trt::f32x16 sum = acc[0];
+#pragma unroll
+  for (int q = 1; q < 16; ++q) sum += acc[q];
+  sink[(int64_t)blockIdx.x * 256 + t] = sum;
+}
+
 extern "C" {
 
 trt_status trt_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
@@ -481,6 +515,32 @@ trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink, int64_t 
                      static_cast<hipStream_t>(stream), static_cast<const trt::u32x4*>(x),
                      bytes / 16, static_cast<trt::u32x4*>(sink));
   return check_launch("read probe launch");
+}
+
+trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iters, float* sink,
+                               int64_t sink_bytes, void* stream) {
+  if (!operands || !sink) return fail(TRT_ERR_NULL, "operands and sink must be non-null");
+  if (dtype != TRT_F16 && dtype != TRT_BF16)
+    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16 or TRT_BF16");
+  if (iters < 1) return fail(TRT_ERR_ARG, "iters must be positive");
+  if (sink_bytes < TRT_MFMA_PROBE_SINK_BYTES)
+    return fail(TRT_ERR_SIZE, "sink must hold TRT_MFMA_PROBE_SINK_BYTES bytes");
+  if (!aligned(operands, 16) || !aligned(sink, 64))
+    return fail(TRT_ERR_ALIGN, "operands must be 16-byte and sink 64-byte aligned");
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(operands), s0 = reinterpret_cast<uintptr_t>(sink);
+  if (o0 < s0 + (uintptr_t)TRT_MFMA_PROBE_SINK_BYTES && s0 < o0 + (uintptr_t)TRT_MFMA_PROBE_OPERAND_BYTES)
+    return fail(TRT_ERR_OVERLAP, "sink must not overlap the operands");
+  static_assert(kMfmaProbeBlocks * 256 * 64 == TRT_MFMA_PROBE_SINK_BYTES, "one sum per thread");
+  const auto* src = static_cast<const trt::u32x4*>(operands);
+  auto* dst = reinterpret_cast<trt::f32x16*>(sink);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == TRT_F16)
+    hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_F16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
+                       iters, dst);
+  else
+    hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_BF16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
+                       iters, dst);
+  return check_launch("matrix-core probe launch");
 }
 
 int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }
