@@ -7,7 +7,8 @@ imports it.
 
 * gemm_block / gemm_cells -- the fp64 GEMM + epilogue in plain C
   (gemm_ref.c), reached through ctypes.
-* decode / round16 -- the 16-bit float formats from their definitions.
+* decode / round16 / round_out -- the binary16, bfloat16 and binary32
+  formats from their definitions.
 * layout_ref -- the ownership, copy and swizzle maps in plain Python ints.
 """
 import ctypes
@@ -19,6 +20,7 @@ from . import build as _build
 
 F16 = 1
 BF16 = 2
+F32 = 3          # output / epilogue-operand dtype only
 
 _lib = None
 
@@ -39,17 +41,21 @@ def lib():
         L.orc_round_f16.argtypes = [ctypes.c_double]
         L.orc_round_bf16.restype = ctypes.c_uint16
         L.orc_round_bf16.argtypes = [ctypes.c_double]
+        L.orc_decode_f32.restype = ctypes.c_double
+        L.orc_decode_f32.argtypes = [ctypes.c_uint32]
+        L.orc_round_f32.restype = ctypes.c_uint32
+        L.orc_round_f32.argtypes = [ctypes.c_double]
         L.orc_round_array.restype = None
         L.orc_round_array.argtypes = [vp, vp, i64, i32]
         L.orc_decode_array.restype = None
         L.orc_decode_array.argtypes = [vp, vp, i64, i32]
         L.orc_gemm_block.restype = i32
         L.orc_gemm_block.argtypes = [i64, i64, i64, vp, i64, i32, vp, i64, i32,
-                                     i32, vp, i32, vp, i64, i32,
+                                     i32, vp, vp, i32, vp, i64, i32,
                                      i64, i64, i64, i64, vp, i32]
         L.orc_gemm_cells.restype = i32
         L.orc_gemm_cells.argtypes = [i64, i64, i64, vp, i64, i32, vp, i64, i32,
-                                     i32, vp, i32, vp, i64, i32,
+                                     i32, vp, vp, i32, vp, i64, i32,
                                      vp, vp, i64, vp, i32]
         L.orc_max_threads.restype = i32
         L.orc_max_threads.argtypes = []
@@ -65,46 +71,70 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _bits_type(dtype):
+    return np.uint32 if dtype == F32 else np.uint16
+
+
 def _u16(a, name):
+    return _raw(a, name, F16)
+
+
+def _raw(a, name, dtype):
+    """Validate a flat buffer of raw bit patterns of `dtype` (uint16, or
+    uint32 for binary32)."""
     if a is None:
         return None
-    if not (isinstance(a, np.ndarray) and a.dtype == np.uint16 and a.flags.c_contiguous):
-        raise TypeError(f"{name} must be a C-contiguous numpy uint16 array of raw bits")
+    t = _bits_type(dtype)
+    if not (isinstance(a, np.ndarray) and a.dtype == t and a.flags.c_contiguous):
+        raise TypeError(f"{name} must be a C-contiguous numpy {t.__name__} array of raw bits")
     return a
 
 
 def decode(bits: np.ndarray, dtype: int) -> np.ndarray:
-    """Decode raw 16-bit patterns (uint16) to float64, from the format definition."""
-    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    """Decode raw bit patterns (uint16; uint32 for F32) to float64, from the
+    format definition."""
+    b = np.ascontiguousarray(bits, dtype=_bits_type(dtype))
     out = np.empty(b.shape, dtype=np.float64)
     lib().orc_decode_array(_ptr(b), _ptr(out), b.size, dtype)
     return out
 
 
-def round16(x: np.ndarray, dtype: int) -> np.ndarray:
-    """Round float64 values to 16-bit patterns, to nearest with ties to even."""
+def round_out(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float64 values to `dtype` bit patterns (uint16, or uint32 for
+    F32), to nearest with ties to even."""
     v = np.ascontiguousarray(x, dtype=np.float64)
-    out = np.empty(v.shape, dtype=np.uint16)
+    out = np.empty(v.shape, dtype=_bits_type(dtype))
     lib().orc_round_array(_ptr(v), _ptr(out), v.size, dtype)
     return out
 
 
+def round16(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float64 values to 16-bit patterns, to nearest with ties to even."""
+    if dtype == F32:
+        raise ValueError("round16 takes a 16-bit dtype")
+    return round_out(x, dtype)
+
+
 def gemm_block(M, N, K, A, lda, opA, B, ldb, opB, in_dtype, bias=None,
-               relu=False, R=None, ldr=0, epi_dtype=None,
+               relu=False, R=None, ldr=0, out_dtype=None, scale=None,
                m_range=None, n_range=None, threads=None) -> np.ndarray:
     """fp64 reference of the block m_range x n_range of epilogue(A.B).
 
-    A, B, bias, R are flat uint16 buffers of raw bits addressed exactly as the
-    library addresses them (leading dimensions in elements, explicit op flags).
-    Returns an (m_hi-m_lo, n_hi-n_lo) float64 array, unrounded.
+    A, B are flat uint16 buffers of raw bits of `in_dtype`; scale [M], bias
+    [N] and R are flat buffers of raw bits of the output dtype (uint32 for
+    F32), addressed exactly as the library addresses them (leading
+    dimensions in elements, explicit op flags).  Returns an
+    (m_hi-m_lo, n_hi-n_lo) float64 array, unrounded.
     """
-    A = _u16(A, "A"); B = _u16(B, "B"); bias = _u16(bias, "bias"); R = _u16(R, "R")
+    od = out_dtype or in_dtype
+    A = _u16(A, "A"); B = _u16(B, "B")
+    bias = _raw(bias, "bias", od); R = _raw(R, "R", od); scale = _raw(scale, "scale", od)
     m_lo, m_hi = m_range if m_range is not None else (0, M)
     n_lo, n_hi = n_range if n_range is not None else (0, N)
     out = np.empty((m_hi - m_lo, n_hi - n_lo), dtype=np.float64)
     rc = lib().orc_gemm_block(M, N, K, _ptr(A), lda, int(opA), _ptr(B), ldb,
-                              int(opB), in_dtype, _ptr(bias), int(bool(relu)),
-                              _ptr(R), ldr, epi_dtype or in_dtype,
+                              int(opB), in_dtype, _ptr(scale), _ptr(bias),
+                              int(bool(relu)), _ptr(R), ldr, od,
                               m_lo, m_hi, n_lo, n_hi, _ptr(out),
                               threads or default_threads())
     if rc != 0:
@@ -113,15 +143,18 @@ def gemm_block(M, N, K, A, lda, opA, B, ldb, opB, in_dtype, bias=None,
 
 
 def gemm_cells(M, N, K, A, lda, opA, B, ldb, opB, in_dtype, ms, ns, bias=None,
-               relu=False, R=None, ldr=0, epi_dtype=None, threads=None) -> np.ndarray:
+               relu=False, R=None, ldr=0, out_dtype=None, scale=None,
+               threads=None) -> np.ndarray:
     """fp64 reference of the scattered cells (ms[i], ns[i]), one by one."""
-    A = _u16(A, "A"); B = _u16(B, "B"); bias = _u16(bias, "bias"); R = _u16(R, "R")
+    od = out_dtype or in_dtype
+    A = _u16(A, "A"); B = _u16(B, "B")
+    bias = _raw(bias, "bias", od); R = _raw(R, "R", od); scale = _raw(scale, "scale", od)
     ms = np.ascontiguousarray(ms, dtype=np.int64)
     ns = np.ascontiguousarray(ns, dtype=np.int64)
     out = np.empty(ms.shape, dtype=np.float64)
     rc = lib().orc_gemm_cells(M, N, K, _ptr(A), lda, int(opA), _ptr(B), ldb,
-                              int(opB), in_dtype, _ptr(bias), int(bool(relu)),
-                              _ptr(R), ldr, epi_dtype or in_dtype,
+                              int(opB), in_dtype, _ptr(scale), _ptr(bias),
+                              int(bool(relu)), _ptr(R), ldr, od,
                               _ptr(ms), _ptr(ns), ms.size, _ptr(out),
                               threads or default_threads())
     if rc != 0:
@@ -142,7 +175,7 @@ def accept(C_bits: np.ndarray, Cref: np.ndarray, out_dtype: int,
     finite = np.isfinite(C)
     bound = atol + rtol * np.abs(Cref)
     ok = bool(finite.all() and (err <= bound).all())
-    ref16 = round16(Cref, out_dtype)
+    refb = round_out(Cref, out_dtype)
     den = np.linalg.norm(Cref)
     return {
         "ok": ok,
@@ -151,5 +184,6 @@ def accept(C_bits: np.ndarray, Cref: np.ndarray, out_dtype: int,
         "max_abs": float(np.nanmax(err)) if C.size else 0.0,
         "max_rel": float(np.nanmax(err / np.maximum(np.abs(Cref), 1e-30))) if C.size else 0.0,
         "frob_rel": float(np.linalg.norm(np.nan_to_num(C - Cref)) / den) if den > 0 else 0.0,
-        "bit_match": float((np.asarray(C_bits, dtype=np.uint16) == ref16).mean()) if C.size else 1.0,
+        "bit_match": float((np.asarray(C_bits, dtype=_bits_type(out_dtype)) == refb).mean())
+        if C.size else 1.0,
     }

@@ -13,7 +13,12 @@
  * an fp32 zero accumulator, acc = acc + dot(lhs[k], rhs[k]) over the K blocks
  * in ascending order, then one cast to the output dtype.  The same page,
  * section "Contract", admits same-output-domain bias / ReLU / residual
- * postprocessing; the order used here is relu(acc + bias) + residual.
+ * postprocessing and names the two broadcast operands of a GEMM output: a
+ * column bias (axes "n", one value per column) and a row scale (axes "m",
+ * one value per row).  The order used here is
+ *   relu(acc * scale(m) + bias(n)) + residual(m,n),
+ * each term only when present.  Epilogue operands are stored in the output
+ * dtype: binary16, bfloat16 or binary32.
  *
  * The oracle takes the sum in fp64 instead of fp32: every product of two
  * 16-bit floats is exact in fp64, and the k order is ascending for every
@@ -26,6 +31,7 @@
  *   opA = 0 : A(m,k) = A[m*lda + k]      opA = 1 : A(m,k) = A[k*lda + m]
  *   opB = 0 : B(k,n) = B[k*ldb + n]      opB = 1 : B(k,n) = B[n*ldb + k]
  *   residual: R(m,n) = R[m*ldr + n]      bias:     bias(n) = bias[n]
+ *   row scale: scale(m) = scale[m]
  */
 #include <math.h>
 #include <stdint.h>
@@ -38,6 +44,7 @@
 
 #define ORC_F16 1
 #define ORC_BF16 2
+#define ORC_F32 3
 
 /* ---- 16-bit formats, decoded from their definitions -------------------- */
 
@@ -75,19 +82,42 @@ double orc_decode_bf16(uint16_t h) {
   return sign ? -v : v;
 }
 
+/* IEEE binary32: 1 sign bit, 8 exponent bits (bias 127), 23 fraction bits.
+ * Exponent field 0 holds zeros and subnormals (fraction * 2^-149); field 255
+ * holds infinities and NaNs. */
+double orc_decode_f32(uint32_t w) {
+  int sign = (int)((w >> 31) & 1u);
+  int expo = (int)((w >> 23) & 0xffu);
+  int32_t frac = (int32_t)(w & 0x7fffffu);
+  double v;
+  if (expo == 0)
+    v = ldexp((double)frac, -149);
+  else if (expo == 255)
+    v = frac ? NAN : INFINITY;
+  else
+    v = ldexp((double)(frac + (1 << 23)), expo - 150); /* (1 + f/2^23) * 2^(e-127) */
+  return sign ? -v : v;
+}
+
 static double decode(uint16_t h, int dtype) {
   return dtype == ORC_BF16 ? orc_decode_bf16(h) : orc_decode_f16(h);
 }
 
-/* Round an fp64 value to a 16-bit float, to nearest with ties to even.
- * frac_bits: 10 (binary16) or 7 (bfloat16); emin: -14 or -126;
- * emax: 15 or 127.  The significand is scaled by a power of two (exact) and
- * rounded with nearbyint() under the default round-to-nearest-even mode. */
-static uint16_t round_to_16(double x, int frac_bits, int emin, int emax,
-                            int exp_bits) {
-  uint16_t sign = signbit(x) ? 0x8000 : 0;
-  uint16_t inf = (uint16_t)(((1u << exp_bits) - 1) << frac_bits);
-  if (isnan(x)) return (uint16_t)(inf | (1u << (frac_bits - 1))); /* quiet NaN */
+/* Element i of a buffer of the given dtype (16-bit patterns or binary32 words). */
+static double decode_at(const void* p, int64_t i, int dtype) {
+  if (dtype == ORC_F32) return orc_decode_f32(((const uint32_t*)p)[i]);
+  return decode(((const uint16_t*)p)[i], dtype);
+}
+
+/* Round an fp64 value to a binary float format, to nearest with ties to
+ * even.  frac_bits: 10 (binary16), 7 (bfloat16) or 23 (binary32); emin:
+ * -14, -126, -126; emax: 15, 127, 127; exp_bits: 5, 8, 8.  The significand
+ * is scaled by a power of two (exact) and rounded with nearbyint() under the
+ * default round-to-nearest-even mode.  Returns the bit pattern. */
+static uint32_t round_bits(double x, int frac_bits, int emin, int emax, int exp_bits) {
+  uint32_t sign = signbit(x) ? (1u << (frac_bits + exp_bits)) : 0u;
+  uint32_t inf = ((1u << exp_bits) - 1u) << frac_bits;
+  if (isnan(x)) return inf | (1u << (frac_bits - 1)); /* quiet NaN */
   double ax = fabs(x);
   if (isinf(ax)) return sign | inf;
   if (ax == 0.0) return sign;
@@ -99,7 +129,7 @@ static uint16_t round_to_16(double x, int frac_bits, int emin, int emax,
     double q = nearbyint(ldexp(ax, frac_bits - emin));
     /* q == 2^frac_bits rounds up into the smallest normal, which has the
      * same bit pattern as the fraction overflowing into the exponent. */
-    return sign | (uint16_t)q;
+    return sign | (uint32_t)q;
   }
   double q = nearbyint(ldexp(ax, frac_bits - E)); /* in [2^fb, 2^(fb+1)] */
   if (q == ldexp(1.0, frac_bits + 1)) {
@@ -107,21 +137,27 @@ static uint16_t round_to_16(double x, int frac_bits, int emin, int emax,
     E += 1;
   }
   if (E > emax) return sign | inf;
-  uint16_t expo_field = (uint16_t)(E + ((1 << (exp_bits - 1)) - 1));
-  uint16_t frac_field = (uint16_t)((int64_t)q - (1 << frac_bits));
-  return sign | (uint16_t)(expo_field << frac_bits) | frac_field;
+  uint32_t expo_field = (uint32_t)(E + ((1 << (exp_bits - 1)) - 1));
+  uint32_t frac_field = (uint32_t)((int64_t)q - ((int64_t)1 << frac_bits));
+  return sign | (expo_field << frac_bits) | frac_field;
 }
 
-uint16_t orc_round_f16(double x) { return round_to_16(x, 10, -14, 15, 5); }
-uint16_t orc_round_bf16(double x) { return round_to_16(x, 7, -126, 127, 8); }
+uint16_t orc_round_f16(double x) { return (uint16_t)round_bits(x, 10, -14, 15, 5); }
+uint16_t orc_round_bf16(double x) { return (uint16_t)round_bits(x, 7, -126, 127, 8); }
+uint32_t orc_round_f32(double x) { return round_bits(x, 23, -126, 127, 8); }
 
-void orc_round_array(const double* x, uint16_t* out, int64_t n, int dtype) {
-  for (int64_t i = 0; i < n; ++i)
-    out[i] = dtype == ORC_BF16 ? orc_round_bf16(x[i]) : orc_round_f16(x[i]);
+/* Round n values to `dtype`: 16-bit patterns, or binary32 words for ORC_F32. */
+void orc_round_array(const double* x, void* out, int64_t n, int dtype) {
+  for (int64_t i = 0; i < n; ++i) {
+    if (dtype == ORC_F32)
+      ((uint32_t*)out)[i] = orc_round_f32(x[i]);
+    else
+      ((uint16_t*)out)[i] = dtype == ORC_BF16 ? orc_round_bf16(x[i]) : orc_round_f16(x[i]);
+  }
 }
 
-void orc_decode_array(const uint16_t* h, double* out, int64_t n, int dtype) {
-  for (int64_t i = 0; i < n; ++i) out[i] = decode(h[i], dtype);
+void orc_decode_array(const void* h, double* out, int64_t n, int dtype) {
+  for (int64_t i = 0; i < n; ++i) out[i] = decode_at(h, i, dtype);
 }
 
 /* ---- the GEMM and its epilogue ------------------------------------------ */
@@ -136,14 +172,17 @@ static double elem_b(const uint16_t* B, int64_t ldb, int opB, int64_t k,
   return decode(opB ? B[n * ldb + k] : B[k * ldb + n], dt);
 }
 
-/* Epilogue of one cell, in fp64: y = acc; y += bias(n); y = max(y, 0);
- * y += R(m,n).  Each step only when its operand or flag is present. */
-static double epilogue(double acc, int64_t m, int64_t n, const uint16_t* bias,
-                       int relu, const uint16_t* R, int64_t ldr, int epi_dt) {
+/* Epilogue of one cell, in fp64: y = acc; y *= scale(m); y += bias(n);
+ * y = max(y, 0); y += R(m,n).  Each step only when its operand or flag is
+ * present; scale, bias and R hold elements of the output dtype out_dt. */
+static double epilogue(double acc, int64_t m, int64_t n, const void* scale,
+                       const void* bias, int relu, const void* R, int64_t ldr,
+                       int out_dt) {
   double y = acc;
-  if (bias) y += decode(bias[n], epi_dt);
+  if (scale) y *= decode_at(scale, m, out_dt);
+  if (bias) y += decode_at(bias, n, out_dt);
   if (relu) y = y > 0.0 ? y : 0.0;
-  if (R) y += decode(R[m * ldr + n], epi_dt);
+  if (R) y += decode_at(R, m * ldr + n, out_dt);
   return y;
 }
 
@@ -159,8 +198,8 @@ static double epilogue(double acc, int64_t m, int64_t n, const uint16_t* bias,
  */
 int orc_gemm_block(int64_t M, int64_t N, int64_t K, const uint16_t* A,
                    int64_t lda, int opA, const uint16_t* B, int64_t ldb,
-                   int opB, int in_dt, const uint16_t* bias, int relu,
-                   const uint16_t* R, int64_t ldr, int epi_dt, int64_t m_lo,
+                   int opB, int in_dt, const void* scale, const void* bias,
+                   int relu, const void* R, int64_t ldr, int out_dt, int64_t m_lo,
                    int64_t m_hi, int64_t n_lo, int64_t n_hi, double* out,
                    int nthreads) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
@@ -187,7 +226,7 @@ int orc_gemm_block(int64_t M, int64_t N, int64_t K, const uint16_t* A,
       for (int64_t j = 0; j < W; ++j) acc[j] += a * brow[j];
     }
     for (int64_t j = 0; j < W; ++j)
-      acc[j] = epilogue(acc[j], m, n_lo + j, bias, relu, R, ldr, epi_dt);
+      acc[j] = epilogue(acc[j], m, n_lo + j, scale, bias, relu, R, ldr, out_dt);
   }
   free(Bd);
   return 0;
@@ -198,8 +237,8 @@ int orc_gemm_block(int64_t M, int64_t N, int64_t K, const uint16_t* A,
  * large for a full oracle run. */
 int orc_gemm_cells(int64_t M, int64_t N, int64_t K, const uint16_t* A,
                    int64_t lda, int opA, const uint16_t* B, int64_t ldb,
-                   int opB, int in_dt, const uint16_t* bias, int relu,
-                   const uint16_t* R, int64_t ldr, int epi_dt,
+                   int opB, int in_dt, const void* scale, const void* bias,
+                   int relu, const void* R, int64_t ldr, int out_dt,
                    const int64_t* ms, const int64_t* ns, int64_t count,
                    double* out, int nthreads) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
@@ -214,7 +253,7 @@ int orc_gemm_cells(int64_t M, int64_t N, int64_t K, const uint16_t* A,
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k)
       acc += elem_a(A, lda, opA, m, k, in_dt) * elem_b(B, ldb, opB, k, n, in_dt);
-    out[i] = epilogue(acc, m, n, bias, relu, R, ldr, epi_dt);
+    out[i] = epilogue(acc, m, n, scale, bias, relu, R, ldr, out_dt);
   }
   return 0;
 }

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import F16, BF16
+from oracle import F16, BF16, F32
 
 
 def f16_bits(x):
@@ -80,6 +80,44 @@ def test_round_bf16_is_direct_from_fp64():
     assert oracle.round16(np.array([1.0 + 2 ** -8 + 2 ** -40]), BF16)[0] == 0x3F81
     assert oracle.round16(np.array([1.0 + 2 ** -8]), BF16)[0] == 0x3F80
     assert oracle.round16(np.array([1.0 + 3 * 2 ** -8]), BF16)[0] == 0x3F82
+
+
+def test_decode_f32_against_numpy():
+    # every exponent field with random fractions, plus the special classes
+    rng = np.random.default_rng(13)
+    expo = np.repeat(np.arange(256, dtype=np.uint32), 512)
+    frac = rng.integers(0, 1 << 23, expo.size, dtype=np.uint32)
+    sign = rng.integers(0, 2, expo.size, dtype=np.uint32)
+    bits = (sign << 31) | (expo << 23) | frac
+    bits = np.concatenate([bits, np.array([0, 0x80000000, 1, 0x807FFFFF, 0x7F800000,
+                                           0xFF800000, 0x7FC00000, 0x7F7FFFFF],
+                                          dtype=np.uint32)])
+    got = oracle.decode(bits, F32)
+    ref = bits.view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_round_f32_matches_numpy():
+    # numpy converts float64 -> float32 with round-half-to-even; the ties are
+    # exact midpoints of neighbouring float32 values, including subnormals
+    rng = np.random.default_rng(14)
+    x = np.concatenate([
+        rng.standard_normal(50000) * 10.0 ** rng.integers(-45, 39, 50000),
+        rng.uniform(-1, 1, 20000) * 2.0 ** -126,
+        np.array([0.0, -0.0, 3.4028234663852886e38, 3.4028235677973366e38, 1e39,
+                  2.0 ** -149, 2.0 ** -150, 3 * 2.0 ** -150, 2.0 ** -151]),
+    ])
+    lo = rng.standard_normal(20000).astype(np.float32)
+    hi = np.nextafter(lo, np.float32(np.inf))
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2
+    x = np.concatenate([x, mid])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32).view(np.uint32)
+    got = oracle.round_out(x, F32)
+    assert np.array_equal(got, ref)
 
 
 # ---- GEMM closed forms ----------------------------------------------------------
@@ -284,3 +322,88 @@ def test_accept_rule():
     nan = bits.copy()
     nan[0, 0] = 0x7E00
     assert not oracle.accept(nan, Cref, F16)["ok"]
+
+
+# ---- row scale and output dtypes ------------------------------------------------
+# "Named layouts" (NineToothed), section "Contract": a row scale is the
+# broadcast operand of axes "m"; the epilogue is relu(acc * scale + bias) + R.
+
+def test_row_scale_identity_closed_form():
+    rng = np.random.default_rng(21)
+    M, K = 6, 5
+    A = f16_bits(rng.uniform(-2, 2, (M, K)))
+    I = f16_bits(np.eye(K))
+    s = f16_bits(rng.uniform(-3, 3, M))
+    a = oracle.decode(A, F16).reshape(M, K)
+    sv = oracle.decode(s, F16)
+    C = gemm(M, K, K, A, I, scale=s)
+    assert np.array_equal(C, sv[:, None] * a)
+    bias = f16_bits(rng.uniform(-2, 2, K))
+    R = f16_bits(rng.uniform(-2, 2, (M, K)))
+    C = gemm(M, K, K, A, I, scale=s, bias=bias, relu=True, R=R, ldr=K)
+    exp = np.maximum(sv[:, None] * a + oracle.decode(bias, F16)[None, :], 0) + \
+        oracle.decode(R, F16).reshape(M, K)
+    assert np.array_equal(C, exp)
+
+
+def test_row_scale_applies_before_bias():
+    # acc = 2 (K = 1), scale 3, bias -5: scale then bias gives 1; bias then
+    # scale would give -9 (0 after ReLU); scale after ReLU would give 0
+    A = f16_bits(np.full((2, 1), 2.0))
+    B = f16_bits(np.ones((1, 3)))
+    s = f16_bits(np.full(2, 3.0))
+    bias = f16_bits(np.full(3, -5.0))
+    C = gemm(2, 3, 1, A, B, scale=s, bias=bias, relu=True)
+    assert np.array_equal(C, np.ones((2, 3)))
+
+
+def test_row_scale_all_ones_gives_k_times_scale():
+    M, N, K = 4, 3, 9
+    s = f16_bits(np.array([1.0, -2.0, 0.5, 0.0]))
+    C = gemm(M, N, K, f16_bits(np.ones((M, K))), f16_bits(np.ones((K, N))), scale=s)
+    assert np.array_equal(C, np.array([9.0, -18.0, 4.5, 0.0])[:, None] * np.ones((M, N)))
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [(F16, BF16), (BF16, F16), (F16, F32), (BF16, F32)])
+def test_brute_force_exact_with_scale_and_mixed_dtypes(in_dt, out_dt):
+    rng = np.random.default_rng(22)
+    M, N, K = 3, 5, 7
+    A = oracle.round16(rng.uniform(-3, 3, (M, K)), in_dt)
+    B = oracle.round16(rng.uniform(-3, 3, (K, N)), in_dt)
+    s = oracle.round_out(rng.uniform(-2, 2, M), out_dt)
+    bias = oracle.round_out(rng.uniform(-2, 2, N), out_dt)
+    R = oracle.round_out(rng.uniform(-2, 2, (M, N)), out_dt).reshape(-1)
+    a = oracle.decode(A, in_dt).reshape(M, K)
+    b = oracle.decode(B, in_dt).reshape(K, N)
+    sv, bv = oracle.decode(s, out_dt), oracle.decode(bias, out_dt)
+    rv = oracle.decode(R, out_dt).reshape(M, N)
+    exact = _exact_sum(a, b)
+    C = gemm(M, N, K, A, B, dt=in_dt, out_dtype=out_dt, scale=s, bias=bias, R=R, ldr=N)
+    for m in range(M):
+        for n in range(N):
+            e = exact[m][n] * Fraction(sv[m]) + Fraction(bv[n]) + Fraction(rv[m, n])
+            bound = 4 * K * 2.0 ** -53 * (abs(sv[m]) * sum(abs(a[m, k] * b[k, n]) for k in range(K))
+                                          + abs(bv[n]) + abs(rv[m, n]))
+            assert abs(Fraction(C[m, n]) - e) <= Fraction(bound)
+
+
+def test_f32_epilogue_operands_are_read_as_binary32():
+    # a value only binary32 can hold (1 + 2^-20) must survive as is
+    v = np.array([1.0 + 2.0 ** -20], dtype=np.float32)
+    bias = np.ascontiguousarray(np.repeat(v, 2).view(np.uint32))
+    C = gemm(1, 2, 1, f16_bits(np.zeros((1, 1))), f16_bits(np.zeros((1, 2))),
+             out_dtype=F32, bias=bias)
+    assert np.array_equal(C, np.full((1, 2), 1.0 + 2.0 ** -20))
+
+
+def test_accept_rule_f32_output():
+    Cref = np.array([[1.0 + 2.0 ** -30, -2.0], [100.0, 0.0]])
+    bits = oracle.round_out(Cref, F32)
+    rep = oracle.accept(bits, Cref, F32)
+    assert rep["ok"] and rep["bit_match"] == 1.0
+    bad = bits.copy()
+    bad[1, 0] = np.array([102.0], dtype=np.float32).view(np.uint32)[0]
+    assert not oracle.accept(bad, Cref, F32)["ok"]
+    nan = bits.copy()
+    nan[0, 0] = 0x7FC00000
+    assert not oracle.accept(nan, Cref, F32)["ok"]
