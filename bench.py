@@ -213,18 +213,23 @@ def main():
     w = W.CONFIGS[args.workload]
     tile = tuple(int(x) for x in args.tile.split(",")) if args.tile else w.tile
     host = W.make_inputs(w)
-    dev = lambda b: None if b is None else torch.from_numpy(b.view(np.int16)).cuda()
+    dev = lambda b: None if b is None else torch.from_numpy(
+        b.view(np.int32 if b.dtype == np.uint32 else np.int16)).cuda()
     A, B, bias, R = dev(host["A"]), dev(host["B"]), dev(host["bias"]), dev(host["R"])
-    C = torch.empty(w.M * w.ldc_, dtype=torch.int16, device="cuda")
+    scale = dev(host["scale"])
+    out_bytes = W.ELEM_BYTES[w.odt]
+    C = torch.empty(w.M * w.ldc_, dtype=torch.int32 if out_bytes == 4 else torch.int16,
+                    device="cuda")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
     def step():
         trt.gemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, w.opA, B.data_ptr(), w.ldb_, w.opB,
-                     C.data_ptr(), w.ldc_, w.dtype, w.dtype,
+                     C.data_ptr(), w.ldc_, w.dtype, w.odt,
                      bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
                      residual=R.data_ptr() if R is not None else 0,
-                     ldr=w.ldr_ if R is not None else 0, tile=tile, stream=sptr)
+                     ldr=w.ldr_ if R is not None else 0,
+                     scale=scale.data_ptr() if scale is not None else 0, tile=tile, stream=sptr)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
@@ -305,6 +310,7 @@ def main():
             oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,
                               w.opB, w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
                               ldr=w.ldr_ if host["R"] is not None else 0,
+                              out_dtype=w.odt, scale=host["scale"],
                               m_range=(0, r), threads=threads)
             return time.perf_counter() - t0
         r1 = min(threads, w.M)
@@ -318,14 +324,16 @@ def main():
         ref = oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,
                                 w.opB, w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
                                 ldr=w.ldr_ if host["R"] is not None else 0,
+                                out_dtype=w.odt, scale=host["scale"],
                                 m_range=(0, rows), threads=threads)
         t_cpu = time.perf_counter() - t0
         cpu_tflops = 2.0 * rows * w.N * w.K / t_cpu / 1e12
         cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, fp64 oracle incl. "
                          f"epilogue), {t_cpu:.1f} s"}
-        Cg = C.cpu().numpy().view(np.uint16).reshape(w.M, w.ldc_)[:rows, :w.N]
-        rep = oracle.accept(np.ascontiguousarray(Cg), ref, w.dtype)
+        Cg = C.cpu().numpy().view(np.uint32 if out_bytes == 4 else np.uint16)
+        Cg = Cg.reshape(w.M, w.ldc_)[:rows, :w.N]
+        rep = oracle.accept(np.ascontiguousarray(Cg), ref, w.odt)
         parity = {"rows": rows, "ok": rep["ok"], "max_abs": rep["max_abs"],
                   "frob_rel": rep["frob_rel"], "bit_match": rep["bit_match"]}
 
@@ -346,7 +354,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "opA": w.opA,
                    "opB": w.opB, "lda": w.lda_, "ldb": w.ldb_, "ldc": w.ldc_,
-                   "epilogue": {"bias": w.bias, "relu": w.relu, "residual": w.residual},
+                   "out_dtype": W.DTYPE_NAMES[w.odt],
+                   "epilogue": {"bias": w.bias, "relu": w.relu, "residual": w.residual,
+                                "row_scale": w.row_scale},
                    "tile": list(tile) if tile else "auto", "csrc_digest": csrc_digest()},
         "roofline": roofline,
         "cpu_baseline": cpu,

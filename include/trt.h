@@ -10,8 +10,8 @@
  * computed by a grid of workgroups, each owning one logical [BM,BN] tile of C
  * and consuming [BM,BK] / [BK,BN] operand tiles per K step.  Products are
  * accumulated in fp32 and cast once, at the end, to the output dtype.  The
- * epilogue, when requested, is  y = relu(acc + bias[n]) + R[m,n]  with each
- * term optional, evaluated in fp32 before the single cast.
+ * epilogue, when requested, is  y = relu(acc * row_scale[m] + bias[n]) + R[m,n]
+ * with each term optional, evaluated in fp32 before the single cast.
  *
  * The library has no global mutable state and never allocates: all buffers
  * belong to the caller.  Every call validates its arguments on the host
@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 2
+#define TRT_ABI_VERSION 3
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -36,7 +36,7 @@ typedef enum {
   TRT_ERR_SIZE = 1,        /* M, N or K < 1, or an extent that overflows int64 */
   TRT_ERR_STRIDE = 2,      /* an input leading dimension < 1, or ldc < N       */
   TRT_ERR_NULL = 3,        /* A, B or C is NULL (or a required output buffer)  */
-  TRT_ERR_ALIGN = 4,       /* a pointer not aligned to its 2-byte element      */
+  TRT_ERR_ALIGN = 4,       /* a pointer not aligned to its element             */
   TRT_ERR_OVERLAP = 5,     /* C's byte range meets an input's byte range       */
   TRT_ERR_DTYPE = 6,       /* unsupported input/output dtype combination       */
   TRT_ERR_UNSUPPORTED = 7, /* no compiled kernel for the requested tile / map  */
@@ -44,8 +44,10 @@ typedef enum {
   TRT_ERR_ARG = 9          /* any other invalid argument (op flag, map id...)  */
 } trt_status;
 
-/* Element types.  Inputs and outputs are IEEE binary16 or bfloat16. */
-typedef enum { TRT_F16 = 1, TRT_BF16 = 2 } trt_dtype;
+/* Element types.  Inputs (A, B) are IEEE binary16 or bfloat16; the output
+ * C and the epilogue operands (bias, residual, row scale), which share the
+ * output dtype, may also be IEEE binary32. */
+typedef enum { TRT_F16 = 1, TRT_BF16 = 2, TRT_F32 = 3 } trt_dtype;
 
 /* Storage of an operand.  An operand is never transposed implicitly
  * ("Named layouts", section "Contract": a transpose is explicit):
@@ -59,15 +61,21 @@ typedef enum { TRT_OP_N = 0, TRT_OP_T = 1 } trt_op;
 
 /* Optional same-output-domain postprocessing ("Named layouts", section
  * "Contract": bias / ReLU / residual on the output's own domain; a column
- * bias spans the n axis only and broadcasts over m).  bias: [N] elements of
- * out_dtype, or NULL.  residual: R(m,n) = residual[m*ldr + n] of out_dtype, or
- * NULL.  relu != 0 applies max(y, 0) after the bias and before the
- * residual.  Passing NULL for the whole struct means a plain GEMM. */
+ * bias spans the n axis only and broadcasts over m, a row scale spans the m
+ * axis only and broadcasts over n).  With acc the fp32 sum of products:
+ *   y = acc * row_scale[m]   (if row_scale)
+ *   y = y + bias[n]          (if bias)
+ *   y = max(y, 0)            (if relu)
+ *   y = y + R(m,n)           (if residual)
+ * bias: [N] elements of out_dtype, or NULL.  row_scale: [M] elements of
+ * out_dtype, or NULL.  residual: R(m,n) = residual[m*ldr + n] of out_dtype,
+ * or NULL.  Passing NULL for the whole struct means a plain GEMM. */
 typedef struct {
   const void* bias;
   int32_t relu;
   const void* residual;
   int64_t ldr;
+  const void* row_scale;
 } trt_epilogue;
 
 /* A workgroup tile: the logical [bm, bn] output tile and the K step bk.
@@ -84,10 +92,12 @@ typedef struct {
  * sizes are positive).  lda, ldb and (when a residual is given) ldr >= 1:
  * input strides are positive; input rows may overlap.  ldc >= N: output
  * writes never overlap each other.  C's byte range must not meet the byte
- * range of A, B, bias or residual -- an in-place residual is rejected, since
- * safety that cannot be proven is an error.  A, B, C must be non-NULL and all
- * pointers 2-byte aligned.  in_dtype must equal out_dtype (TRT_F16 or
- * TRT_BF16).  Elements of C outside [0,M) x [0,N) (the ldc padding) are never
+ * range of A, B, bias, residual or row_scale -- an in-place residual is
+ * rejected, since safety that cannot be proven is an error.  A, B, C must be
+ * non-NULL; A and B 2-byte aligned, C and the epilogue operands aligned to
+ * the output element (2 or 4 bytes).  in_dtype is TRT_F16 or TRT_BF16;
+ * out_dtype is TRT_F16, TRT_BF16 or TRT_F32, independently of in_dtype
+ * (otherwise TRT_ERR_DTYPE).  Elements of C outside [0,M) x [0,N) (the ldc padding) are never
  * written.  Elements of A and B outside the logical operands (the lda/ldb
  * padding) never influence C, and no byte outside an operand's extent
  * ((rows-1)*ld + cols elements from its base) is ever read.

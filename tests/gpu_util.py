@@ -9,12 +9,15 @@ import thread_register_tile_amd as trt
 import workloads as W
 
 GUARD = 2048            # elements of sentinel before and after C
-SENTINEL = 0x7BAD       # a finite f16/bf16 pattern the kernel never writes by chance
+# finite patterns the kernel never writes by chance: 16-bit and binary32 outputs
+SENTINEL = {W.F16: 0x7BAD, W.BF16: 0x7BAD, W.F32: 0x7BAD7BAD}
 
 
 def to_dev(bits):
     if bits is None:
         return None
+    if bits.dtype == np.uint32:
+        return torch.from_numpy(bits.view(np.int32)).to("cuda")
     return torch.from_numpy(bits.view(np.int16)).to("cuda")
 
 
@@ -28,45 +31,56 @@ class Run:
         self.B = to_dev(self.host["B"])
         self.bias = to_dev(self.host["bias"])
         self.R = to_dev(self.host["R"])
+        self.scale = to_dev(self.host.get("scale"))
         self.ldc = ldc or w.ldc_
         n_c = (w.M - 1) * self.ldc + w.N
-        self.Cbuf = torch.full((n_c + 2 * GUARD,), SENTINEL, dtype=torch.int16, device="cuda")
+        self.sentinel = SENTINEL[w.odt]
+        self.esize = W.ELEM_BYTES[w.odt]
+        tdt = torch.int32 if self.esize == 4 else torch.int16
+        self.Cbuf = torch.full((n_c + 2 * GUARD,), self.sentinel - (1 << 32 if self.esize == 4 and
+                                                                  self.sentinel >= 1 << 31 else 0),
+                               dtype=tdt, device="cuda")
 
     def c_ptr(self):
-        return self.Cbuf.data_ptr() + 2 * GUARD
+        return self.Cbuf.data_ptr() + self.esize * GUARD
 
     def launch(self, tile=None):
         w = self.w
         trt.gemm_raw(w.M, w.N, w.K, self.A.data_ptr(), w.lda_, w.opA, self.B.data_ptr(),
-                     w.ldb_, w.opB, self.c_ptr(), self.ldc, w.dtype, w.dtype,
+                     w.ldb_, w.opB, self.c_ptr(), self.ldc, w.dtype, w.odt,
                      bias=self.bias.data_ptr() if self.bias is not None else 0,
                      relu=w.relu,
                      residual=self.R.data_ptr() if self.R is not None else 0,
                      ldr=w.ldr_ if self.R is not None else 0,
+                     scale=self.scale.data_ptr() if self.scale is not None else 0,
                      tile=tile if tile is not None else w.tile,
                      stream=torch.cuda.current_stream().cuda_stream)
 
     def result(self):
-        """C as an (M, N) uint16 array; asserts guards and ldc padding intact."""
+        """C as an (M, N) array of raw bits (uint16, or uint32 for binary32
+        output); asserts guards and ldc padding intact."""
         torch.cuda.synchronize()
-        buf = self.Cbuf.cpu().numpy().view(np.uint16)
+        ut = np.uint32 if self.esize == 4 else np.uint16
+        buf = self.Cbuf.cpu().numpy().view(ut)
         w = self.w
-        assert (buf[:GUARD] == SENTINEL).all(), "write before C"
-        assert (buf[-GUARD:] == SENTINEL).all(), "write after C"
+        SENT = ut(self.sentinel)
+        assert (buf[:GUARD] == SENT).all(), "write before C"
+        assert (buf[-GUARD:] == SENT).all(), "write after C"
         body = buf[GUARD:-GUARD]
-        full = np.full(w.M * self.ldc, SENTINEL, dtype=np.uint16)
+        full = np.full(w.M * self.ldc, SENT, dtype=ut)
         full[:body.size] = body
         full = full.reshape(w.M, self.ldc)
         if self.ldc > w.N:
             pad = full[:-1, w.N:] if w.M > 1 else full[:0, w.N:]
-            assert (pad == SENTINEL).all(), "write into ldc padding"
+            assert (pad == SENT).all(), "write into ldc padding"
         return np.ascontiguousarray(full[:, :w.N])
 
 
 def oracle_args(w: W.Workload, host):
     return dict(M=w.M, N=w.N, K=w.K, A=host["A"], lda=w.lda_, opA=w.opA, B=host["B"],
                 ldb=w.ldb_, opB=w.opB, in_dtype=w.dtype, bias=host["bias"], relu=w.relu,
-                R=host["R"], ldr=w.ldr_ if host["R"] is not None else 0)
+                R=host["R"], ldr=w.ldr_ if host["R"] is not None else 0,
+                out_dtype=w.odt, scale=host.get("scale"))
 
 
 def reference_block(w, host, m_range=None, n_range=None):

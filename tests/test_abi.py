@@ -49,12 +49,12 @@ def args(**kw):
     return a
 
 
-def status(tile=None, bias=0, relu=False, residual=0, ldr=0, **kw):
+def status(tile=None, bias=0, relu=False, residual=0, ldr=0, scale=0, **kw):
     a = args(**kw)
     return trt.validate_raw(a["M"], a["N"], a["K"], a["A"], a["lda"], a["opA"], a["B"],
                             a["ldb"], a["opB"], a["C"], a["ldc"], a["in_dtype"],
                             a["out_dtype"], bias=bias, relu=relu, residual=residual,
-                            ldr=ldr, tile=tile)
+                            ldr=ldr, scale=scale, tile=tile)
 
 
 def test_valid_call():
@@ -72,7 +72,7 @@ def test_valid_call():
     (dict(A=0), trt.ERR_NULL), (dict(B=0), trt.ERR_NULL), (dict(C=0), trt.ERR_NULL),
     (dict(A=BASE + 1), trt.ERR_ALIGN), (dict(C=BASE * 3 + 1), trt.ERR_ALIGN),
     (dict(in_dtype=3, out_dtype=3), trt.ERR_DTYPE),
-    (dict(in_dtype=trt.F16, out_dtype=trt.BF16), trt.ERR_DTYPE),
+    (dict(in_dtype=trt.F32, out_dtype=trt.F32), trt.ERR_DTYPE),
     (dict(opA=2), trt.ERR_ARG), (dict(opB=-1), trt.ERR_ARG),
     # C overlapping an input: any byte in common is an error
     (dict(C=BASE + 64 * 2), trt.ERR_OVERLAP),
@@ -240,3 +240,40 @@ def test_mfma_probe_rejections(kw, code):
     with pytest.raises(trt.TrtError) as e:
         trt.mfma_loop_probe_raw(a["dtype"], a["ops"], a["iters"], a["sink"], a["sink_bytes"])
     assert e.value.status == code
+
+
+# ---- output dtypes and the row scale ----------------------------------------------
+
+def test_epilogue_struct_layout():
+    import ctypes
+    # include/trt.h: bias, relu, residual, ldr, row_scale (row_scale appended)
+    assert ctypes.sizeof(trt.Epilogue) == 40
+    assert trt.Epilogue.row_scale.offset == 32
+
+
+def test_output_dtypes_accepted():
+    for i in (trt.F16, trt.BF16):
+        for o in (trt.F16, trt.BF16, trt.F32):
+            assert status(in_dtype=i, out_dtype=o) == trt.OK, (i, o)
+    assert status(in_dtype=trt.F32, out_dtype=trt.F32) == trt.ERR_DTYPE
+    assert status(in_dtype=trt.F16, out_dtype=4) == trt.ERR_DTYPE
+
+
+def test_f32_output_alignment_and_extent():
+    # C, bias, residual and row scale are aligned to the 4-byte output element
+    assert status(out_dtype=trt.F32, C=BASE * 3 + 2) == trt.ERR_ALIGN
+    assert status(out_dtype=trt.F32, bias=BASE * 4 + 2) == trt.ERR_ALIGN
+    assert status(out_dtype=trt.F32, scale=BASE * 4 + 2) == trt.ERR_ALIGN
+    assert status(out_dtype=trt.F16, scale=BASE * 4 + 2) == trt.OK
+    # C of 4-byte elements spans 4*(63*64 + 64) bytes
+    c_bytes = 4 * (63 * 64 + 64)
+    assert status(out_dtype=trt.F32, C=BASE - c_bytes) == trt.OK
+    assert status(out_dtype=trt.F32, C=BASE - c_bytes + 4) == trt.ERR_OVERLAP
+
+
+def test_row_scale_overlap_rejected():
+    # the row scale spans M elements of the output type
+    assert status(scale=BASE * 3 + 2 * 10) == trt.ERR_OVERLAP
+    assert status(scale=BASE * 3 - 2 * 64) == trt.OK          # ends where C starts
+    assert status(scale=BASE * 3 - 2 * 64 + 2) == trt.ERR_OVERLAP
+    assert status(out_dtype=trt.F32, scale=BASE * 3 - 4 * 64 + 4) == trt.ERR_OVERLAP

@@ -25,7 +25,7 @@ STATUS_NAMES = {OK: "TRT_OK", ERR_SIZE: "TRT_ERR_SIZE", ERR_STRIDE: "TRT_ERR_STR
                 ERR_UNSUPPORTED: "TRT_ERR_UNSUPPORTED", ERR_HIP: "TRT_ERR_HIP",
                 ERR_ARG: "TRT_ERR_ARG"}
 
-F16, BF16 = 1, 2
+F16, BF16, F32 = 1, 2, 3
 OP_N, OP_T = 0, 1
 
 MAP_C_OWNER = 0
@@ -49,7 +49,8 @@ class TrtError(RuntimeError):
 
 class Epilogue(ctypes.Structure):
     _fields_ = [("bias", ctypes.c_void_p), ("relu", ctypes.c_int32),
-                ("residual", ctypes.c_void_p), ("ldr", ctypes.c_int64)]
+                ("residual", ctypes.c_void_p), ("ldr", ctypes.c_int64),
+                ("row_scale", ctypes.c_void_p)]
 
 
 class TileDesc(ctypes.Structure):
@@ -124,27 +125,28 @@ def _tile(tile):
     return ctypes.byref(TileDesc(*tile))
 
 
-def _epi(bias_ptr, relu, res_ptr, ldr):
-    if not bias_ptr and not relu and not res_ptr:
+def _epi(bias_ptr, relu, res_ptr, ldr, scale_ptr=0):
+    if not bias_ptr and not relu and not res_ptr and not scale_ptr:
         return None
-    return ctypes.byref(Epilogue(bias_ptr or None, int(bool(relu)), res_ptr or None, ldr))
+    return ctypes.byref(Epilogue(bias_ptr or None, int(bool(relu)), res_ptr or None, ldr,
+                                 scale_ptr or None))
 
 
 # ---- raw entry points (pointers and sizes, as in include/trt.h) --------------
 
 def gemm_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
-             bias=0, relu=False, residual=0, ldr=0, tile=None, stream=0):
+             bias=0, relu=False, residual=0, ldr=0, scale=0, tile=None, stream=0):
     """trt_gemm_tiled on raw device addresses (ints).  Raises TrtError."""
     _check(lib().trt_gemm_tiled(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
-                                out_dtype, _epi(bias, relu, residual, ldr), _tile(tile),
-                                stream or None))
+                                out_dtype, _epi(bias, relu, residual, ldr, scale),
+                                _tile(tile), stream or None))
 
 
 def validate_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
-                 bias=0, relu=False, residual=0, ldr=0, tile=None) -> int:
+                 bias=0, relu=False, residual=0, ldr=0, scale=0, tile=None) -> int:
     """trt_validate: the status a call would return, without any GPU work."""
     return lib().trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
-                              out_dtype, _epi(bias, relu, residual, ldr), _tile(tile))
+                              out_dtype, _epi(bias, relu, residual, ldr, scale), _tile(tile))
 
 
 def tiles():
@@ -196,7 +198,7 @@ _DT = {}
 def _dtype_code(t):
     torch = _torch()
     if not _DT:
-        _DT.update({torch.float16: F16, torch.bfloat16: BF16})
+        _DT.update({torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32})
     if t.dtype not in _DT:
         raise TrtError(ERR_DTYPE, f"unsupported dtype {t.dtype}")
     return _DT[t.dtype]
@@ -216,16 +218,18 @@ def _ld(t, name):
     return max(t.stride(0), 1)
 
 
-def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, out=None,
-         tile=None, M=None, N=None, K=None):
-    """C = relu(A.B + bias) + residual on the GPU, in one kernel.
+def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, row_scale=None,
+         out=None, out_dtype=None, tile=None, M=None, N=None, K=None):
+    """C = relu((A.B) * row_scale[:, None] + bias) + residual on the GPU, in one kernel.
 
     A is [M, K] (opA="N") or its transpose stored as [K, M] (opA="T"); B is
     [K, N] (opB="N") or stored as [N, K] (opB="T").  Tensors may be
     row-padded views (unit inner stride, any row stride).  bias is [N],
-    residual [M, N], both of the output dtype.  out, if given, is written;
-    otherwise a new [M, N] tensor is returned.  Runs on torch's current
-    stream; no synchronisation.
+    row_scale [M], residual [M, N], all of the output dtype: out's dtype if
+    out is given, else out_dtype (a torch dtype: float16, bfloat16 or
+    float32), else A's dtype.  out, if given, is written; otherwise a new
+    [M, N] tensor is returned.  Runs on torch's current stream; no
+    synchronisation.
     """
     torch = _torch()
     opa = OP_T if opA in ("T", OP_T, True) else OP_N
@@ -241,7 +245,7 @@ def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, out=No
     if _dtype_code(B) != dt:
         raise TrtError(ERR_DTYPE, "A and B dtypes differ")
     if out is None:
-        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
     ldr = 0
     if residual is not None:
         ldr = _ld(residual, "residual")
@@ -249,6 +253,7 @@ def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, out=No
              out.data_ptr(), _ld(out, "out"), dt, _dtype_code(out),
              bias=bias.data_ptr() if bias is not None else 0, relu=relu,
              residual=residual.data_ptr() if residual is not None else 0, ldr=ldr,
+             scale=row_scale.data_ptr() if row_scale is not None else 0,
              tile=tile, stream=_stream(A.device))
     return out
 

@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["trt.hip", "kern_tiny.hip", "kern_64.hip", "kern_128.hip", "kern_256.hip",
-           "kern_256f.hip", "kern_dma256.hip", "kern_skinny.hip"]
+           "kern_256f.hip", "kern_dma256_f16_ak.hip", "kern_dma256_f16_am.hip",
+           "kern_dma256_bf16_ak.hip", "kern_dma256_bf16_am.hip", "kern_skinny.hip"]
 LIB = os.path.join(HERE, "libtrt.so")
 ARCH = "gfx950"
 
@@ -21,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-shared",
     "-Wall",

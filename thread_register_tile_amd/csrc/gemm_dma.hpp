@@ -173,26 +173,31 @@ struct FragReader {
 // written in two passes of half its fragment rows: each wave stores its raw
 // fp32 accumulators of the pass into an LDS staging array (rows padded by 16
 // bytes so the 32 rows a fragment store touches fall on distinct banks);
-// then every thread takes four consecutive columns of successive rows, adds
-// the bias it read once for those columns, applies ReLU, adds the residual,
-// rounds once to the output type and stores 8 bytes -- a wave covers 512
-// contiguous bytes of a row ("My Triton From Scratch, Part 16: Register
-// Tiles", sections "Masks and stores" and "Broadcasts cannot be treated as
-// full register tiles": per-element masks, bias held once per owned column).
+// then every thread takes four consecutive columns of successive rows,
+// multiplies by the row scale, adds the bias it read once for those columns,
+// applies ReLU, adds the residual, rounds once to the output type OT and
+// stores one vector -- a wave covers 64 consecutive runs of a row ("My
+// Triton From Scratch, Part 16: Register Tiles", sections "Masks and stores"
+// and "Broadcasts cannot be treated as full register tiles": per-element
+// masks, bias held once per owned column).
 //
 // MODE, chosen once per tile: EPI_FAST when the whole tile is inside C and
-// 8-byte vectors are allowed (EPI_FAST_RES with a residual), else
-// EPI_MASKED.  The fast modes have no branch in the store phase: the
-// residual rows of a pass are loaded before its staging writes, and the LDS
+// vector runs are allowed (EPI_FAST_RES with a residual; either with
+// EPI_SCALED added when there is a row scale), else EPI_MASKED.
+// The fast modes have no branch in the store phase: the residual rows (and
+// row scales) of a pass are loaded before its staging writes, and the LDS
 // reads of a batch of rows are all issued before the first of their stores.
 // EPI_MASKED masks and stores every element on its own.
-enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2 };
+enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4 };
 
-template <class TL, int DT, int MODE>
+template <class TL, int OT, int MODE_>
 __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
                                                 const f32x16 (&acc)[TL::FM][TL::FN],
                                                 float* stage, int m0, int n0, int t,
                                                 const float (&bias)[4]) {
+  using O = Out<OT>;
+  constexpr int MODE = MODE_ & 3;                      // EPI_MASKED / EPI_FAST / EPI_FAST_RES
+  constexpr bool SCALED = (MODE_ & EPI_SCALED) != 0;   // fast modes: row scale present
   constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
   constexpr int PITCH = BN + 4;                       // floats per staged row
   constexpr int HALF_ROWS = TL::BM / 2;               // rows per pass
@@ -208,21 +213,33 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   const int col = COLS_PER_T * (t % T_PER_ROW);       // this thread's 4 columns
   const int n = n0 + col;
   const bool relu = p.relu != 0;
+  const bool scaled = p.scale != nullptr;
   // staged row -> tile row: the wave row block, then the pass's half of it
   auto tile_row = [&](int pass, int prow) {
     return (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
            prow % (HALF_ROWS / TL::WM);
   };
+  // Residuals and row scales travel in a ring of RING rows per thread: 64
+  // registers of residual (a whole pass for 16-bit outputs, half a pass for
+  // binary32).  Row `it` is loaded when its slot frees, i.e. right after row
+  // it - RING was used, so each load has at least one batch of stores ahead
+  // of it; the first RING rows are loaded before the staging writes.
+  constexpr int RING = O::BYTES == 2 ? ITERS : ITERS / 2;
+  static_assert(RING % BATCH == 0 && ITERS % RING == 0, "whole batches per ring");
+  auto row_of = [&](int pass, int it) { return m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW); };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    u32x2 rr[MODE == EPI_FAST_RES ? ITERS : 1];
-    if constexpr (MODE == EPI_FAST_RES) {
-#pragma unroll
-      for (int it = 0; it < ITERS; ++it) {
-        const int m = m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW);
-        rr[it] = *reinterpret_cast<const u32x2*>(p.R + (int64_t)m * p.ldr + n);
+    typename O::Vec rr[MODE == EPI_FAST_RES ? RING : 1];
+    float sc[SCALED ? RING : 1];
+    auto fetch = [&](int it) {
+      if constexpr (MODE != EPI_MASKED) {
+        const int m = row_of(pass, it);
+        if constexpr (MODE == EPI_FAST_RES) rr[it % RING] = O::ld4(p.R, (int64_t)m * p.ldr + n);
+        if constexpr (SCALED) sc[it % RING] = O::ld(p.scale, m);
       }
-    }
+    };
+#pragma unroll
+    for (int it = 0; it < RING; ++it) fetch(it);
     // accumulators of fragment rows fm = 2*pass, 2*pass+1 -> staged rows
     // prow = 64*wr + 32*(fm - 2*pass) + lane%32
 #pragma unroll
@@ -251,20 +268,21 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
           const int it = b0 + i;
-          const int m = m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW);
-          float y[4] = {v[i][0] + bias[0], v[i][1] + bias[1], v[i][2] + bias[2],
-                        v[i][3] + bias[3]};
+          float y[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = (relu && !(y[e] > 0.f)) ? 0.f : y[e];
-          if constexpr (MODE == EPI_FAST_RES) {
-            y[0] += to_f32<DT>(rr[it][0] & 0xFFFFu); y[1] += to_f32<DT>(rr[it][0] >> 16);
-            y[2] += to_f32<DT>(rr[it][1] & 0xFFFFu); y[3] += to_f32<DT>(rr[it][1] >> 16);
+          for (int e = 0; e < 4; ++e) {
+            // an absent bias is -0, an exact identity (-0 included), so no
+            // select is needed
+            y[e] = (SCALED ? v[i][e] * sc[it % RING] : v[i][e]) + bias[e];
+            y[e] = (relu && !(y[e] > 0.f)) ? 0.f : y[e];
+            if constexpr (MODE == EPI_FAST_RES) y[e] += O::elem(rr[it % RING], e);
           }
-          u32x2 o;
-          o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
-          o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
-          *reinterpret_cast<u32x2*>(p.C + (int64_t)m * p.ldc + n) = o;
+          O::st4(p.C, (int64_t)row_of(pass, it) * p.ldc + n, O::pack(y));
         }
+        // the batch's slots are free: fetch the rows RING further on
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+          if (b0 + i + RING < ITERS) fetch(b0 + i + RING);
       }
     } else {
       const bool vec = p.epi_vec && n + 4 <= p.N;
@@ -274,27 +292,31 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
         const int m = m0 + tile_row(pass, prow);
         if (m >= p.M) continue;
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow * PITCH + col);
-        float y[4] = {a4[0] + bias[0], a4[1] + bias[1], a4[2] + bias[2], a4[3] + bias[3]};
+        float y[4] = {a4[0], a4[1], a4[2], a4[3]};
+        if (scaled) {
+          const float s = O::ld(p.scale, m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] *= s;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] += bias[e];
         if (relu) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
         }
         if (p.R) {
-          const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
+          const int64_t r0 = (int64_t)m * p.ldr + n;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
+            if (n + e < p.N) y[e] += O::ld(p.R, r0 + e);
         }
-        uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
+        const int64_t c0 = (int64_t)m * p.ldc + n;
         if (vec) {
-          u32x2 o;
-          o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
-          o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
-          *reinterpret_cast<u32x2*>(cp) = o;
+          O::st4(p.C, c0, O::pack(y));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+            if (n + e < p.N) O::st(p.C, c0 + e, y[e]);
         }
       }
     }
@@ -302,29 +324,36 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   }
 }
 
-template <class TL, int DT>
+template <class TL, int OT>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&acc)[TL::FM][TL::FN],
                                              float* stage, int m0, int n0, int t) {
+  using O = Out<OT>;
   const int n = n0 + 4 * (t % (TL::BN / 4));          // this thread's 4 columns
   const bool vec = p.epi_vec && n + 4 <= p.N;
-  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  // -0 when there is no bias: x + (-0) == x for every x, -0 included
+  float bias[4] = {-0.f, -0.f, -0.f, -0.f};
   if (p.bias) {
     if (vec) {
-      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-      bias[0] = to_f32<DT>(bb[0] & 0xFFFFu); bias[1] = to_f32<DT>(bb[0] >> 16);
-      bias[2] = to_f32<DT>(bb[1] & 0xFFFFu); bias[3] = to_f32<DT>(bb[1] >> 16);
+      const auto bb = O::ld4(p.bias, n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bias[e] = O::elem(bb, e);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (n + e < p.N) bias[e] = to_f32<DT>(p.bias[n + e]);
+        if (n + e < p.N) bias[e] = O::ld(p.bias, n + e);
     }
   }
   if (!(p.epi_vec && n0 + TL::BN <= p.N && m0 + TL::BM <= p.M))
-    epilogue_passes<TL, DT, EPI_MASKED>(p, acc, stage, m0, n0, t, bias);
+    epilogue_passes<TL, OT, EPI_MASKED>(p, acc, stage, m0, n0, t, bias);
+  else if (p.scale)
+    if (p.R)
+      epilogue_passes<TL, OT, EPI_FAST_RES | EPI_SCALED>(p, acc, stage, m0, n0, t, bias);
+    else
+      epilogue_passes<TL, OT, EPI_FAST | EPI_SCALED>(p, acc, stage, m0, n0, t, bias);
   else if (p.R)
-    epilogue_passes<TL, DT, EPI_FAST_RES>(p, acc, stage, m0, n0, t, bias);
+    epilogue_passes<TL, OT, EPI_FAST_RES>(p, acc, stage, m0, n0, t, bias);
   else
-    epilogue_passes<TL, DT, EPI_FAST>(p, acc, stage, m0, n0, t, bias);
+    epilogue_passes<TL, OT, EPI_FAST>(p, acc, stage, m0, n0, t, bias);
 }
 
 template <class TL, int DT, bool A_KC, bool B_KC>
@@ -430,7 +459,9 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
   __syncthreads();
 
-  epilogue_lds<TL, DT>(p, acc, reinterpret_cast<float*>(lds_raw), m0, n0, t);
+  with_out_type(p.out_dt, [&]<int OT>() {
+    epilogue_lds<TL, OT>(p, acc, reinterpret_cast<float*>(lds_raw), m0, n0, t);
+  });
 }
 
 }  // namespace trt

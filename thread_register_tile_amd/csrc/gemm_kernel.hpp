@@ -37,7 +37,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum : int { DT_F16 = 1, DT_BF16 = 2 };
+// Element types: inputs are DT_F16 or DT_BF16; the output (and the epilogue
+// operands, stored in the output type) may also be DT_F32.
+enum : int { DT_F16 = 1, DT_BF16 = 2, DT_F32 = 3 };
 
 // ---- element conversions ----------------------------------------------------
 
@@ -92,18 +94,77 @@ __device__ __forceinline__ f32x16 mfma32<DT_BF16>(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ---- output elements ---------------------------------------------------------------
+// C, bias, residual and row scale hold elements of the output type OT.  Out
+// reads and writes one element, or a run of four consecutive ones as one
+// vector (8 bytes for 16-bit types, 16 for binary32) when the caller has
+// checked that the run is in range and aligned.
+template <int OT>
+struct Out {
+  using Vec = u32x2;
+  static constexpr int BYTES = 2;
+  __device__ static float ld(const void* p, int64_t i) {
+    return to_f32<OT>(static_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ static void st(void* p, int64_t i, float y) {
+    static_cast<uint16_t*>(p)[i] = (uint16_t)from_f32<OT>(y);
+  }
+  __device__ static Vec ld4(const void* p, int64_t i) {
+    return *reinterpret_cast<const Vec*>(static_cast<const uint16_t*>(p) + i);
+  }
+  __device__ static void st4(void* p, int64_t i, Vec v) {
+    *reinterpret_cast<Vec*>(static_cast<uint16_t*>(p) + i) = v;
+  }
+  __device__ static float elem(Vec v, int e) {
+    return to_f32<OT>((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
+  }
+  __device__ static Vec pack(const float (&y)[4]) {
+    return Vec{from_f32<OT>(y[0]) | (from_f32<OT>(y[1]) << 16),
+               from_f32<OT>(y[2]) | (from_f32<OT>(y[3]) << 16)};
+  }
+};
+template <>
+struct Out<DT_F32> {
+  using Vec = f32x4;
+  static constexpr int BYTES = 4;
+  __device__ static float ld(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  __device__ static void st(void* p, int64_t i, float y) { static_cast<float*>(p)[i] = y; }
+  __device__ static Vec ld4(const void* p, int64_t i) {
+    return *reinterpret_cast<const Vec*>(static_cast<const float*>(p) + i);
+  }
+  __device__ static void st4(void* p, int64_t i, Vec v) {
+    *reinterpret_cast<Vec*>(static_cast<float*>(p) + i) = v;
+  }
+  __device__ static float elem(Vec v, int e) { return v[e]; }
+  __device__ static Vec pack(const float (&y)[4]) { return Vec{y[0], y[1], y[2], y[3]}; }
+};
+
+// Calls f.template operator()<OT>() for the run-time output type (uniform
+// over the grid, so the branch costs one scalar compare).
+template <class F>
+__device__ __forceinline__ void with_out_type(int out_dt, F&& f) {
+  if (out_dt == DT_F16)
+    f.template operator()<DT_F16>();
+  else if (out_dt == DT_BF16)
+    f.template operator()<DT_BF16>();
+  else
+    f.template operator()<DT_F32>();
+}
+
 // ---- kernel arguments --------------------------------------------------------------
 
 struct GemmArgs {
   const uint16_t* A;
   const uint16_t* B;
-  uint16_t* C;
-  const uint16_t* bias;  // [N] or null
-  const uint16_t* R;     // residual, R(m,n) = R[m*ldr + n], or null
+  void* C;               // output, elements of out_dt
+  const void* bias;      // [N] of out_dt, or null
+  const void* R;         // residual of out_dt, R(m,n) = R[m*ldr + n], or null
+  const void* scale;     // row scale [M] of out_dt, or null
   int64_t lda, ldb, ldc, ldr;
   int32_t M, N, K;
   int32_t relu;
-  int32_t epi_vec;       // 8-byte vector epilogue allowed (alignment holds)
+  int32_t out_dt;        // DT_F16, DT_BF16 or DT_F32
+  int32_t epi_vec;       // 4-element vector epilogue allowed (alignment holds)
   int32_t tiles_m, tiles_n;
   int64_t a_bytes, b_bytes;  // byte extents of the A and B operands
 };
@@ -237,17 +298,61 @@ using Operand = typename std::conditional<KC, KContigOperand<TL, R, VEC>,
                                           MNContigOperand<TL, R, VEC>>::type;
 
 // ---- fused epilogue --------------------------------------------------------------
+// The output type of the generic kernels' epilogue is read at run time: one
+// copy of the (fully unrolled) epilogue serves all three output types, each
+// element access branching on the uniform type code.
+struct OutAny {
+  int dt;
+  __device__ __forceinline__ float cvt16(uint32_t h) const {
+    return dt == DT_BF16 ? to_f32<DT_BF16>(h) : to_f32<DT_F16>(h);
+  }
+  __device__ __forceinline__ uint32_t rnd16(float y) const {
+    return dt == DT_BF16 ? from_f32<DT_BF16>(y) : from_f32<DT_F16>(y);
+  }
+  __device__ __forceinline__ float ld(const void* p, int64_t i) const {
+    if (dt == DT_F32) return static_cast<const float*>(p)[i];
+    return cvt16(static_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ __forceinline__ void st(void* p, int64_t i, float y) const {
+    if (dt == DT_F32)
+      static_cast<float*>(p)[i] = y;
+    else
+      static_cast<uint16_t*>(p)[i] = (uint16_t)rnd16(y);
+  }
+  // four consecutive elements from i (aligned, in range)
+  __device__ __forceinline__ void ld4(const void* p, int64_t i, float (&v)[4]) const {
+    if (dt == DT_F32) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+      v[0] = w[0]; v[1] = w[1]; v[2] = w[2]; v[3] = w[3];
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+      v[0] = cvt16(w[0] & 0xFFFFu); v[1] = cvt16(w[0] >> 16);
+      v[2] = cvt16(w[1] & 0xFFFFu); v[3] = cvt16(w[1] >> 16);
+    }
+  }
+  __device__ __forceinline__ void st4(void* p, int64_t i, const float (&y)[4]) const {
+    if (dt == DT_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = f32x4{y[0], y[1], y[2], y[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p) + i) =
+          u32x2{rnd16(y[0]) | (rnd16(y[1]) << 16), rnd16(y[2]) | (rnd16(y[3]) << 16)};
+    }
+  }
+};
+
 // Per accumulator register ("My Triton From Scratch, Part 16: Register Tiles",
 // sections "Pointer tiles" and "Masks and stores"): the register's (row, col)
 // comes from the tile's ownership map, the bias is read once per owned column
-// (it is broadcast along m), y = relu(acc + bias) + R is evaluated in fp32,
-// rounded once to the output type, and stored under its own mask.  A lane
-// owns four consecutive columns of a row per fragment, stored as one 8-byte
-// vector when the whole run is in range and the buffers are aligned.
-template <class TL, int DT, class AccT>
+// (it is broadcast along m) and the row scale once per owned row (broadcast
+// along n), y = relu(acc * scale + bias) + R is evaluated in fp32, rounded
+// once to the output type, and stored under its own mask.  A lane owns four
+// consecutive columns of a row per fragment, stored as one vector when the
+// whole run is in range and the buffers are aligned.
+template <class TL, class AccT>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& p,
                                                const AccT (&acc)[TL::FM][TL::FN], int m0,
                                                int n0, int lane, int wave) {
+  const OutAny O{p.out_dt};
 #pragma unroll
   for (int i = 0; i < TL::FM; ++i) {
 #pragma unroll
@@ -261,15 +366,21 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p,
         float y[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                       acc[i][j][4 * q + 3]};
         const bool vec = p.epi_vec && (n + 4 <= p.N);
+        if (p.scale) {
+          const float s = O.ld(p.scale, m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] *= s;
+        }
         if (p.bias) {
           if (vec) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-            y[0] += to_f32<DT>(bb[0] & 0xFFFFu); y[1] += to_f32<DT>(bb[0] >> 16);
-            y[2] += to_f32<DT>(bb[1] & 0xFFFFu); y[3] += to_f32<DT>(bb[1] >> 16);
+            float bb[4];
+            O.ld4(p.bias, n, bb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] += bb[e];
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) y[e] += to_f32<DT>(p.bias[n + e]);
+              if (n + e < p.N) y[e] += O.ld(p.bias, n + e);
           }
         }
         if (p.relu) {
@@ -277,27 +388,25 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p,
           for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
         }
         if (p.R) {
-          const uint16_t* rp = p.R + (int64_t)m * p.ldr + n;
+          const int64_t r0 = (int64_t)m * p.ldr + n;
           if (vec) {
-            const u32x2 rr = *reinterpret_cast<const u32x2*>(rp);
-            y[0] += to_f32<DT>(rr[0] & 0xFFFFu); y[1] += to_f32<DT>(rr[0] >> 16);
-            y[2] += to_f32<DT>(rr[1] & 0xFFFFu); y[3] += to_f32<DT>(rr[1] >> 16);
+            float rr[4];
+            O.ld4(p.R, r0, rr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] += rr[e];
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) y[e] += to_f32<DT>(rp[e]);
+              if (n + e < p.N) y[e] += O.ld(p.R, r0 + e);
           }
         }
-        uint16_t* cp = p.C + (int64_t)m * p.ldc + n;
+        const int64_t c0 = (int64_t)m * p.ldc + n;
         if (vec) {
-          u32x2 o;
-          o[0] = from_f32<DT>(y[0]) | (from_f32<DT>(y[1]) << 16);
-          o[1] = from_f32<DT>(y[2]) | (from_f32<DT>(y[3]) << 16);
-          *reinterpret_cast<u32x2*>(cp) = o;
+          O.st4(p.C, c0, y);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) cp[e] = (uint16_t)from_f32<DT>(y[e]);
+            if (n + e < p.N) O.st(p.C, c0 + e, y[e]);
         }
       }
     }
@@ -380,7 +489,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  epilogue_store<TL, DT>(p, acc, m0, n0, lane, wave);
+  epilogue_store<TL>(p, acc, m0, n0, lane, wave);
 }
 
 }  // namespace trt

@@ -154,14 +154,20 @@ __global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmAr
   }
   if (m >= p.M) return;
   const int nc = n0 + nl;
+  with_out_type(p.out_dt, [&]<int OT>() {
+    using O = Out<OT>;
+    const float s = p.scale ? O::ld(p.scale, m) : 1.f;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    if (nc + e >= p.N) continue;
-    if (p.bias) y[e] += to_f32<DT>(p.bias[nc + e]);
-    if (p.relu) y[e] = y[e] > 0.f ? y[e] : 0.f;
-    if (p.R) y[e] += to_f32<DT>(p.R[(int64_t)m * p.ldr + nc + e]);
-    p.C[(int64_t)m * p.ldc + nc + e] = (uint16_t)from_f32<DT>(y[e]);
-  }
+    for (int e = 0; e < 2; ++e) {
+      if (nc + e >= p.N) continue;
+      float v = y[e];
+      if (p.scale) v *= s;
+      if (p.bias) v += O::ld(p.bias, nc + e);
+      if (p.relu) v = v > 0.f ? v : 0.f;
+      if (p.R) v += O::ld(p.R, (int64_t)m * p.ldr + nc + e);
+      O::st(p.C, (int64_t)m * p.ldc + nc + e, v);
+    }
+  });
 }
 
 }  // namespace trt

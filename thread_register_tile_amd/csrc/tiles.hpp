@@ -19,9 +19,22 @@ using Tile256F = Tile<256, 256, 32, 2, 2, 16>; // generic kernel on the pipeline
 template <class TL>
 void launch_generic(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s);
 
-// Launch the pipelined direct-to-LDS kernel of tile TL.
+// Launch the pipelined direct-to-LDS kernel of tile TL for input type DT and
+// A storage (A_KC: k-contiguous), defined per (DT, A storage) in the
+// kern_dma256_*.hip translation units.
+template <class TL, int DT, bool A_KC>
+void launch_pipelined_a(GemmArgs a, bool b_kc, hipStream_t s);
+
 template <class TL>
-void launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s);
+inline void launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s) {
+  a.tiles_m = (a.M + TL::BM - 1) / TL::BM;
+  a.tiles_n = (a.N + TL::BN - 1) / TL::BN;
+  const bool akc = opA == 0, bkc = opB == 1;
+  if (dt == DT_F16)
+    akc ? launch_pipelined_a<TL, DT_F16, true>(a, bkc, s) : launch_pipelined_a<TL, DT_F16, false>(a, bkc, s);
+  else
+    akc ? launch_pipelined_a<TL, DT_BF16, true>(a, bkc, s) : launch_pipelined_a<TL, DT_BF16, false>(a, bkc, s);
+}
 
 // Launch the HBM-streaming kernel for M <= 16 (kern_skinny.hip).
 void launch_skinny(GemmArgs a, int dt, hipStream_t s);

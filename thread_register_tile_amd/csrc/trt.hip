@@ -374,9 +374,10 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(A);
   a.B = static_cast<const uint16_t*>(B);
-  a.C = static_cast<uint16_t*>(C);
-  a.bias = epi ? static_cast<const uint16_t*>(epi->bias) : nullptr;
-  a.R = epi ? static_cast<const uint16_t*>(epi->residual) : nullptr;
+  a.C = C;
+  a.bias = epi ? epi->bias : nullptr;
+  a.R = epi ? epi->residual : nullptr;
+  a.scale = epi ? epi->row_scale : nullptr;
   a.lda = lda;
   a.ldb = ldb;
   a.ldc = ldc;
@@ -385,6 +386,7 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   a.N = (int32_t)N;
   a.K = (int32_t)K;
   a.relu = (epi && epi->relu) ? 1 : 0;
+  a.out_dt = out_dtype;
   int64_t sa = 0, sb = 0;
   trt::span_bytes(opA ? K : M, opA ? M : K, lda, sa);
   trt::span_bytes(opB ? N : K, opB ? K : N, ldb, sb);
@@ -392,9 +394,11 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   a.b_bytes = sb;
   // 16-byte operand vectors need 16-byte aligned bases and rows.
   const bool vec = aligned(A, 16) && aligned(B, 16) && lda % 8 == 0 && ldb % 8 == 0;
-  // 8-byte epilogue vectors need 8-byte aligned C, bias, residual rows.
-  a.epi_vec = aligned(C, 8) && ldc % 4 == 0 && (!a.bias || aligned(a.bias, 8)) &&
-              (!a.R || (aligned(a.R, 8) && a.ldr % 4 == 0));
+  // Epilogue vectors of 4 output elements (8 or 16 bytes) need aligned C,
+  // bias and residual rows.
+  const uintptr_t va = 4 * (uintptr_t)trt::elem_bytes(out_dtype);
+  a.epi_vec = aligned(C, va) && ldc % 4 == 0 && (!a.bias || aligned(a.bias, va)) &&
+              (!a.R || (aligned(a.R, va) && a.ldr % 4 == 0));
   e->launch(a, in_dtype, opA, opB, vec, static_cast<hipStream_t>(stream));
   return check_launch("gemm launch");
 }

@@ -24,12 +24,16 @@ struct Extent {
   uintptr_t lo, hi;  // [lo, hi) in bytes; lo == hi for an absent buffer
 };
 
+// Bytes of one element of a dtype: 2 for the 16-bit types, 4 for binary32.
+inline int64_t elem_bytes(int32_t dtype) { return dtype == TRT_F32 ? 4 : 2; }
+
 // Bytes spanned by a rows x cols matrix with leading dimension ld (elements
-// of 2 bytes), or false on overflow.
-inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t& bytes) {
+// of `esize` bytes), or false on overflow.
+inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t& bytes,
+                       int64_t esize = 2) {
   if (rows <= 0 || cols <= 0) { bytes = 0; return true; }
   const __int128 last = (__int128)(rows - 1) * ld + cols;  // elements
-  const __int128 b = last * 2;
+  const __int128 b = last * esize;
   if (b > ((__int128)1 << 62)) return false;
   bytes = (int64_t)b;
   return true;
@@ -65,12 +69,13 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
     msg = "in_dtype must be TRT_F16 or TRT_BF16";
     return TRT_ERR_DTYPE;
   }
-  if (out_dtype != in_dtype) {
-    msg = "out_dtype must equal in_dtype";
+  if (out_dtype != TRT_F16 && out_dtype != TRT_BF16 && out_dtype != TRT_F32) {
+    msg = "out_dtype must be TRT_F16, TRT_BF16 or TRT_F32";
     return TRT_ERR_DTYPE;
   }
   const bool has_bias = epi && epi->bias;
   const bool has_res = epi && epi->residual;
+  const bool has_scale = epi && epi->row_scale;
   if (lda < 1 || ldb < 1 || (has_res && epi->ldr < 1)) {
     msg = "input leading dimensions must be >= 1";
     return TRT_ERR_STRIDE;
@@ -83,18 +88,27 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
     msg = "A, B and C must be non-null";
     return TRT_ERR_NULL;
   }
-  const void* ptrs[5] = {A, B, C, has_bias ? epi->bias : nullptr,
-                         has_res ? epi->residual : nullptr};
-  for (const void* q : ptrs)
-    if (q && (reinterpret_cast<uintptr_t>(q) & 1u)) {
-      msg = "pointers must be 2-byte aligned";
+  // every pointer aligned to its element: 2 bytes for A and B, the output
+  // element for C and the epilogue operands
+  const int64_t osz = elem_bytes(out_dtype);
+  const void* in_ptrs[2] = {A, B};
+  const void* out_ptrs[4] = {C, has_bias ? epi->bias : nullptr, has_res ? epi->residual : nullptr,
+                             has_scale ? epi->row_scale : nullptr};
+  for (const void* q : in_ptrs)
+    if (reinterpret_cast<uintptr_t>(q) & 1u) {
+      msg = "A and B must be 2-byte aligned";
+      return TRT_ERR_ALIGN;
+    }
+  for (const void* q : out_ptrs)
+    if (q && (reinterpret_cast<uintptr_t>(q) & (uintptr_t)(osz - 1))) {
+      msg = "C, bias, residual and row_scale must be aligned to the output element";
       return TRT_ERR_ALIGN;
     }
   int64_t sa, sb, sc, sr = 0;
   const bool ok = span_bytes(opA ? K : M, opA ? M : K, lda, sa) &&
                   span_bytes(opB ? N : K, opB ? K : N, ldb, sb) &&
-                  span_bytes(M, N, ldc, sc) &&
-                  (!has_res || span_bytes(M, N, epi->ldr, sr));
+                  span_bytes(M, N, ldc, sc, osz) &&
+                  (!has_res || span_bytes(M, N, epi->ldr, sr, osz));
   if (!ok) {
     msg = "operand extent overflows";
     return TRT_ERR_SIZE;
@@ -104,10 +118,11 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
     return Extent{lo, q ? lo + (uintptr_t)bytes : lo};
   };
   const Extent ec = ext(C, sc);
-  const Extent ins[4] = {ext(A, sa), ext(B, sb), ext(has_bias ? epi->bias : nullptr, 2 * N),
-                         ext(has_res ? epi->residual : nullptr, sr)};
-  static const char* names[4] = {"A", "B", "bias", "residual"};
-  for (int i = 0; i < 4; ++i)
+  const Extent ins[5] = {ext(A, sa), ext(B, sb), ext(has_bias ? epi->bias : nullptr, osz * N),
+                         ext(has_res ? epi->residual : nullptr, sr),
+                         ext(has_scale ? epi->row_scale : nullptr, osz * M)};
+  static const char* names[5] = {"A", "B", "bias", "residual", "row_scale"};
+  for (int i = 0; i < 5; ++i)
     if (overlaps(ec, ins[i])) {
       msg = std::string("C overlaps ") + names[i] + " (an in-place output is not provably safe)";
       return TRT_ERR_OVERLAP;

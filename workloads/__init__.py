@@ -6,12 +6,14 @@ draws their raw 16-bit operand buffers from a seeded generator.  Both the
 oracle and the HIP path are fed these same bytes.
 
 Recipe (one generator per tensor): numpy PCG64 seeded with
-[config_seed, tensor_id]; tensor ids A=0, B=1, bias=2, residual=3.  Values are
-drawn in float64 in *storage* order (A^T order when A is stored transposed),
-rounded to the 16-bit type (float16: numpy's float64->float16 conversion;
-bfloat16: float64->float32, then round-to-nearest-even on the float32 bits)
-and written into a padded buffer whose leading-dimension padding holds NaN,
-so that any read of the padding poisons the result.
+[config_seed, tensor_id]; tensor ids A=0, B=1, bias=2, residual=3, row
+scale=4.  Values are drawn in float64 in *storage* order (A^T order when A is
+stored transposed), rounded to the element type (float16: numpy's
+float64->float16 conversion; bfloat16: float64->float32, then
+round-to-nearest-even on the float32 bits; float32: numpy's float64->float32
+conversion) and written into a padded buffer whose leading-dimension padding
+holds NaN, so that any read of the padding poisons the result.  A and B use
+the input type; bias, residual and row scale use the output type.
 """
 from dataclasses import dataclass, field, replace
 from typing import Optional
@@ -20,9 +22,11 @@ import numpy as np
 
 F16 = 1
 BF16 = 2
-DTYPE_NAMES = {F16: "f16", BF16: "bf16"}
+F32 = 3                 # output / epilogue-operand type only
+DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32"}
+ELEM_BYTES = {F16: 2, BF16: 2, F32: 4}
 
-TENSOR_A, TENSOR_B, TENSOR_BIAS, TENSOR_R = 0, 1, 2, 3
+TENSOR_A, TENSOR_B, TENSOR_BIAS, TENSOR_R, TENSOR_SCALE = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -36,7 +40,9 @@ class Workload:
     lda: Optional[int] = None
     ldb: Optional[int] = None
     ldc: Optional[int] = None
-    dtype: int = F16
+    dtype: int = F16       # input type of A and B
+    out_dtype: Optional[int] = None   # output type (C, bias, residual, row scale); None: dtype
+    row_scale: bool = False
     bias: bool = False
     relu: bool = False
     residual: bool = False
@@ -78,16 +84,23 @@ class Workload:
         return self.N
 
     @property
+    def odt(self):
+        return self.out_dtype if self.out_dtype is not None else self.dtype
+
+    @property
     def flops(self):
         return 2 * self.M * self.N * self.K
 
     @property
     def algorithmic_bytes(self):
-        b = 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
+        o = ELEM_BYTES[self.odt]
+        b = 2 * (self.M * self.K + self.K * self.N) + o * self.M * self.N
         if self.bias:
-            b += 2 * self.N
+            b += o * self.N
         if self.residual:
-            b += 2 * self.M * self.N
+            b += o * self.M * self.N
+        if self.row_scale:
+            b += o * self.M
         return b
 
 
@@ -103,7 +116,13 @@ RAGGED = Workload("ragged", 4000, 3072, 5000, opA=1, lda=5064, ldb=3136,
 SKINNY = Workload("skinny", 16, 16384, 16384, dtype=F16, dist="normal",
                   scale=128.0, seed=5)
 
-CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY)}
+# A further epilogue variant: the epilogue shape with bf16 inputs, a binary32
+# output and binary32 epilogue operands, and a row scale ("Named layouts",
+# section "Contract": the axes-"m" broadcast operand).
+ROWSCALE = Workload("rowscale", 8192, 8192, 4096, dtype=BF16, out_dtype=F32, row_scale=True,
+                    bias=True, relu=True, residual=True, dist="uniform", scale=1.0, seed=6)
+
+CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY, ROWSCALE)}
 
 
 def shrink(w: Workload, M=None, N=None, K=None, **kw) -> Workload:
@@ -132,12 +151,15 @@ def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
 
 
 def to_bits(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Raw bits of x rounded to dtype: uint16, or uint32 for F32."""
     if dtype == F16:
         return np.ascontiguousarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float64).astype(np.float32).view(np.uint32)
     return f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32))
 
 
-NAN_BITS = {F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0)}
+NAN_BITS = {F16: np.uint16(0x7E00), BF16: np.uint16(0x7FC0), F32: np.uint32(0x7FC00000)}
 
 
 def _draw(w: Workload, tensor_id: int, rows: int, cols: int) -> np.ndarray:
@@ -149,31 +171,36 @@ def _draw(w: Workload, tensor_id: int, rows: int, cols: int) -> np.ndarray:
         x = rng.standard_normal(size=shape) / w.scale
     elif w.dist == "ternary":
         # exact-arithmetic mode: operands in {-1, 0, 1}, epilogue terms in {-2..2}
-        lim = 2 if tensor_id in (TENSOR_BIAS, TENSOR_R) else 1
+        lim = 2 if tensor_id in (TENSOR_BIAS, TENSOR_R, TENSOR_SCALE) else 1
         x = rng.integers(-lim, lim + 1, size=shape).astype(np.float64)
     else:
         raise ValueError(w.dist)
     return x
 
 
-def _padded(w: Workload, tensor_id: int, rows: int, cols: int, ld: int) -> np.ndarray:
-    bits = to_bits(_draw(w, tensor_id, rows, cols), w.dtype)
-    buf = np.full((rows, ld), NAN_BITS[w.dtype], dtype=np.uint16)
+def _padded(w: Workload, tensor_id: int, rows: int, cols: int, ld: int, dtype=None) -> np.ndarray:
+    dtype = dtype or w.dtype
+    bits = to_bits(_draw(w, tensor_id, rows, cols), dtype)
+    buf = np.full((rows, ld), NAN_BITS[dtype], dtype=bits.dtype)
     buf[:, :cols] = bits
     return buf.reshape(-1)
 
 
 def make_inputs(w: Workload) -> dict:
-    """Raw host buffers (flat uint16) for a workload: A, B and, if enabled,
-    bias [N] and residual [M, N] (leading dimension N)."""
+    """Raw host buffers for a workload: A, B (flat uint16 of the input type)
+    and, if enabled, bias [N], residual [M, N] (leading dimension N) and row
+    scale [M] (flat, of the output type: uint16, or uint32 for F32)."""
     out = {
         "A": _padded(w, TENSOR_A, w.a_rows, w.a_cols, w.lda_),
         "B": _padded(w, TENSOR_B, w.b_rows, w.b_cols, w.ldb_),
         "bias": None,
         "R": None,
+        "scale": None,
     }
     if w.bias:
-        out["bias"] = _padded(w, TENSOR_BIAS, 1, w.N, w.N)
+        out["bias"] = _padded(w, TENSOR_BIAS, 1, w.N, w.N, w.odt)
     if w.residual:
-        out["R"] = _padded(w, TENSOR_R, w.M, w.N, w.N)
+        out["R"] = _padded(w, TENSOR_R, w.M, w.N, w.N, w.odt)
+    if w.row_scale:
+        out["scale"] = _padded(w, TENSOR_SCALE, 1, w.M, w.M, w.odt)
     return out
