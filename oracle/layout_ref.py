@@ -15,7 +15,9 @@ Page maps
     "Choosing the physical thread shape";
   * GF(2) linear layouts -- "Triton LinearLayout", sections "Basis-vector
     representation", "LinearLayout::apply" and "Surjectivity, injectivity,
-    and broadcasts".
+    and broadcasts";
+  * the layout algebra -- same page, sections "Combining layouts" and
+    "invertAndCompose: derive data movement" (lin_* functions).
 
 MI355X maps (not on the pages; the matrix-core operand layout is AMD's
 documented v_mfma_f32_16x16x32_{f16,bf16} register layout)
@@ -218,6 +220,103 @@ def gf2_is_injective(bases, out_bits):
 
 def gf2_is_surjective(bases, out_bits):
     return gf2_rank(bases, out_bits) == sum(out_bits)
+
+
+# --------------------------------------------------------------------------
+# The layout algebra ("Triton LinearLayout", sections "Combining layouts" and
+# "invertAndCompose: derive data movement"), on flat maps: a map of nin input
+# bits to nout output bits is (cols, nout) with cols[i] the packed output word
+# of input bit i.
+# --------------------------------------------------------------------------
+
+def lin_apply(cols, x):
+    """XOR of the columns selected by the set bits of x."""
+    y = 0
+    for i, c in enumerate(cols):
+        if (x >> i) & 1:
+            y ^= c
+    return y
+
+
+def lin_compose(outer, inner):
+    """outer o inner: the page's rule -- outer applied to each basis of inner."""
+    return [lin_apply(outer, c) for c in inner]
+
+
+def lin_product(a, a_nout, b):
+    """Direct sum: inputs of a then b, outputs of a then b (b's shifted up)."""
+    return list(a) + [c << a_nout for c in b]
+
+
+def lin_sublayout(cols, nout, in_bits, out_bits):
+    """Keep the input bits listed in in_bits and the output bits listed in
+    out_bits (each list in increasing order); kept output bits are packed."""
+    out = []
+    for i in in_bits:
+        w = 0
+        for k, b in enumerate(out_bits):
+            w |= ((cols[i] >> b) & 1) << k
+        out.append(w)
+    return out
+
+
+def lin_rank(cols, nout):
+    rows = list(cols)
+    rank = 0
+    for bit in range(nout):
+        pivot = next((r for r in rows if (r >> bit) & 1), None)
+        if pivot is None:
+            continue
+        rows.remove(pivot)
+        rows = [r ^ pivot if (r >> bit) & 1 else r for r in rows]
+        rank += 1
+    return rank
+
+
+def lin_solve(S, nout, t):
+    """A word q over S's input bits with lin_apply(S, q) == t, or None.
+
+    Gauss-Jordan elimination on the augmented system [S | t]: each row is an
+    output bit; the unknowns are S's input bits; free unknowns are set to 0."""
+    nin = len(S)
+    rows = []
+    for b in range(nout):
+        coef = 0
+        for j, c in enumerate(S):
+            if (c >> b) & 1:
+                coef |= 1 << j
+        rows.append([coef, (t >> b) & 1])
+    pivots = []
+    r = 0
+    for j in range(nin):
+        p = next((k for k in range(r, len(rows)) if (rows[k][0] >> j) & 1), None)
+        if p is None:
+            continue
+        rows[r], rows[p] = rows[p], rows[r]
+        for k in range(len(rows)):
+            if k != r and (rows[k][0] >> j) & 1:
+                rows[k] = [rows[k][0] ^ rows[r][0], rows[k][1] ^ rows[r][1]]
+        pivots.append(j)
+        r += 1
+    if any(row[0] == 0 and row[1] for row in rows):
+        return None
+    q = 0
+    for k, j in enumerate(pivots):
+        if rows[k][1]:
+            q |= 1 << j
+    return q
+
+
+def lin_invert_and_compose(R, S, nout):
+    """Q with S(Q(x)) == R(x) for all x -- the page's S^-1 o R, where S may be
+    non-injective (a pseudo-inverse) -- or None if R leaves S's image."""
+    Q = []
+    for c in R:
+        q = lin_solve(S, nout, c)
+        if q is None:
+            return None
+        Q.append(q)
+    return Q
 
 
 def log2_exact(n):

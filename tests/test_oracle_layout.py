@@ -4,6 +4,7 @@ Every fixture under tests/golden/ names the page and section it comes from.
 """
 import itertools
 
+import numpy as np
 import pytest
 
 from oracle import layout_ref as L
@@ -354,3 +355,101 @@ def test_dma_mn_transposed_reads_conflict_free(R):
             for n, window in [(16, 128), (32, 256)]:
                 for q in range(0, 64, n):
                     assert _conflicts_bytes(lanes[q:q + n], window) == 1
+
+
+# ---- the layout algebra ("Triton LinearLayout", sections "Combining layouts" and
+# "invertAndCompose: derive data movement"), pinned by enumeration ------------------
+
+def _rand_lin(rng, nin, nout, zero_frac=0.0):
+    cols = [int(rng.integers(0, 1 << nout)) if nout else 0 for _ in range(nin)]
+    return [0 if rng.random() < zero_frac else c for c in cols]
+
+
+def test_lin_apply_page_example():
+    # lane bits 0-1 -> (1,1), (2,2); warp bits 2-3 -> (0,1), (0,2); outputs
+    # packed as row (bits 0-1) | col (bits 2-3).  The page evaluates
+    # lane=3, warp=2 to (row=3, col=1).
+    cols = [1 | 1 << 2, 2 | 2 << 2, 0 | 1 << 2, 0 | 2 << 2]
+    assert L.lin_apply(cols, 3 | 2 << 2) == 3 | 1 << 2
+    # and the whole map is (lane, lane XOR warp)
+    for lane in range(4):
+        for warp in range(4):
+            assert L.lin_apply(cols, lane | warp << 2) == lane | (lane ^ warp) << 2
+
+
+def test_lin_compose_is_function_composition():
+    rng = np.random.default_rng(31)
+    for _ in range(40):
+        nin, nmid, nout = (int(v) for v in rng.integers(0, 7, 3))
+        inner = _rand_lin(rng, nin, nmid)
+        outer = _rand_lin(rng, nmid, nout)
+        comp = L.lin_compose(outer, inner)
+        for x in range(1 << nin):
+            assert L.lin_apply(comp, x) == L.lin_apply(outer, L.lin_apply(inner, x))
+
+
+def test_lin_product_is_a_direct_sum():
+    rng = np.random.default_rng(32)
+    for _ in range(30):
+        an, ao, bn, bo = (int(v) for v in rng.integers(0, 5, 4))
+        a, b = _rand_lin(rng, an, ao), _rand_lin(rng, bn, bo)
+        p = L.lin_product(a, ao, b)
+        for xa in range(1 << an):
+            for xb in range(1 << bn):
+                assert L.lin_apply(p, xa | xb << an) == L.lin_apply(a, xa) | L.lin_apply(b, xb) << ao
+
+
+def test_lin_sublayout_restricts_and_projects():
+    rng = np.random.default_rng(33)
+    for _ in range(30):
+        nin, nout = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+        cols = _rand_lin(rng, nin, nout)
+        ins = sorted(int(i) for i in rng.choice(nin, int(rng.integers(0, nin + 1)), replace=False))
+        outs = sorted(int(o) for o in rng.choice(nout, int(rng.integers(0, nout + 1)), replace=False))
+        sub = L.lin_sublayout(cols, nout, ins, outs)
+        for x in range(1 << len(ins)):
+            full_x = sum(((x >> k) & 1) << i for k, i in enumerate(ins))
+            y = L.lin_apply(cols, full_x)
+            assert L.lin_apply(sub, x) == sum(((y >> b) & 1) << k for k, b in enumerate(outs))
+
+
+def test_lin_rank_counts_distinct_images():
+    rng = np.random.default_rng(34)
+    for _ in range(40):
+        nin, nout = int(rng.integers(0, 7)), int(rng.integers(0, 7))
+        cols = _rand_lin(rng, nin, nout, zero_frac=0.2)
+        images = {L.lin_apply(cols, x) for x in range(1 << nin)}
+        assert 1 << L.lin_rank(cols, nout) == len(images)
+
+
+def test_lin_invert_and_compose_solves_s_q_equals_r():
+    rng = np.random.default_rng(35)
+    solved = unsolvable = 0
+    for _ in range(80):
+        nr, ns, nt = int(rng.integers(0, 6)), int(rng.integers(0, 7)), int(rng.integers(0, 6))
+        S = _rand_lin(rng, ns, nt, zero_frac=0.25)          # may broadcast (zero bases)
+        if rng.random() < 0.3 and ns:
+            S[int(rng.integers(0, ns))] = S[0]              # duplicate: not injective
+        R = _rand_lin(rng, nr, nt)
+        Q = L.lin_invert_and_compose(R, S, nt)
+        span = {L.lin_apply(S, y) for y in range(1 << ns)}
+        if Q is None:
+            assert any(c not in span for c in R)
+            unsolvable += 1
+            continue
+        solved += 1
+        for x in range(1 << nr):
+            assert L.lin_apply(S, L.lin_apply(Q, x)) == L.lin_apply(R, x)
+    assert solved > 20 and unsolvable > 5
+
+
+def test_lin_invert_and_compose_page_example():
+    # R = S = the page's (lane, warp) -> (lane, lane XOR warp): S^-1 o R = identity
+    cols = [1 | 1 << 2, 2 | 2 << 2, 0 | 1 << 2, 0 | 2 << 2]
+    assert L.lin_invert_and_compose(cols, cols, 4) == [1, 2, 4, 8]
+    # with warp bit 1 broadcast in S (a zero basis), S reaches only half of the
+    # 4 x 4 coordinates: (row 0, col 2) is outside its image, (3, 3) inside
+    S = [1 | 1 << 2, 2 | 2 << 2, 0 | 1 << 2, 0]
+    assert L.lin_invert_and_compose([0 | 2 << 2], S, 4) is None
+    Q = L.lin_invert_and_compose([3 | 3 << 2], S, 4)
+    assert Q is not None and L.lin_apply(S, Q[0]) == 3 | 3 << 2
