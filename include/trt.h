@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 3
+#define TRT_ABI_VERSION 4
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -260,6 +260,43 @@ trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink,
 #define TRT_MFMA_PROBE_SINK_BYTES 4194304
 trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iters,
                                float* sink, int64_t sink_bytes, void* stream);
+
+/*
+ * The GF(2) layout algebra of the layout module ("Triton LinearLayout",
+ * sections "Combining layouts" and "invertAndCompose: derive data
+ * movement"), on caller arrays, host only (no HIP call).  The library derives
+ * the inverse copy maps of its pipelined kernel with the same code at build
+ * time.  A map of nin input bits to nout output bits (0 <= nin, nout <= 32)
+ * is given by its nin columns: cols[i] is the image of input bit i, a word
+ * with no bit at or above nout; the image of x is the XOR of the columns of
+ * x's set bits.  Output arrays belong to the caller.  Errors: TRT_ERR_ARG
+ * (bit counts out of range, a column beyond nout, mismatched sizes),
+ * TRT_ERR_NULL, TRT_ERR_SIZE (a product beyond 32 bits).
+ */
+/* GF(2) rank of the map, or -1 on an argument error. */
+int32_t trt_gf2_rank(int32_t nin, int32_t nout, const uint32_t* cols);
+/* out (inner_nin columns of outer_nout bits) = outer o inner; outer_nin
+ * must equal inner_nout. */
+trt_status trt_gf2_compose(int32_t outer_nin, int32_t outer_nout, const uint32_t* outer,
+                           int32_t inner_nin, int32_t inner_nout, const uint32_t* inner,
+                           uint32_t* out);
+/* out (a_nin + b_nin columns) = the direct sum of a and b: input bits of a
+ * then of b, output bits of a then of b (b's columns shifted by a_nout). */
+trt_status trt_gf2_product(int32_t a_nin, int32_t a_nout, const uint32_t* a,
+                           int32_t b_nin, int32_t b_nout, const uint32_t* b,
+                           uint32_t* out);
+/* out = the map restricted to the input bits set in in_mask and projected
+ * onto the output bits set in out_mask (kept bits in order, packed); its
+ * sizes go to *out_nin and *out_nout. */
+trt_status trt_gf2_sublayout(int32_t nin, int32_t nout, const uint32_t* cols,
+                             uint32_t in_mask, uint32_t out_mask, uint32_t* out,
+                             int32_t* out_nin, int32_t* out_nout);
+/* q (r_nin columns of s_nin bits) with S(q(x)) == R(x) for every x, where
+ * R: r_nin -> t_bits and S: s_nin -> t_bits; S may be non-injective (the
+ * solution then uses only the columns of S independent of earlier ones).
+ * TRT_ERR_ARG if some value of R is not a value of S. */
+trt_status trt_gf2_invert_and_compose(int32_t r_nin, int32_t t_bits, const uint32_t* r,
+                                      int32_t s_nin, const uint32_t* s, uint32_t* q);
 
 /* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
 int32_t trt_abi_version(void);

@@ -277,3 +277,59 @@ def test_row_scale_overlap_rejected():
     assert status(scale=BASE * 3 - 2 * 64) == trt.OK          # ends where C starts
     assert status(scale=BASE * 3 - 2 * 64 + 2) == trt.ERR_OVERLAP
     assert status(out_dtype=trt.F32, scale=BASE * 3 - 4 * 64 + 4) == trt.ERR_OVERLAP
+
+
+# ---- the GF(2) layout algebra of the library against the oracle's ------------------
+
+def _rand_cols(rng, nin, nout, zero_frac=0.0):
+    return [0 if rng.random() < zero_frac else (int(rng.integers(0, 1 << nout)) if nout else 0)
+            for _ in range(nin)]
+
+
+def test_gf2_algebra_matches_oracle():
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        a_in, a_out, b_in, b_out = (int(v) for v in rng.integers(0, 9, 4))
+        a = _rand_cols(rng, a_in, a_out, 0.2)
+        b = _rand_cols(rng, b_in, b_out, 0.2)
+        assert trt.gf2_rank(a, a_out) == L.lin_rank(a, a_out)
+        assert trt.gf2_product(a, a_out, b, b_out) == L.lin_product(a, a_out, b)
+        outer = _rand_cols(rng, a_out, b_out)
+        assert trt.gf2_compose(outer, b_out, a, a_out) == L.lin_compose(outer, a)
+        in_mask, out_mask = int(rng.integers(0, 1 << 9)), int(rng.integers(0, 1 << 9))
+        cols, ni, no = trt.gf2_sublayout(a, a_out, in_mask, out_mask)
+        ins = [i for i in range(a_in) if (in_mask >> i) & 1]
+        outs = [o for o in range(a_out) if (out_mask >> o) & 1]
+        assert (cols, ni, no) == (L.lin_sublayout(a, a_out, ins, outs), len(ins), len(outs))
+
+
+def test_gf2_invert_and_compose_matches_oracle():
+    rng = np.random.default_rng(42)
+    solved = 0
+    for _ in range(300):
+        nr, ns, nt = int(rng.integers(0, 8)), int(rng.integers(0, 9)), int(rng.integers(0, 8))
+        S = _rand_cols(rng, ns, nt, 0.25)
+        if ns and rng.random() < 0.3:
+            S[int(rng.integers(0, ns))] = S[0]
+        R = _rand_cols(rng, nr, nt)
+        ref = L.lin_invert_and_compose(R, S, nt)
+        if ref is None:
+            with pytest.raises(trt.TrtError) as e:
+                trt.gf2_invert_and_compose(R, S, nt)
+            assert e.value.status == trt.ERR_ARG
+        else:
+            # the same particular solution: pivots on the first independent columns
+            assert trt.gf2_invert_and_compose(R, S, nt) == ref
+            solved += 1
+    assert solved > 100
+
+
+def test_gf2_argument_errors():
+    with pytest.raises(trt.TrtError) as e:
+        trt.gf2_compose([1, 2], 2, [1], 1)          # outer has 2 input bits, inner 1 output bit
+    assert e.value.status == trt.ERR_ARG
+    with pytest.raises(trt.TrtError):
+        trt.gf2_product([1] * 20, 1, [1] * 20, 1)   # 40 input bits
+    assert trt.lib().trt_gf2_rank(1, 2, trt._u32([4])) == -1   # column beyond nout
+    with pytest.raises(trt.TrtError):
+        trt.gf2_rank([0] * 33, 4)

@@ -98,6 +98,18 @@ def lib():
         L.trt_hbm_read_probe.restype = i32
         L.trt_mfma_loop_probe.argtypes = [i32, vp, i32, vp, i64, vp]
         L.trt_mfma_loop_probe.restype = i32
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        L.trt_gf2_rank.argtypes = [i32, i32, u32p]
+        L.trt_gf2_rank.restype = i32
+        L.trt_gf2_compose.argtypes = [i32, i32, u32p, i32, i32, u32p, u32p]
+        L.trt_gf2_compose.restype = i32
+        L.trt_gf2_product.argtypes = [i32, i32, u32p, i32, i32, u32p, u32p]
+        L.trt_gf2_product.restype = i32
+        L.trt_gf2_sublayout.argtypes = [i32, i32, u32p, ctypes.c_uint32, ctypes.c_uint32, u32p,
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.trt_gf2_sublayout.restype = i32
+        L.trt_gf2_invert_and_compose.argtypes = [i32, i32, u32p, i32, u32p, u32p]
+        L.trt_gf2_invert_and_compose.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
         L.trt_last_error.argtypes = []
@@ -329,3 +341,47 @@ def mfma_loop_probe(operands, iters, dtype=F16, sink=None):
 def mfma_loop_probe_flops(iters):
     """FLOPs of one trt_mfma_loop_probe launch."""
     return 256 * 4 * iters * 32 * 2 * 32 * 32 * 16
+
+
+# ---- the GF(2) layout algebra (host only; maps as lists of column words) -------
+
+def _u32(cols):
+    arr = (ctypes.c_uint32 * max(len(cols), 1))(*[int(c) for c in cols])
+    return arr
+
+
+def gf2_rank(cols, nout):
+    r = lib().trt_gf2_rank(len(cols), nout, _u32(cols))
+    if r < 0:
+        raise TrtError(ERR_ARG, last_error())
+    return r
+
+
+def gf2_compose(outer, outer_nout, inner, inner_nout):
+    """outer o inner (outer has inner_nout input bits)."""
+    out = (ctypes.c_uint32 * max(len(inner), 1))()
+    _check(lib().trt_gf2_compose(len(outer), outer_nout, _u32(outer), len(inner), inner_nout,
+                                 _u32(inner), out))
+    return list(out)[:len(inner)]
+
+
+def gf2_product(a, a_nout, b, b_nout):
+    out = (ctypes.c_uint32 * max(len(a) + len(b), 1))()
+    _check(lib().trt_gf2_product(len(a), a_nout, _u32(a), len(b), b_nout, _u32(b), out))
+    return list(out)[:len(a) + len(b)]
+
+
+def gf2_sublayout(cols, nout, in_mask, out_mask):
+    """Returns (columns, nin, nout) of the restricted, projected map."""
+    out = (ctypes.c_uint32 * 32)()
+    ni, no = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().trt_gf2_sublayout(len(cols), nout, _u32(cols), in_mask, out_mask, out,
+                                   ctypes.byref(ni), ctypes.byref(no)))
+    return list(out)[:ni.value], ni.value, no.value
+
+
+def gf2_invert_and_compose(R, S, t_bits):
+    """Q with S(Q(x)) == R(x); raises TrtError (ERR_ARG) when R leaves S's image."""
+    out = (ctypes.c_uint32 * max(len(R), 1))()
+    _check(lib().trt_gf2_invert_and_compose(len(R), t_bits, _u32(R), len(S), _u32(S), out))
+    return list(out)[:len(R)]

@@ -86,6 +86,15 @@ struct DmaOperand {
   static constexpr int BYTES = R * 64;                   // one stage of this operand
   static_assert(CHUNKS % TL::THREADS == 0, "whole copy iterations");
   static_assert(KC || R >= 128, "the rows-contiguous swizzle needs 16 chunks per k row");
+  // the slot maps are GF(2)-linear bijections and their derived inverses
+  // undo them exactly
+  static_assert(TL::template slot_maps_linear<R>(), "linear, bijective slot maps");
+  static_assert(gf2::equal(gf2::compose(TL::template kc_slot_inv<R>, TL::template kc_slot_lin<R>()),
+                           gf2::identity(ilog2(R) + 2)) &&
+                    gf2::equal(gf2::compose(TL::template mn_slot_inv<R>,
+                                            TL::template mn_slot_lin<R>()),
+                               gf2::identity(ilog2(R / 8) + 5)),
+                "derived inverse slot maps");
 
   const char* base;      // operand base address
   int64_t extent;        // operand extent in bytes
@@ -101,7 +110,7 @@ struct DmaOperand {
     for (int i = 0; i < NCH; ++i) {
       const int s = i * TL::THREADS + t;  // LDS slot this lane fills
       if (KC) {
-        const int r = TL::kc_slot_row(s), g = TL::kc_slot_g(s);
+        const int r = TL::template kc_slot_row<R>(s), g = TL::template kc_slot_g<R>(s);
         voff[i] = (uint32_t)(((int64_t)(row0 + r) * ld + 8 * g) * 2);
         kchunk = 8 * g;  // the same for every i: rows advance by THREADS/4
       } else {

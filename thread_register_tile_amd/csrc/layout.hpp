@@ -91,6 +91,177 @@ struct Gf2Map {
 };
 
 // ---------------------------------------------------------------------------
+// The layout algebra ("Triton LinearLayout", sections "Combining layouts" and
+// "invertAndCompose: derive data movement"), on GF(2)-linear maps of at most
+// 32 input bits to at most 32 output bits.  A map is stored by its columns:
+// col[i] is the image of input bit i as a packed output word.  The same
+// constexpr code derives maps at compile time (the inverse copy maps of the
+// pipelined kernel below) and serves the C ABI at run time.
+// ---------------------------------------------------------------------------
+namespace gf2 {
+
+struct Lin {
+  uint32_t col[32];
+  int nin, nout;
+
+  constexpr uint32_t apply(uint32_t x) const {
+    uint32_t y = 0;
+    for (int i = 0; i < nin; ++i)
+      if ((x >> i) & 1u) y ^= col[i];
+    return y;
+  }
+  constexpr uint32_t out_mask() const { return nout >= 32 ? 0xFFFFFFFFu : (1u << nout) - 1u; }
+};
+
+constexpr Lin zero(int nin, int nout) {
+  Lin l{};
+  l.nin = nin;
+  l.nout = nout;
+  return l;
+}
+
+constexpr Lin identity(int n) {
+  Lin l = zero(n, n);
+  for (int i = 0; i < n; ++i) l.col[i] = 1u << i;
+  return l;
+}
+
+// Echelon basis of a set of words: piv[b] holds a vector whose lowest set bit
+// is b (0 when there is none) and comb[b] the combination of the input
+// columns that produced it.
+struct Echelon {
+  uint32_t piv[32], comb[32];
+  int rank;
+
+  // Reduce word v (with combination c) by the pivots; returns the rest.
+  constexpr uint32_t reduce(uint32_t v, uint32_t& c) const {
+    while (v) {
+      const int b = __builtin_ctz(v);
+      if (!piv[b]) return v;
+      v ^= piv[b];
+      c ^= comb[b];
+    }
+    return 0;
+  }
+};
+
+constexpr Echelon echelon(const Lin& l) {
+  Echelon e{};
+  for (int i = 0; i < l.nin; ++i) {
+    uint32_t c = 1u << i;
+    const uint32_t v = e.reduce(l.col[i], c);
+    if (v) {
+      const int b = __builtin_ctz(v);
+      e.piv[b] = v;
+      e.comb[b] = c;
+      ++e.rank;
+    }
+  }
+  return e;
+}
+
+// Rank; injective = rank equals the input bits, surjective = the output bits
+// ("Triton LinearLayout", section "Surjectivity, injectivity, and broadcasts").
+constexpr int rank(const Lin& l) { return echelon(l).rank; }
+constexpr bool injective(const Lin& l) { return rank(l) == l.nin; }
+constexpr bool surjective(const Lin& l) { return rank(l) == l.nout; }
+constexpr bool bijective(const Lin& l) { return l.nin == l.nout && injective(l); }
+
+// outer o inner: outer applied to every column of inner (outer.nin == inner.nout).
+constexpr Lin compose(const Lin& outer, const Lin& inner) {
+  Lin l = zero(inner.nin, outer.nout);
+  for (int i = 0; i < inner.nin; ++i) l.col[i] = outer.apply(inner.col[i]);
+  return l;
+}
+
+// Direct sum: the input bits of a then those of b; the output bits of a then
+// those of b (a.nin + b.nin <= 32, a.nout + b.nout <= 32).
+constexpr Lin product(const Lin& a, const Lin& b) {
+  Lin l = zero(a.nin + b.nin, a.nout + b.nout);
+  for (int i = 0; i < a.nin; ++i) l.col[i] = a.col[i];
+  for (int i = 0; i < b.nin; ++i) l.col[a.nin + i] = b.col[i] << a.nout;
+  return l;
+}
+
+// Restriction to the input bits set in in_mask and projection onto the
+// output bits set in out_mask; kept bits stay in order and are packed.
+constexpr Lin sublayout(const Lin& l, uint32_t in_mask, uint32_t out_mask) {
+  Lin r = zero(__builtin_popcount(in_mask & (l.nin >= 32 ? 0xFFFFFFFFu : (1u << l.nin) - 1u)),
+               __builtin_popcount(out_mask & l.out_mask()));
+  int k = 0;
+  for (int i = 0; i < l.nin; ++i) {
+    if (!((in_mask >> i) & 1u)) continue;
+    uint32_t w = 0;
+    int o = 0;
+    for (int b = 0; b < l.nout; ++b)
+      if ((out_mask >> b) & 1u) w |= ((l.col[i] >> b) & 1u) << o++;
+    r.col[k++] = w;
+  }
+  return r;
+}
+
+// Given R: X -> T and S: Y -> T (same output bits), a map Q: X -> Y with
+// S(Q(x)) == R(x) for every x; false if some value of R is not a value of S.
+// S need not be injective (broadcast bits): Q picks, per column of R, the
+// solution that uses no column of S dependent on earlier ones.
+constexpr bool invert_and_compose(const Lin& R, const Lin& S, Lin& Q) {
+  Q = zero(R.nin, S.nin);
+  if (R.nout != S.nout) return false;
+  const Echelon e = echelon(S);
+  for (int i = 0; i < R.nin; ++i) {
+    uint32_t c = 0;
+    if (e.reduce(R.col[i], c)) return false;
+    Q.col[i] = c;
+  }
+  return true;
+}
+
+// Inverse of a bijective map.
+constexpr Lin inverse(const Lin& l) {
+  Lin q{};
+  invert_and_compose(identity(l.nout), l, q);
+  return q;
+}
+
+constexpr bool equal(const Lin& a, const Lin& b) {
+  if (a.nin != b.nin || a.nout != b.nout) return false;
+  for (int i = 0; i < a.nin; ++i)
+    if (a.col[i] != b.col[i]) return false;
+  return true;
+}
+
+// The GF(2) map of an integer function f on n input bits, read off its
+// values on the unit vectors (meaningful when f is GF(2)-linear; callers
+// check that with agrees()).
+template <class F>
+constexpr Lin from_function(int nin, int nout, F f) {
+  Lin l = zero(nin, nout);
+  for (int i = 0; i < nin; ++i) l.col[i] = (uint32_t)f(1u << i);
+  return l;
+}
+
+// apply() with the number of input bits fixed at compile time, for maps
+// known at compile time: the loop unrolls and every column folds into an
+// immediate, so device code evaluates the map with a few bit operations.
+template <int N>
+TRT_HD uint32_t apply_n(const Lin& l, uint32_t x) {
+  uint32_t y = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) y ^= ((x >> i) & 1u) ? l.col[i] : 0u;
+  return y;
+}
+
+// Whether f equals the map l on every input.
+template <class F>
+constexpr bool agrees(const Lin& l, F f) {
+  for (uint32_t x = 0; x < (1u << l.nin); ++x)
+    if ((uint32_t)f(x) != l.apply(x)) return false;
+  return true;
+}
+
+}  // namespace gf2
+
+// ---------------------------------------------------------------------------
 // A workgroup tile: logical shape, thread shape, register shape.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int MF_ = 16>
@@ -212,8 +383,28 @@ struct Tile {
   // constant address offset.
   TRT_HD static int kc_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
   TRT_HD static int kc_slot(int r, int g) { return 4 * r + (g ^ kc_swz(r)); }
-  TRT_HD static int kc_slot_row(int s) { return s >> 2; }
-  TRT_HD static int kc_slot_g(int s) { return (s & 3) ^ kc_swz(s >> 2); }
+  // The copy side needs the inverse, slot -> (row, chunk).  It is derived
+  // with the layout algebra: the slot map as a GF(2) map of (g, r) bits
+  // (2 chunk bits low, then the row bits), inverted.
+  template <int R>
+  static constexpr gf2::Lin kc_slot_lin() {
+    constexpr int rb = ilog2(R);
+    return gf2::from_function(rb + 2, rb + 2, [](uint32_t x) {
+      return (uint32_t)kc_slot((int)(x >> 2), (int)(x & 3));
+    });
+  }
+  template <int R>
+  static constexpr gf2::Lin kc_slot_inv = gf2::inverse(kc_slot_lin<R>());
+  template <int R>
+  TRT_HD static int kc_slot_row(int s) {
+    constexpr gf2::Lin inv = kc_slot_inv<R>;
+    return (int)(gf2::apply_n<ilog2(R) + 2>(inv, (uint32_t)s) >> 2);
+  }
+  template <int R>
+  TRT_HD static int kc_slot_g(int s) {
+    constexpr gf2::Lin inv = kc_slot_inv<R>;
+    return (int)(gf2::apply_n<ilog2(R) + 2>(inv, (uint32_t)s) & 3u);
+  }
   // rows-contiguous operand, [32 k rows][R/8 chunks of 8 rows]: chunk (k, c)
   // in slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*k0 XOR 12*k1 in the bits of k.
   // A transposing fragment read covers 4 consecutive k rows: 32 bytes of each
@@ -223,10 +414,40 @@ struct Tile {
   TRT_HD static int mn_swz(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 12 : 0); }
   template <int R>
   TRT_HD static int mn_slot(int k, int c) { return k * (R / 8) + (c ^ mn_swz(k)); }
+  // The inverse, slot -> (k, chunk), derived like kc_slot_inv: the slot map
+  // as a GF(2) map of (c, k) bits (chunk bits low, then 5 k bits), inverted.
   template <int R>
-  TRT_HD static int mn_slot_k(int s) { return s / (R / 8); }
+  static constexpr gf2::Lin mn_slot_lin() {
+    constexpr int cb = ilog2(R / 8);
+    return gf2::from_function(cb + 5, cb + 5, [](uint32_t x) {
+      return (uint32_t)mn_slot<R>((int)(x >> cb), (int)(x & ((1u << cb) - 1u)));
+    });
+  }
   template <int R>
-  TRT_HD static int mn_slot_c(int s) { return (s % (R / 8)) ^ mn_swz(s / (R / 8)); }
+  static constexpr gf2::Lin mn_slot_inv = gf2::inverse(mn_slot_lin<R>());
+  template <int R>
+  TRT_HD static int mn_slot_k(int s) {
+    constexpr gf2::Lin inv = mn_slot_inv<R>;
+    return (int)(gf2::apply_n<ilog2(R / 8) + 5>(inv, (uint32_t)s) >> ilog2(R / 8));
+  }
+  template <int R>
+  TRT_HD static int mn_slot_c(int s) {
+    constexpr gf2::Lin inv = mn_slot_inv<R>;
+    return (int)(gf2::apply_n<ilog2(R / 8) + 5>(inv, (uint32_t)s) & ((1u << ilog2(R / 8)) - 1u));
+  }
+  // The derivations hold only if the slot maps are GF(2)-linear bijections:
+  // checked on every input.
+  template <int R>
+  static constexpr bool slot_maps_linear() {
+    constexpr int rb = ilog2(R), cb = ilog2(R / 8);
+    return gf2::bijective(kc_slot_lin<R>()) && gf2::bijective(mn_slot_lin<R>()) &&
+           gf2::agrees(kc_slot_lin<R>(), [](uint32_t x) {
+             return (uint32_t)kc_slot((int)(x >> 2), (int)(x & 3));
+           }) &&
+           gf2::agrees(mn_slot_lin<R>(), [](uint32_t x) {
+             return (uint32_t)mn_slot<R>((int)(x >> cb), (int)(x & ((1u << cb) - 1u)));
+           }) && rb >= 1;
+  }
 
   // ---- cooperative copies ---------------------------------------------------
   // "My Triton From Scratch, Part 12: CUDA Tile Layouts", section

@@ -346,6 +346,95 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const trt::u32x4* __r
   sink[(int64_t)blockIdx.x * 256 + t] = sum;
 }
 
+// ---- the layout algebra on caller arrays (host only) ------------------------
+
+namespace {
+
+// A caller's map: nin columns, each within nout bits.
+trt_status read_lin(int32_t nin, int32_t nout, const uint32_t* cols, trt::gf2::Lin& l,
+                    const char* what) {
+  if (nin < 0 || nin > 32 || nout < 0 || nout > 32)
+    return fail(TRT_ERR_ARG, std::string(what) + ": bit counts must be in [0, 32]");
+  if (nin > 0 && !cols) return fail(TRT_ERR_NULL, std::string(what) + ": columns must be non-null");
+  l = trt::gf2::zero(nin, nout);
+  for (int i = 0; i < nin; ++i) {
+    if (cols[i] & ~l.out_mask())
+      return fail(TRT_ERR_ARG, std::string(what) + ": a column has bits beyond nout");
+    l.col[i] = cols[i];
+  }
+  return TRT_OK;
+}
+
+void write_lin(const trt::gf2::Lin& l, uint32_t* out) {
+  for (int i = 0; i < l.nin; ++i) out[i] = l.col[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t trt_gf2_rank(int32_t nin, int32_t nout, const uint32_t* cols) {
+  trt::gf2::Lin l{};
+  if (read_lin(nin, nout, cols, l, "map") != TRT_OK) return -1;
+  g_err.clear();
+  return trt::gf2::rank(l);
+}
+
+trt_status trt_gf2_compose(int32_t outer_nin, int32_t outer_nout, const uint32_t* outer,
+                           int32_t inner_nin, int32_t inner_nout, const uint32_t* inner,
+                           uint32_t* out) {
+  trt::gf2::Lin o{}, i{};
+  if (const trt_status st = read_lin(outer_nin, outer_nout, outer, o, "outer"); st != TRT_OK) return st;
+  if (const trt_status st = read_lin(inner_nin, inner_nout, inner, i, "inner"); st != TRT_OK) return st;
+  if (outer_nin != inner_nout) return fail(TRT_ERR_ARG, "outer input bits must equal inner output bits");
+  if (inner_nin > 0 && !out) return fail(TRT_ERR_NULL, "out must be non-null");
+  write_lin(trt::gf2::compose(o, i), out);
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_gf2_product(int32_t a_nin, int32_t a_nout, const uint32_t* a, int32_t b_nin,
+                           int32_t b_nout, const uint32_t* b, uint32_t* out) {
+  trt::gf2::Lin la{}, lb{};
+  if (const trt_status st = read_lin(a_nin, a_nout, a, la, "a"); st != TRT_OK) return st;
+  if (const trt_status st = read_lin(b_nin, b_nout, b, lb, "b"); st != TRT_OK) return st;
+  if (a_nin + b_nin > 32 || a_nout + b_nout > 32)
+    return fail(TRT_ERR_SIZE, "the product has more than 32 input or output bits");
+  if (a_nin + b_nin > 0 && !out) return fail(TRT_ERR_NULL, "out must be non-null");
+  write_lin(trt::gf2::product(la, lb), out);
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_gf2_sublayout(int32_t nin, int32_t nout, const uint32_t* cols, uint32_t in_mask,
+                             uint32_t out_mask, uint32_t* out, int32_t* out_nin,
+                             int32_t* out_nout) {
+  trt::gf2::Lin l{};
+  if (const trt_status st = read_lin(nin, nout, cols, l, "map"); st != TRT_OK) return st;
+  const trt::gf2::Lin r = trt::gf2::sublayout(l, in_mask, out_mask);
+  if (r.nin > 0 && !out) return fail(TRT_ERR_NULL, "out must be non-null");
+  write_lin(r, out);
+  if (out_nin) *out_nin = r.nin;
+  if (out_nout) *out_nout = r.nout;
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_gf2_invert_and_compose(int32_t r_nin, int32_t t_bits, const uint32_t* r,
+                                      int32_t s_nin, const uint32_t* s, uint32_t* q) {
+  trt::gf2::Lin lr{}, ls{}, lq{};
+  if (const trt_status st = read_lin(r_nin, t_bits, r, lr, "R"); st != TRT_OK) return st;
+  if (const trt_status st = read_lin(s_nin, t_bits, s, ls, "S"); st != TRT_OK) return st;
+  if (r_nin > 0 && !q) return fail(TRT_ERR_NULL, "q must be non-null");
+  if (!trt::gf2::invert_and_compose(lr, ls, lq))
+    return fail(TRT_ERR_ARG, "a value of R is not a value of S");
+  write_lin(lq, q);
+  g_err.clear();
+  return TRT_OK;
+}
+
+}  // extern "C"
+
 extern "C" {
 
 trt_status trt_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
