@@ -9,7 +9,9 @@ imports it.
   (gemm_ref.c), reached through ctypes.
 * decode / round16 / round_out -- the binary16, bfloat16 and binary32
   formats from their definitions.
-* layout_ref -- the ownership, copy and swizzle maps in plain Python ints.
+* layout_ref -- the ownership, copy and swizzle maps in plain Python ints,
+  and the GF(2) layout algebra.
+* reduce_ref -- the rank-1 block reduction (sum / max / min per block).
 """
 import ctypes
 import os
