@@ -167,6 +167,77 @@ def mfma_loop_tflops(trt, torch, host_a, dtype, kern_ms, launches):
     return trt.mfma_loop_probe_flops(iters) / s / 1e12
 
 
+def bench_reduce(args, trt, torch, np, W):
+    """The rank-1 block reduction workload: one JSON line in HBM GB/s."""
+    from oracle import reduce_ref as RR
+    w = W.REDUCE
+    bits = W.make_reduce_input(w)
+    x = torch.from_numpy(bits.view(np.int32 if bits.dtype == np.uint32 else np.int16)).cuda()
+    out = torch.empty(w.nblocks, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step():
+        trt.block_reduce_raw(x.data_ptr(), w.n, w.block, w.dtype, w.op, out.data_ptr(), sptr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(args.steps, 20))]
+    for a, b in evs:
+        a.record(stream); step(); b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
+    kgbs = w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_bytes": w.algorithmic_bytes, "kernel_ms": round(kern_ms, 5)}
+    if not args.no_stream_read:
+        sr = stream_read_gbps(trt, torch)
+        roofline["stream_read_GBps"] = round(sr, 1)
+        roofline["frac_of_stream_read"] = round(kgbs / sr, 4)
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        got = out.cpu().numpy()
+        # the oracle on the first blocks, sized to the CPU budget by a short run
+        t0 = time.perf_counter()
+        RR.block_reduce(bits[:64 * w.block], w.dtype, 64 * w.block, w.block, w.op)
+        per_block = (time.perf_counter() - t0) / 64
+        nb = int(min(w.nblocks, max(64, args.cpu_seconds / max(per_block, 1e-9))))
+        t0 = time.perf_counter()
+        ref = RR.block_reduce(bits[:nb * w.block], w.dtype, nb * w.block, w.block, w.op)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": (W.ELEM_BYTES[w.dtype] * nb * w.block + 4 * nb) / t_cpu / 1e9,
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"blocks 0..{nb - 1} of {w.nblocks} (python + fsum, one core), {t_cpu:.1f} s"}
+        import oracle
+        err = np.abs(got[:nb].astype(np.float64) - ref)
+        absum = np.abs(oracle.decode(bits[:nb * w.block], w.dtype)).reshape(nb, w.block).sum(1)
+        bound = w.block * 2.0 ** -24 * absum + 2.0 ** -24 * np.abs(ref)   # binary32 summation
+        parity = {"blocks": nb, "max_abs": float(err.max()), "ok": bool((err <= bound).all())}
+    line = {
+        "metric": "rank-1 block reduction, HBM GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": W.DTYPE_NAMES[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": f"block sum of {w.n} f16 elements, BLOCK={w.block}",
+                   "n": w.n, "block": w.block, "op": ["sum", "max", "min"][w.op],
+                   "csrc_digest": csrc_digest()},
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +281,8 @@ def main():
         sys.exit(1)
     trt.lib()  # fail loudly if the HIP library is missing
 
+    if args.workload == "reduce":
+        return bench_reduce(args, trt, torch, np, W)
     w = W.CONFIGS[args.workload]
     tile = tuple(int(x) for x in args.tile.split(",")) if args.tile else w.tile
     host = W.make_inputs(w)

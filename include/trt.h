@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 4
+#define TRT_ABI_VERSION 5
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -297,6 +297,26 @@ trt_status trt_gf2_sublayout(int32_t nin, int32_t nout, const uint32_t* cols,
  * TRT_ERR_ARG if some value of R is not a value of S. */
 trt_status trt_gf2_invert_and_compose(int32_t r_nin, int32_t t_bits, const uint32_t* r,
                                       int32_t s_nin, const uint32_t* s, uint32_t* q);
+
+/*
+ * trt_block_reduce -- the rank-1 block reduction ("My Triton From Scratch,
+ * Part 12: CUDA Tile Layouts", section "Output shape is not always thread
+ * shape"): out[b] = op over x[b*block .. min(n, (b+1)*block) - 1] for every
+ * block b = 0 .. ceil(n / block) - 1 (the last block may be partial; its
+ * missing elements are masked off).  x: n contiguous elements of dtype
+ * (TRT_F16, TRT_BF16 or TRT_F32), aligned to its element; out: ceil(n/block)
+ * binary32 results, 4-byte aligned, disjoint from x; both device buffers
+ * owned by the caller.  op: TRT_REDUCE_SUM (accumulated in binary32, in an
+ * order of the library's choosing), TRT_REDUCE_MAX or TRT_REDUCE_MIN (an
+ * element of the block; NaN if any element is NaN; +0 and -0 compare
+ * equal).  n, block >= 1, n <= 2^40.  Errors before any HIP call:
+ * TRT_ERR_SIZE, TRT_ERR_DTYPE, TRT_ERR_ARG (op), TRT_ERR_NULL,
+ * TRT_ERR_ALIGN, TRT_ERR_OVERLAP; TRT_ERR_HIP if the launch fails.
+ * Enqueued on `stream`.
+ */
+typedef enum { TRT_REDUCE_SUM = 0, TRT_REDUCE_MAX = 1, TRT_REDUCE_MIN = 2 } trt_reduce_op;
+trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dtype,
+                            int32_t op, float* out, void* stream);
 
 /* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
 int32_t trt_abi_version(void);

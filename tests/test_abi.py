@@ -333,3 +333,23 @@ def test_gf2_argument_errors():
     assert trt.lib().trt_gf2_rank(1, 2, trt._u32([4])) == -1   # column beyond nout
     with pytest.raises(trt.TrtError):
         trt.gf2_rank([0] * 33, 4)
+
+
+# ---- the block reduction: argument checks (no HIP call on error) -------------------
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), trt.ERR_SIZE), (dict(block=0), trt.ERR_SIZE), (dict(n=(1 << 40) + 1), trt.ERR_SIZE),
+    (dict(dtype=4), trt.ERR_DTYPE), (dict(op=3), trt.ERR_ARG),
+    (dict(x=0), trt.ERR_NULL), (dict(out=0), trt.ERR_NULL),
+    (dict(x=BASE + 1), trt.ERR_ALIGN), (dict(dtype=trt.F32, x=BASE + 2), trt.ERR_ALIGN),
+    (dict(out=BASE * 2 + 2), trt.ERR_ALIGN),
+    (dict(out=BASE + 1000), trt.ERR_OVERLAP),          # inside x (4096 f16 = 8 KiB)
+    (dict(out=BASE - 4 * 64 + 4), trt.ERR_OVERLAP),    # 64 results end inside x
+])
+def test_block_reduce_rejections(kw, code):
+    a = dict(x=BASE, n=4096, block=64, dtype=trt.F16, op=trt.REDUCE_SUM, out=BASE * 2)
+    a.update(kw)
+    with pytest.raises(trt.TrtError) as e:
+        trt.block_reduce_raw(a["x"], a["n"], a["block"], a["dtype"], a["op"], a["out"])
+    assert e.value.status == code
+    assert trt.last_error() != ""

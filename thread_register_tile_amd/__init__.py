@@ -110,6 +110,8 @@ def lib():
         L.trt_gf2_sublayout.restype = i32
         L.trt_gf2_invert_and_compose.argtypes = [i32, i32, u32p, i32, u32p, u32p]
         L.trt_gf2_invert_and_compose.restype = i32
+        L.trt_block_reduce.argtypes = [vp, i64, i64, i32, i32, vp, vp]
+        L.trt_block_reduce.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
         L.trt_last_error.argtypes = []
@@ -385,3 +387,25 @@ def gf2_invert_and_compose(R, S, t_bits):
     out = (ctypes.c_uint32 * max(len(R), 1))()
     _check(lib().trt_gf2_invert_and_compose(len(R), t_bits, _u32(R), len(S), _u32(S), out))
     return list(out)[:len(R)]
+
+
+# ---- the rank-1 block reduction ---------------------------------------------------
+
+REDUCE_SUM, REDUCE_MAX, REDUCE_MIN = 0, 1, 2
+
+
+def block_reduce_raw(x, n, block, dtype, op, out, stream=0):
+    """trt_block_reduce on raw device addresses; raises TrtError on error."""
+    _check(lib().trt_block_reduce(x, n, block, dtype, op, out, stream or None))
+
+
+def block_reduce(x, block, op=REDUCE_SUM, out=None):
+    """out[b] = op over each block of `block` consecutive elements of the 1-D
+    device tensor x (float16, bfloat16 or float32); returns float32 [nblocks]."""
+    torch = _torch()
+    n = x.numel()
+    nb = -(-n // block)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.float32, device=x.device)
+    block_reduce_raw(x.data_ptr(), n, block, _dtype_code(x), op, out.data_ptr(), _stream(x.device))
+    return out

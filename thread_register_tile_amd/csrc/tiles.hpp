@@ -39,4 +39,8 @@ inline void launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s
 // Launch the HBM-streaming kernel for M <= 16 (kern_skinny.hip).
 void launch_skinny(GemmArgs a, int dt, hipStream_t s);
 
+// Launch the rank-1 block reduction (kern_reduce.hip).
+struct ReduceArgs;
+void launch_reduce(const ReduceArgs& a, int dt, int op, hipStream_t s);
+
 }  // namespace trt

@@ -8,6 +8,7 @@
 #include "../../include/trt.h"
 #include "gemm_kernel.hpp"
 #include "gemm_skinny.hpp"
+#include "reduce.hpp"
 #include "tiles.hpp"
 #include "validate.hpp"
 
@@ -634,6 +635,33 @@ trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iter
     hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_BF16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
                        iters, dst);
   return check_launch("matrix-core probe launch");
+}
+
+trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dtype, int32_t op,
+                            float* out, void* stream) {
+  if (n < 1 || block < 1) return fail(TRT_ERR_SIZE, "n and block must be >= 1");
+  if (n > (int64_t(1) << 40)) return fail(TRT_ERR_SIZE, "n must be <= 2^40");
+  if (dtype != TRT_F16 && dtype != TRT_BF16 && dtype != TRT_F32)
+    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16, TRT_BF16 or TRT_F32");
+  if (op != TRT_REDUCE_SUM && op != TRT_REDUCE_MAX && op != TRT_REDUCE_MIN)
+    return fail(TRT_ERR_ARG, "op must be TRT_REDUCE_SUM, TRT_REDUCE_MAX or TRT_REDUCE_MIN");
+  if (!x || !out) return fail(TRT_ERR_NULL, "x and out must be non-null");
+  const int64_t esz = trt::elem_bytes(dtype);
+  if (!aligned(x, (uintptr_t)esz) || !aligned(out, 4))
+    return fail(TRT_ERR_ALIGN, "x must be aligned to its element and out to 4 bytes");
+  const int64_t nblocks = (n + block - 1) / block;
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), o0 = reinterpret_cast<uintptr_t>(out);
+  if (x0 < o0 + (uintptr_t)(4 * nblocks) && o0 < x0 + (uintptr_t)(esz * n))
+    return fail(TRT_ERR_OVERLAP, "out must not overlap x");
+  trt::ReduceArgs a{};
+  a.x = x;
+  a.out = out;
+  a.n = n;
+  a.block = block;
+  a.nblocks = nblocks;
+  a.vec = aligned(x, 16) && (block * esz) % 16 == 0;
+  trt::launch_reduce(a, dtype, op, static_cast<hipStream_t>(stream));
+  return check_launch("block reduction launch");
 }
 
 int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }

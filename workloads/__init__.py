@@ -204,3 +204,43 @@ def make_inputs(w: Workload) -> dict:
     if w.row_scale:
         out["scale"] = _padded(w, TENSOR_SCALE, 1, w.M, w.M, w.odt)
     return out
+
+
+# ---- the rank-1 block reduction ("My Triton From Scratch, Part 12: CUDA Tile
+# Layouts", section "Output shape is not always thread shape") -------------------
+
+@dataclass(frozen=True)
+class ReduceWorkload:
+    name: str
+    n: int
+    block: int
+    dtype: int = F16
+    op: int = 0             # 0 sum, 1 max, 2 min
+    dist: str = "normal"    # normal | uniform | ternary (exact sums)
+    scale: float = 1.0
+    seed: int = 0
+
+    @property
+    def nblocks(self):
+        return -(-self.n // self.block)
+
+    @property
+    def algorithmic_bytes(self):
+        return ELEM_BYTES[self.dtype] * self.n + 4 * self.nblocks
+
+
+REDUCE = ReduceWorkload("reduce", 1 << 28, 1024, dtype=F16, op=0, dist="normal", scale=1.0, seed=7)
+
+
+def make_reduce_input(w: ReduceWorkload) -> np.ndarray:
+    """The n input elements (raw bits: uint16, or uint32 for F32), tensor id 0."""
+    rng = np.random.default_rng([w.seed, 0])
+    if w.dist == "normal":
+        x = rng.standard_normal(w.n) / w.scale
+    elif w.dist == "uniform":
+        x = rng.uniform(-w.scale, w.scale, w.n)
+    elif w.dist == "ternary":
+        x = rng.integers(-1, 2, w.n).astype(np.float64)
+    else:
+        raise ValueError(w.dist)
+    return to_bits(x, w.dtype)
