@@ -243,7 +243,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     auto fetch = [&](int it) {
       if constexpr (MODE != EPI_MASKED) {
         const int m = row_of(pass, it);
-        if constexpr (MODE == EPI_FAST_RES) rr[it % RING] = O::ld4(p.R, (int64_t)m * p.ldr + n);
+        if constexpr (MODE == EPI_FAST_RES) rr[it % RING] = O::ld4_once(p.R, (int64_t)m * p.ldr + n);
         if constexpr (SCALED) sc[it % RING] = O::ld(p.scale, m);
       }
     };
@@ -286,7 +286,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
             y[e] = (relu && !(y[e] > 0.f)) ? 0.f : y[e];
             if constexpr (MODE == EPI_FAST_RES) y[e] += O::elem(rr[it % RING], e);
           }
-          O::st4(p.C, (int64_t)row_of(pass, it) * p.ldc + n, O::pack(y));
+          O::st4_once(p.C, (int64_t)row_of(pass, it) * p.ldc + n, O::pack(y));
         }
         // the batch's slots are free: fetch the rows RING further on
 #pragma unroll

@@ -115,6 +115,13 @@ struct Out {
   __device__ static void st4(void* p, int64_t i, Vec v) {
     *reinterpret_cast<Vec*>(static_cast<uint16_t*>(p) + i) = v;
   }
+  // read / write once: non-temporal (the residual and C of the fast epilogue)
+  __device__ static Vec ld4_once(const void* p, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(static_cast<const uint16_t*>(p) + i));
+  }
+  __device__ static void st4_once(void* p, int64_t i, Vec v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(static_cast<uint16_t*>(p) + i));
+  }
   __device__ static float elem(Vec v, int e) {
     return to_f32<OT>((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
   }
@@ -134,6 +141,12 @@ struct Out<DT_F32> {
   }
   __device__ static void st4(void* p, int64_t i, Vec v) {
     *reinterpret_cast<Vec*>(static_cast<float*>(p) + i) = v;
+  }
+  __device__ static Vec ld4_once(const void* p, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(static_cast<const float*>(p) + i));
+  }
+  __device__ static void st4_once(void* p, int64_t i, Vec v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(static_cast<float*>(p) + i));
   }
   __device__ static float elem(Vec v, int e) { return v[e]; }
   __device__ static Vec pack(const float (&y)[4]) { return Vec{y[0], y[1], y[2], y[3]}; }

@@ -96,8 +96,10 @@ __global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmAr
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool ok = n < p.N && kb + j < p.K;
-      const u32x2 v =
-          *reinterpret_cast<const u32x2*>(p.B + (ok ? (int64_t)(kb + j) * p.ldb + n : 0));
+      // B is read exactly once: non-temporal loads keep it from displacing
+      // cache lines that are reused
+      const u32x2 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2*>(p.B + (ok ? (int64_t)(kb + j) * p.ldb + n : 0)));
       bq[s][j] = ok ? v : u32x2{0u, 0u};
     }
   };

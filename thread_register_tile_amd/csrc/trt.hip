@@ -285,30 +285,32 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-// Plain streaming read of x (n 16-byte words): each workgroup XORs the words
-// it reads (grid-stride, four independent loads in flight per lane, marked
-// non-temporal) and writes one 16-byte digest; the XOR of all digests is the
-// XOR of all words.  A memory-bound yardstick for the streaming GEMM.
+// Plain streaming read of x (n 16-byte words): every wave reads runs of 128
+// consecutive words (2 KiB, two non-temporal loads per lane) in turn, the
+// runs dealt round-robin over all waves of the grid, and XORs what it read;
+// each workgroup writes one 16-byte digest, so the XOR of all digests is the
+// XOR of all words.  A memory-bound yardstick for the streaming kernels.
 constexpr int kReadProbeBlocks = 2048;
 __global__ __launch_bounds__(256) void hbm_read_kernel(const trt::u32x4* __restrict__ x, int64_t n,
                                                        trt::u32x4* sink) {
   __shared__ trt::u32x4 part[4];
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t runs = n / 128;
   trt::u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    trt::u32x4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&x[i + u * stride]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u];
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < runs; r += (int64_t)gridDim.x * 4) {
+    const trt::u32x4 v0 = __builtin_nontemporal_load(&x[128 * r + lane]);
+    const trt::u32x4 v1 = __builtin_nontemporal_load(&x[128 * r + 64 + lane]);
+    acc ^= v0 ^ v1;
   }
-  for (; i < n; i += stride) acc ^= x[i];
+  // the words after the last whole run, one per thread of the grid
+  for (int64_t i = 128 * runs + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    acc ^= x[i];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] ^= __shfl_xor(acc[e], off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  if (lane == 0) part[wave] = acc;
   __syncthreads();
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
