@@ -475,7 +475,14 @@ def dma_kc_slot(r, g):
 
 
 def dma_mn_slot(R, k, c):
-    sm = (6 * _bit(k, 0)) ^ (12 * _bit(k, 1))
+    """Slot of chunk c (8 rows) of k row k in a rows-contiguous operand tile of
+    R rows.  With a multiple of 16 chunks per k row the chunk is XOR-ed with
+    6*k0 ^ 12*k1; with 24 chunks (R = 192) the XOR must stay inside aligned
+    groups of 8 chunks: 6*k0 ^ 4*k1."""
+    if (R // 8) % 16 == 0:
+        sm = (6 * _bit(k, 0)) ^ (12 * _bit(k, 1))
+    else:
+        sm = (6 * _bit(k, 0)) ^ (4 * _bit(k, 1))
     return k * (R // 8) + (c ^ sm)
 
 

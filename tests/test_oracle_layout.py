@@ -310,7 +310,22 @@ def test_owner_runs_of_four_columns():
 
 # ---- direct-to-LDS tiles ---------------------------------------------------------
 
-@pytest.mark.parametrize("R", [128, 256])
+def test_non_power_of_two_tile_owned_exactly_once():
+    # the 256x192 pipelined tile: 2x2 waves of 128x96, 4x3 fragments of 32x32;
+    # its ownership is integer-affine, not GF(2)-linear, so it is checked by
+    # enumeration ("My Triton From Scratch, Part 16: Register Tiles", section
+    # "A strided ownership rule")
+    cfg = (256, 192, 32, 2, 2, 32)
+    regs = L.gemm_regs_per_lane(cfg)
+    assert regs == 192
+    seen = set()
+    for w in range(4):
+        for l in range(64):
+            for r in range(regs):
+                seen.add(L.gemm_c_owner(cfg, r, l, w))
+    assert len(seen) == 256 * 192 and seen == {(i, j) for i in range(256) for j in range(192)}
+
+@pytest.mark.parametrize("R", [128, 192, 256])
 def test_dma_slots_bijective(R):
     assert sorted(L.dma_kc_slot(r, g) for r in range(R) for g in range(4)) == list(range(4 * R))
     assert sorted(L.dma_mn_slot(R, k, c) for k in range(32) for c in range(R // 8)) \
@@ -328,7 +343,7 @@ def _conflicts_bytes(addr_bytes, window):
     return max(len(v) for v in banks.values())
 
 
-@pytest.mark.parametrize("R", [128, 256])
+@pytest.mark.parametrize("R", [128, 192, 256])
 def test_dma_kc_fragment_reads_conflict_free(R):
     # 32x32x16 operand read: lane l reads row rbase + l%32, chunk g = 2s + l//32
     for rbase in range(0, R, 32):
@@ -339,7 +354,7 @@ def test_dma_kc_fragment_reads_conflict_free(R):
                     assert _conflicts_bytes(lanes[q:q + n], window) == 1
 
 
-@pytest.mark.parametrize("R", [128, 256])
+@pytest.mark.parametrize("R", [128, 192, 256])
 def test_dma_mn_transposed_reads_conflict_free(R):
     # transposing read: lane l (group gq = l//16, l16 = l%16) reads 8 bytes at
     # k row 8*(gq//2) + 4h + l16//4, columns c0 + 16*(gq%2) + 4*(l16%4)
