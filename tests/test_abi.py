@@ -140,7 +140,9 @@ def test_tile_table():
 
 
 ALL_TILES = [(16, 64, 32, 1, 1, 16), (64, 64, 64, 2, 2, 16), (128, 128, 64, 2, 2, 16),
-             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 2, 32), (16, 64, 256, 8, 1, 16)]
+             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 2, 32), (256, 192, 32, 2, 2, 32),
+             (16, 64, 256, 8, 1, 16)]
+NON_GF2 = (256, 192, 32, 2, 2, 32)   # 3 fragment columns per wave: affine ownership
 SKINNY = (16, 64, 256, 8, 1, 16)
 
 
@@ -163,8 +165,13 @@ def test_c_owner_matches_oracle(cfg):
     assert np.array_equal(rows, exp[:, 0]) and np.array_equal(cols, exp[:, 1])
     # exactly once over the tile
     assert len(set(zip(rows.tolist(), cols.tolist()))) == cfg[0] * cfg[1]
-    rank, ib, ob = trt.layout_rank(tile)
-    assert rank == ib == ob == L.log2_exact(cfg[0] * cfg[1])
+    if cfg == NON_GF2:
+        with pytest.raises(trt.TrtError) as e:
+            trt.layout_rank(tile)
+        assert e.value.status == trt.ERR_UNSUPPORTED
+    else:
+        rank, ib, ob = trt.layout_rank(tile)
+        assert rank == ib == ob == L.log2_exact(cfg[0] * cfg[1])
 
 
 @pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (256, 256, 64, 2, 2),
@@ -192,16 +199,19 @@ def test_layout_dump_host_errors():
     assert trt.layout_size(trt.MAP_C_OWNER, (48, 64, 32)) == -1
 
 
-def test_dma_slot_maps_match_oracle():
-    tile = (256, 256, 32)
-    for mid, R in [(trt.MAP_DMA_KC_SLOT_A, 256), (trt.MAP_DMA_KC_SLOT_B, 256)]:
+@pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32)])
+def test_dma_slot_maps_match_oracle(tile):
+    for mid, R in [(trt.MAP_DMA_KC_SLOT_A, tile[0]), (trt.MAP_DMA_KC_SLOT_B, tile[1])]:
         slot, _ = trt.layout_dump_host(mid, tile)
         assert slot.tolist() == [L.dma_kc_slot(r, g) for r in range(R) for g in range(4)]
-    for mid, R in [(trt.MAP_DMA_MN_SLOT_A, 256), (trt.MAP_DMA_MN_SLOT_B, 256)]:
+    for mid, R in [(trt.MAP_DMA_MN_SLOT_A, tile[0]), (trt.MAP_DMA_MN_SLOT_B, tile[1])]:
         slot, _ = trt.layout_dump_host(mid, tile)
         assert slot.tolist() == [L.dma_mn_slot(R, k, c) for k in range(32) for c in range(R // 8)]
+
     # not defined for tiles without the 32-wide K step
     assert trt.layout_size(trt.MAP_DMA_KC_SLOT_A, (256, 256, 64)) == -1
+    # the 256x192 tile has no generic-kernel copy maps
+    assert all(trt.layout_size(m, (256, 192, 32)) == -1 for m in range(1, 7))
     # the streaming tile has only its ownership map
     assert trt.layout_size(trt.MAP_C_OWNER, (16, 64, 256)) == 1024
     assert all(trt.layout_size(m, (16, 64, 256)) == -1 for m in range(1, 11))

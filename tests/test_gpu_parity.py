@@ -78,7 +78,7 @@ def test_mfma_probe_one_hot():
 # ---- device layout maps == host maps (== oracle, checked on the CPU) ----------
 
 @pytest.mark.parametrize("tile", [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64),
-                                  (256, 256, 32), (16, 64, 256)])
+                                  (256, 256, 32), (256, 192, 32), (16, 64, 256)])
 def test_layout_dump_device_equals_host(tile):
     for mid in range(11):
         if trt.layout_size(mid, tile) < 0:
@@ -91,7 +91,8 @@ def test_layout_dump_device_equals_host(tile):
 
 # ---- small shapes, every compiled instance, full comparison ---------------------
 
-TILES = [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64), (256, 256, 32)]
+TILES = [(16, 64, 32), (64, 64, 64), (128, 128, 64), (256, 256, 64), (256, 256, 32),
+         (256, 192, 32)]
 
 
 def small_case(tile, dtype, opA, opB, pad, epi, seed, dist="uniform"):
@@ -100,9 +101,10 @@ def small_case(tile, dtype, opA, opB, pad, epi, seed, dist="uniform"):
     if BM == 256:
         M, N, K = BM + 37, BN + 19, 2 * BK + 9
     if BK == 32 and BM == 256:
-        # the pipelined kernel: k-contiguous operands need K % 8 == 0; a
-        # partial last K step and ragged M, N edges remain
-        M, N, K = 2 * BM + 37, BN + 19, 5 * BK + 8
+        # the pipelined kernel: k-contiguous operands need K % 8 == 0, rows-
+        # contiguous ones M or N % 8 == 0; a partial last K step and ragged M,
+        # N edges remain
+        M, N, K = 2 * BM + 40, BN + 24, 5 * BK + 8
     lda = (M if opA else K) + pad
     ldb = (K if opB else N) + pad
     return W.Workload(f"small{tile}", M, N, K, opA=opA, opB=opB, lda=lda, ldb=ldb,
@@ -177,6 +179,42 @@ def test_pipelined_tile_ragged_shapes():
         run.launch()
         assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
                       what=f"M={M} N={N} K={K} op={opA}{opB} dt={dt}")
+
+
+def test_pipelined_192_tile_ragged_shapes():
+    # the 256x192 tile (3 fragment columns per wave, integer-affine ownership)
+    # on ragged shapes, all four storage combinations, both dtypes, with and
+    # without the epilogue, and one tile grid wider than 192 columns by 8
+    rng = np.random.default_rng(19)
+    for trial in range(20):
+        M = 8 * int(rng.integers(1, 90))
+        N = 8 * int(rng.integers(1, 90)) if trial else 192 * 3 + 8
+        K = 8 * int(rng.integers(1, 40))
+        opA, opB = trial % 2, (trial // 2) % 2
+        dt = W.F16 if trial % 3 else W.BF16
+        a_cols = M if opA else K
+        b_cols = K if opB else N
+        w = W.Workload("dma192", M, N, K, opA=opA, opB=opB,
+                       lda=a_cols + 8 * (trial % 2), ldb=b_cols + 8 * ((trial // 3) % 2),
+                       dtype=dt, dist="ternary", seed=5000 + trial,
+                       bias=bool(trial % 2), relu=bool(trial % 4 == 1),
+                       residual=bool(trial % 3 == 0), row_scale=bool(trial % 5 == 2),
+                       tile=(256, 192, 32))
+        run = Run(w, ldc=N + 4 * (trial % 3))
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
+                      what=f"M={M} N={N} K={K} op={opA}{opB} dt={dt}")
+
+
+def test_tile_choice_uses_192_for_ragged():
+    # 4000 x 3072: 256x256 tiles would leave 64 of 256 compute units idle;
+    # the library picks 256x192 (all four storages give the same answer)
+    w = W.RAGGED
+    run = Run(w)
+    run.launch(tile=None)
+    C = run.result()
+    ms, ns = sample_cells(w, 300, seed=3)
+    assert_accept(C[ms, ns], reference_cells(w, run.host, ms, ns), w.dtype, what="ragged auto")
 
 
 def test_streaming_tile_shapes():

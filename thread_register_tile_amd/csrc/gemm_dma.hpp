@@ -86,15 +86,18 @@ struct DmaOperand {
   static constexpr int BYTES = R * 64;                   // one stage of this operand
   static_assert(CHUNKS % TL::THREADS == 0, "whole copy iterations");
   static_assert(KC || R >= 128, "the rows-contiguous swizzle needs 16 chunks per k row");
-  // the slot maps are GF(2)-linear bijections and their derived inverses
-  // undo them exactly
-  static_assert(TL::template slot_maps_linear<R>(), "linear, bijective slot maps");
-  static_assert(gf2::equal(gf2::compose(TL::template kc_slot_inv<R>, TL::template kc_slot_lin<R>()),
-                           gf2::identity(ilog2(R) + 2)) &&
-                    gf2::equal(gf2::compose(TL::template mn_slot_inv<R>,
-                                            TL::template mn_slot_lin<R>()),
-                               gf2::identity(ilog2(R / 8) + 5)),
+  // power-of-two R: the slot maps are GF(2)-linear bijections and their
+  // derived inverses undo them exactly; any R: the inverses are exact
+  static_assert(!is_pow2(R) || TL::template slot_maps_linear<R>(), "linear, bijective slot maps");
+  static_assert(!is_pow2(R) ||
+                    (gf2::equal(gf2::compose(TL::template kc_slot_inv<R>,
+                                             TL::template kc_slot_lin<R>()),
+                                gf2::identity(ilog2(R) + 2)) &&
+                     gf2::equal(gf2::compose(TL::template mn_slot_inv<R>,
+                                             TL::template mn_slot_lin<R>()),
+                                gf2::identity(ilog2(R / 8) + 5))),
                 "derived inverse slot maps");
+  static_assert(TL::template slot_inverses_exact<R>(), "inverse slot maps");
 
   const char* base;      // operand base address
   int64_t extent;        // operand extent in bytes
@@ -162,7 +165,7 @@ struct FragReader {
 #pragma unroll
       for (int f = 0; f < F; ++f) {
         const int c = (rbase + 32 * f) / 8 + 2 * (gq & 1) + ((l16 & 3) >> 1);
-        addr[f] = region + 16 * (k * (R / 8) + (c ^ TL::mn_swz(k))) + 8 * (l16 & 1);
+        addr[f] = region + 16 * (k * (R / 8) + (c ^ TL::template mn_swz<R>(k))) + 8 * (l16 & 1);
       }
     }
   }
@@ -199,43 +202,69 @@ struct FragReader {
 // EPI_MASKED masks and stores every element on its own.
 enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4 };
 
+// The store phase works on items: one item is a row of one column panel,
+// PANEL columns wide (the whole tile row when BN is a power of two, else 64
+// columns), handled by PANEL / 4 threads that own 4 consecutive columns
+// each.  Iteration `it` of a thread covers panel it % PANELS of staged row
+// (it / PANELS) * ROWS_PER_STEP + t / T_PER_ROW: a thread walks the panels
+// of one row before moving on, so the panel of every iteration -- and the
+// bias it needs -- is known at compile time.
+template <class TL>
+struct EpiShape {
+  static constexpr int BN = TL::BN;
+  static constexpr int PANEL = is_pow2(BN) ? BN : 64;
+  static constexpr int PANELS = BN / PANEL;
+  static constexpr int COLS_PER_T = 4;
+  static constexpr int T_PER_ROW = PANEL / COLS_PER_T;
+  static constexpr int ROWS_PER_STEP = TL::THREADS / T_PER_ROW;
+  static constexpr int HALF_ROWS = TL::BM / 2;        // staged rows per pass
+  static constexpr int ITERS = HALF_ROWS / ROWS_PER_STEP * PANELS;
+  static_assert(BN % PANEL == 0 && TL::THREADS % T_PER_ROW == 0 &&
+                    HALF_ROWS % ROWS_PER_STEP == 0,
+                "whole rows per step");
+};
+
 template <class TL, int OT, int MODE_>
 __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
                                                 const f32x16 (&acc)[TL::FM][TL::FN],
                                                 float* stage, int m0, int n0, int t,
-                                                const float (&bias)[4]) {
+                                                const float (&bias)[EpiShape<TL>::PANELS][4]) {
   using O = Out<OT>;
+  using ES = EpiShape<TL>;
   constexpr int MODE = MODE_ & 3;                      // EPI_MASKED / EPI_FAST / EPI_FAST_RES
   constexpr bool SCALED = (MODE_ & EPI_SCALED) != 0;   // fast modes: row scale present
   constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
   constexpr int PITCH = BN + 4;                       // floats per staged row
-  constexpr int HALF_ROWS = TL::BM / 2;               // rows per pass
-  constexpr int COLS_PER_T = 4;
-  constexpr int T_PER_ROW = BN / COLS_PER_T;          // threads across a row
-  constexpr int ROWS_PER_IT = TL::THREADS / T_PER_ROW;
-  constexpr int ITERS = HALF_ROWS / ROWS_PER_IT;
-  constexpr int BATCH = 8;                            // rows read ahead of their stores
+  constexpr int HALF_ROWS = ES::HALF_ROWS;
+  constexpr int PANELS = ES::PANELS, T_PER_ROW = ES::T_PER_ROW;
+  constexpr int ITERS = ES::ITERS;
+  constexpr int BATCH = 8;                            // items read ahead of their stores
   static_assert(FM % 2 == 0 && TL::WM == 2, "two passes over the wave rows");
   static_assert(ITERS % BATCH == 0, "whole batches");
   const int lane = t & 63, wave = t >> 6;
   const int wr = wave / TL::WN, wc = wave % TL::WN;
-  const int col = COLS_PER_T * (t % T_PER_ROW);       // this thread's 4 columns
-  const int n = n0 + col;
+  const int tcol = ES::COLS_PER_T * (t % T_PER_ROW);  // this thread's 4 columns in a panel
   const bool relu = p.relu != 0;
   const bool scaled = p.scale != nullptr;
+  // iteration it -> staged row, panel, tile column (the panel is a
+  // compile-time constant once the loops are unrolled)
+  auto prow_of = [&](int it) { return (it / PANELS) * ES::ROWS_PER_STEP + t / T_PER_ROW; };
+  auto col_of = [&](int it) { return (it % PANELS) * ES::PANEL + tcol; };
+  auto bias_of = [&](int it, int e) { return bias[it % PANELS][e]; };
   // staged row -> tile row: the wave row block, then the pass's half of it
   auto tile_row = [&](int pass, int prow) {
     return (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
            prow % (HALF_ROWS / TL::WM);
   };
-  // Residuals and row scales travel in a ring of RING rows per thread: 64
-  // registers of residual (a whole pass for 16-bit outputs, half a pass for
-  // binary32).  Row `it` is loaded when its slot frees, i.e. right after row
-  // it - RING was used, so each load has at least one batch of stores ahead
-  // of it; the first RING rows are loaded before the staging writes.
-  constexpr int RING = O::BYTES == 2 ? ITERS : ITERS / 2;
-  static_assert(RING % BATCH == 0 && ITERS % RING == 0, "whole batches per ring");
-  auto row_of = [&](int pass, int it) { return m0 + tile_row(pass, it * ROWS_PER_IT + t / T_PER_ROW); };
+  // Residuals and row scales travel in a ring of RING items per thread, at
+  // most 64 registers of residual (the whole pass for 16-bit outputs, up to
+  // 16 items for binary32).  Item `it` is loaded when its slot frees, i.e.
+  // right after item it - RING was used, so each load has at least one batch
+  // of stores ahead of it; the first RING items are loaded before the
+  // staging writes.
+  constexpr int RING = O::BYTES == 2 ? ITERS : (ITERS < 16 ? ITERS : 16);
+  static_assert(RING >= BATCH, "a batch fits the ring");
+  auto row_of = [&](int pass, int it) { return m0 + tile_row(pass, prow_of(it)); };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     typename O::Vec rr[MODE == EPI_FAST_RES ? RING : 1];
@@ -243,7 +272,8 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     auto fetch = [&](int it) {
       if constexpr (MODE != EPI_MASKED) {
         const int m = row_of(pass, it);
-        if constexpr (MODE == EPI_FAST_RES) rr[it % RING] = O::ld4_once(p.R, (int64_t)m * p.ldr + n);
+        if constexpr (MODE == EPI_FAST_RES)
+          rr[it % RING] = O::ld4_once(p.R, (int64_t)m * p.ldr + n0 + col_of(it));
         if constexpr (SCALED) sc[it % RING] = O::ld(p.scale, m);
       }
     };
@@ -272,8 +302,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
         f32x4 v[BATCH];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
-          v[i] = *reinterpret_cast<const f32x4*>(
-              stage + ((b0 + i) * ROWS_PER_IT + t / T_PER_ROW) * PITCH + col);
+          v[i] = *reinterpret_cast<const f32x4*>(stage + prow_of(b0 + i) * PITCH + col_of(b0 + i));
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
           const int it = b0 + i;
@@ -282,25 +311,25 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
           for (int e = 0; e < 4; ++e) {
             // an absent bias is -0, an exact identity (-0 included), so no
             // select is needed
-            y[e] = (SCALED ? v[i][e] * sc[it % RING] : v[i][e]) + bias[e];
+            y[e] = (SCALED ? v[i][e] * sc[it % RING] : v[i][e]) + bias_of(it, e);
             y[e] = (relu && !(y[e] > 0.f)) ? 0.f : y[e];
             if constexpr (MODE == EPI_FAST_RES) y[e] += O::elem(rr[it % RING], e);
           }
-          O::st4_once(p.C, (int64_t)row_of(pass, it) * p.ldc + n, O::pack(y));
+          O::st4_once(p.C, (int64_t)row_of(pass, it) * p.ldc + n0 + col_of(it), O::pack(y));
         }
-        // the batch's slots are free: fetch the rows RING further on
+        // the batch's slots are free: fetch the items RING further on
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
           if (b0 + i + RING < ITERS) fetch(b0 + i + RING);
       }
     } else {
-      const bool vec = p.epi_vec && n + 4 <= p.N;
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
-        const int prow = it * ROWS_PER_IT + t / T_PER_ROW;
-        const int m = m0 + tile_row(pass, prow);
+        const int m = row_of(pass, it);
+        const int n = n0 + col_of(it);
         if (m >= p.M) continue;
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow * PITCH + col);
+        const bool vec = p.epi_vec && n + 4 <= p.N;
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow_of(it) * PITCH + col_of(it));
         float y[4] = {a4[0], a4[1], a4[2], a4[3]};
         if (scaled) {
           const float s = O::ld(p.scale, m);
@@ -308,7 +337,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
           for (int e = 0; e < 4; ++e) y[e] *= s;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] += bias[e];
+        for (int e = 0; e < 4; ++e) y[e] += bias_of(it, e);
         if (relu) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = y[e] > 0.f ? y[e] : 0.f;
@@ -337,19 +366,26 @@ template <class TL, int OT>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x16 (&acc)[TL::FM][TL::FN],
                                              float* stage, int m0, int n0, int t) {
   using O = Out<OT>;
-  const int n = n0 + 4 * (t % (TL::BN / 4));          // this thread's 4 columns
-  const bool vec = p.epi_vec && n + 4 <= p.N;
-  // -0 when there is no bias: x + (-0) == x for every x, -0 included
-  float bias[4] = {-0.f, -0.f, -0.f, -0.f};
-  if (p.bias) {
-    if (vec) {
-      const auto bb = O::ld4(p.bias, n);
+  using ES = EpiShape<TL>;
+  // the bias of this thread's 4 columns in every panel; -0 where there is
+  // none: x + (-0) == x for every x, -0 included
+  float bias[ES::PANELS][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bias[e] = O::elem(bb, e);
-    } else {
+  for (int q = 0; q < ES::PANELS; ++q) {
+    const int n = n0 + q * ES::PANEL + ES::COLS_PER_T * (t % ES::T_PER_ROW);
+    const bool vec = p.epi_vec && n + 4 <= p.N;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < p.N) bias[e] = O::ld(p.bias, n + e);
+    for (int e = 0; e < 4; ++e) bias[q][e] = -0.f;
+    if (p.bias) {
+      if (vec) {
+        const auto bb = O::ld4(p.bias, n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias[q][e] = O::elem(bb, e);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) bias[q][e] = O::ld(p.bias, n + e);
+      }
     }
   }
   if (!(p.epi_vec && n0 + TL::BN <= p.N && m0 + TL::BM <= p.M))

@@ -284,7 +284,13 @@ struct Tile {
   static constexpr int G = BK / 8;
   static constexpr int KSUB = BK / 32;  // matrix-core k steps per K step
 
-  static_assert(is_pow2(BM) && is_pow2(BN) && is_pow2(BK), "power-of-two tiles");
+  // Power-of-two tiles have a GF(2)-linear ownership map; a tile with a
+  // non-power-of-two number of fragments per wave (BN = 192: 3 fragments of
+  // 32 columns) has an integer-affine one ("My Triton From Scratch, Part 16:
+  // Register Tiles", section "A strided ownership rule").
+  static constexpr bool POW2 = is_pow2(BM) && is_pow2(BN) && is_pow2(FM) && is_pow2(FN);
+  static_assert(is_pow2(BM) && is_pow2(BK) && (is_pow2(BN) || BN % 64 == 0),
+                "power-of-two BM and BK; BN a power of two or a multiple of 64");
   static_assert(is_pow2(WM) && is_pow2(WN), "power-of-two wave grid");
   static_assert(MF == 16 || MF == 32, "16x16 or 32x32 fragments");
   static_assert(WTM >= MF && WTN >= MF && WTM % MF == 0 && WTN % MF == 0,
@@ -307,7 +313,25 @@ struct Tile {
     return (wave % WN) * WTN + MF * fn + in_frag;
   }
 
-  // ---- the same ownership as GF(2) bases -----------------------------------
+  // Exactly-once ownership by enumeration, for any tile: every (register,
+  // lane, wave) lands inside the tile and no element is reached twice; with
+  // REGS * 64 * WAVES == BM * BN that also means every element is reached.
+  static constexpr bool owner_exactly_once() {
+    if (REGS * 64 * WAVES != BM * BN) return false;
+    uint64_t seen[BM * BN / 64] = {};
+    for (int w = 0; w < WAVES; ++w)
+      for (int l = 0; l < 64; ++l)
+        for (int r = 0; r < REGS; ++r) {
+          const int row = owner_row(r, l, w), col = owner_col(r, l, w);
+          if (row < 0 || row >= BM || col < 0 || col >= BN) return false;
+          const int i = row * BN + col;
+          if ((seen[i >> 6] >> (i & 63)) & 1u) return false;
+          seen[i >> 6] |= uint64_t(1) << (i & 63);
+        }
+    return true;
+  }
+
+  // ---- the same ownership as GF(2) bases (power-of-two tiles) ---------------
   // Input bits, low to high: register bits, 6 lane bits, wave bits.
   static constexpr int REG_BITS = ilog2(REGS);
   static constexpr int WAVE_BITS = ilog2(WAVES);
@@ -352,7 +376,7 @@ struct Tile {
     return true;
   }
 
-  static_assert(c_map().bijective(),
+  static_assert(!POW2 || c_map().bijective(),
                 "C ownership must cover every tile element exactly once");
   // The exhaustive owner_matches_bases() check runs once per compiled tile,
   // in the library's tile registry.
@@ -395,15 +419,25 @@ struct Tile {
   }
   template <int R>
   static constexpr gf2::Lin kc_slot_inv = gf2::inverse(kc_slot_lin<R>());
+  // (For a non-power-of-two R the slot map is affine, not GF(2)-linear: its
+  // inverse is the integer one, row = s / 4, chunk = (s mod 4) XOR sk(row).)
   template <int R>
   TRT_HD static int kc_slot_row(int s) {
-    constexpr gf2::Lin inv = kc_slot_inv<R>;
-    return (int)(gf2::apply_n<ilog2(R) + 2>(inv, (uint32_t)s) >> 2);
+    if constexpr (is_pow2(R)) {
+      constexpr gf2::Lin inv = kc_slot_inv<R>;
+      return (int)(gf2::apply_n<ilog2(R) + 2>(inv, (uint32_t)s) >> 2);
+    } else {
+      return s >> 2;
+    }
   }
   template <int R>
   TRT_HD static int kc_slot_g(int s) {
-    constexpr gf2::Lin inv = kc_slot_inv<R>;
-    return (int)(gf2::apply_n<ilog2(R) + 2>(inv, (uint32_t)s) & 3u);
+    if constexpr (is_pow2(R)) {
+      constexpr gf2::Lin inv = kc_slot_inv<R>;
+      return (int)(gf2::apply_n<ilog2(R) + 2>(inv, (uint32_t)s) & 3u);
+    } else {
+      return (s & 3) ^ kc_swz(s >> 2);
+    }
   }
   // rows-contiguous operand, [32 k rows][R/8 chunks of 8 rows]: chunk (k, c)
   // in slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*k0 XOR 12*k1 in the bits of k.
@@ -411,9 +445,18 @@ struct Tile {
   // per 16 lanes, 64 bytes of each per 32 lanes.  sm sends the four rows to
   // four distinct 32-byte slots of a 128-byte window (bits 1-2) and four
   // distinct 64-byte slots of a 256-byte window (bits 2-3).
-  TRT_HD static int mn_swz(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 12 : 0); }
+  // With 24 chunks per k row (R = 192) the XOR has to stay inside aligned
+  // groups of 8 chunks: sm(k) = 6*k0 XOR 4*k1, which still sends the four
+  // rows of a read to distinct bank groups (k0 and k1 flip different bits
+  // of the chunk, and rows of the same k0 sit 8 chunks apart in a 256-byte
+  // window only when k1 also differs).
   template <int R>
-  TRT_HD static int mn_slot(int k, int c) { return k * (R / 8) + (c ^ mn_swz(k)); }
+  TRT_HD static int mn_swz(int k) {
+    return (R / 8) % 16 == 0 ? (((k & 1) ? 6 : 0) ^ ((k & 2) ? 12 : 0))
+                             : (((k & 1) ? 6 : 0) ^ ((k & 2) ? 4 : 0));
+  }
+  template <int R>
+  TRT_HD static int mn_slot(int k, int c) { return k * (R / 8) + (c ^ mn_swz<R>(k)); }
   // The inverse, slot -> (k, chunk), derived like kc_slot_inv: the slot map
   // as a GF(2) map of (c, k) bits (chunk bits low, then 5 k bits), inverted.
   template <int R>
@@ -427,13 +470,30 @@ struct Tile {
   static constexpr gf2::Lin mn_slot_inv = gf2::inverse(mn_slot_lin<R>());
   template <int R>
   TRT_HD static int mn_slot_k(int s) {
-    constexpr gf2::Lin inv = mn_slot_inv<R>;
-    return (int)(gf2::apply_n<ilog2(R / 8) + 5>(inv, (uint32_t)s) >> ilog2(R / 8));
+    if constexpr (is_pow2(R)) {
+      constexpr gf2::Lin inv = mn_slot_inv<R>;
+      return (int)(gf2::apply_n<ilog2(R / 8) + 5>(inv, (uint32_t)s) >> ilog2(R / 8));
+    } else {
+      return s / (R / 8);
+    }
   }
   template <int R>
   TRT_HD static int mn_slot_c(int s) {
-    constexpr gf2::Lin inv = mn_slot_inv<R>;
-    return (int)(gf2::apply_n<ilog2(R / 8) + 5>(inv, (uint32_t)s) & ((1u << ilog2(R / 8)) - 1u));
+    if constexpr (is_pow2(R)) {
+      constexpr gf2::Lin inv = mn_slot_inv<R>;
+      return (int)(gf2::apply_n<ilog2(R / 8) + 5>(inv, (uint32_t)s) & ((1u << ilog2(R / 8)) - 1u));
+    } else {
+      return (s % (R / 8)) ^ mn_swz<R>(s / (R / 8));
+    }
+  }
+  // For any R: the inverse maps undo the forward maps on every slot.
+  template <int R>
+  static constexpr bool slot_inverses_exact() {
+    for (int s = 0; s < 4 * R; ++s) {
+      if (kc_slot(kc_slot_row<R>(s), kc_slot_g<R>(s)) != s) return false;
+      if (mn_slot<R>(mn_slot_k<R>(s), mn_slot_c<R>(s)) != s) return false;
+    }
+    return true;
   }
   // The derivations hold only if the slot maps are GF(2)-linear bijections:
   // checked on every input.

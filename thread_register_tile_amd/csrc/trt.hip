@@ -34,6 +34,7 @@ using trt::GemmArgs;
 // ---- compiled tiles ------------------------------------------------------------
 
 using trt::Tile256;
+using trt::Tile256x192D;
 using trt::Tile256D;
 using trt::Tile64;
 using trt::Tile128;
@@ -89,6 +90,17 @@ template <class TL>
 TRT_HD int64_t map_size(int map) {
   if constexpr (!HasCopyMaps<TL>::value) {
     return map == TRT_MAP_C_OWNER ? (int64_t)TL::WAVES * 64 * TL::REGS : -1;
+  } else if constexpr (!TL::POW2) {
+    // (BK == 32 for every such tile)
+    // a tile of the pipelined kernel only: its ownership and slot maps
+    switch (map) {
+      case TRT_MAP_C_OWNER: return (int64_t)TL::WAVES * 64 * TL::REGS;
+      case TRT_MAP_DMA_KC_SLOT_A: return (int64_t)TL::BM * 4;
+      case TRT_MAP_DMA_KC_SLOT_B: return (int64_t)TL::BN * 4;
+      case TRT_MAP_DMA_MN_SLOT_A: return (int64_t)32 * (TL::BM / 8);
+      case TRT_MAP_DMA_MN_SLOT_B: return (int64_t)32 * (TL::BN / 8);
+      default: return -1;
+    }
   } else {
   constexpr bool dma = TL::BK == 32;
   using KA = typename TL::template KContig<TL::BM>;
@@ -150,10 +162,18 @@ TRT_HD void eval_map(int map, int64_t x, int& r, int& c) {
       r = TL::lds_slot((int)(x / TL::G), (int)(x % TL::G));
       c = 0;
       return;
-    case TRT_MAP_COPY_KCONTIG_A: eval_kcontig<TL, typename TL::template KContig<TL::BM>>(x, r, c); return;
-    case TRT_MAP_COPY_MNCONTIG_A: eval_mncontig<TL, typename TL::template MNContig<TL::BM>>(x, r, c); return;
-    case TRT_MAP_COPY_KCONTIG_B: eval_kcontig<TL, typename TL::template KContig<TL::BN>>(x, r, c); return;
-    case TRT_MAP_COPY_MNCONTIG_B: eval_mncontig<TL, typename TL::template MNContig<TL::BN>>(x, r, c); return;
+    case TRT_MAP_COPY_KCONTIG_A:
+      if constexpr (TL::POW2) eval_kcontig<TL, typename TL::template KContig<TL::BM>>(x, r, c);
+      return;
+    case TRT_MAP_COPY_MNCONTIG_A:
+      if constexpr (TL::POW2) eval_mncontig<TL, typename TL::template MNContig<TL::BM>>(x, r, c);
+      return;
+    case TRT_MAP_COPY_KCONTIG_B:
+      if constexpr (TL::POW2) eval_kcontig<TL, typename TL::template KContig<TL::BN>>(x, r, c);
+      return;
+    case TRT_MAP_COPY_MNCONTIG_B:
+      if constexpr (TL::POW2) eval_mncontig<TL, typename TL::template MNContig<TL::BN>>(x, r, c);
+      return;
     case TRT_MAP_DMA_KC_SLOT_A:
     case TRT_MAP_DMA_KC_SLOT_B:
       r = TL::kc_slot((int)(x / 4), (int)(x % 4));
@@ -248,20 +268,39 @@ constexpr int tile_mf() {
   else return TL::MF;
 }
 
+template <class TL>
+constexpr bool tile_is_gf2() {
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return true;
+  else return TL::POW2;
+}
+
+template <class TL>
+constexpr bool ownership_checked() {
+  if constexpr (std::is_same_v<TL, trt::SkinnyTile>) return TL::owner_matches_bases();
+  else if constexpr (TL::POW2) return TL::owner_matches_bases();
+  else return TL::owner_exactly_once();
+}
+
 template <class TL, bool DMA = false>
 constexpr TileEntry entry() {
-  static_assert(TL::owner_matches_bases(),
-                "kernel ownership arithmetic must equal its GF(2) bases");
-  return TileEntry{TL::BM, TL::BN, tile_bk<TL>(), tile_wm<TL>(), tile_wn<TL>(), TL::REGS,
-                   tile_mf<TL>(),
-                   launcher<TL, DMA>(), &size_host<TL>,
-                   &eval_host<TL>, &dump_launch<TL>,
-                   TL::c_map().rank(), TL::C_IN_BITS, trt::ilog2(TL::BM * TL::BN)};
+  // power-of-two tiles: the kernel's ownership arithmetic equals its GF(2)
+  // bases (whose full rank is asserted in layout.hpp); other tiles: every
+  // element owned exactly once, by enumeration
+  static_assert(ownership_checked<TL>(), "kernel ownership: exactly once");
+  if constexpr (tile_is_gf2<TL>())
+    return TileEntry{TL::BM, TL::BN, tile_bk<TL>(), tile_wm<TL>(), tile_wn<TL>(), TL::REGS,
+                     tile_mf<TL>(), launcher<TL, DMA>(), &size_host<TL>, &eval_host<TL>,
+                     &dump_launch<TL>, TL::c_map().rank(), TL::C_IN_BITS,
+                     trt::ilog2(TL::BM * TL::BN)};
+  else
+    return TileEntry{TL::BM, TL::BN, tile_bk<TL>(), tile_wm<TL>(), tile_wn<TL>(), TL::REGS,
+                     tile_mf<TL>(), launcher<TL, DMA>(), &size_host<TL>, &eval_host<TL>,
+                     &dump_launch<TL>, -1, -1, -1};
 }
 
 const TileEntry kTiles[] = {entry<TileTiny>(), entry<Tile64>(), entry<Tile128>(),
                             entry<Tile256>(), entry<Tile256D, true>(),
-                            entry<trt::SkinnyTile>()};
+                            entry<Tile256x192D, true>(), entry<trt::SkinnyTile>()};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 const TileEntry* find_tile(const trt_tile* t) {
@@ -270,15 +309,26 @@ const TileEntry* find_tile(const trt_tile* t) {
   return nullptr;
 }
 
-// Tile choice when the caller names none: the largest tile that still gives
-// the 256 compute units a full wave of workgroups; a 16-row tile when M is
-// that small.
+const TileEntry* tile_named(int bm, int bn, int bk) {
+  const trt_tile t{bm, bn, bk};
+  return find_tile(&t);
+}
+
+// Tile choice when the caller names none.  M <= 16: the streaming tile.
+// Otherwise, when either pipelined tile gives the 256 compute units a full
+// wave of workgroups, the one that needs the least work per compute unit:
+// rounds of 256 workgroups times the tile's area (the 256x192 tile fills
+// all compute units where 256x256 tiles would leave some idle).  Smaller
+// problems take the generic kernel on 128x128 or 64x64 tiles.
 const TileEntry* choose_tile(int64_t M, int64_t N) {
-  auto count = [&](const TileEntry& e) { return ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn); };
-  if (M <= 16) return &kTiles[5];
-  if (count(kTiles[4]) >= 192) return &kTiles[4];
-  if (count(kTiles[2]) >= 128) return &kTiles[2];
-  return &kTiles[1];
+  auto count = [&](const TileEntry* e) { return ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn); };
+  auto cost = [&](const TileEntry* e) { return (count(e) + 255) / 256 * e->bm * e->bn; };
+  if (M <= 16) return tile_named(16, 64, 256);
+  const TileEntry* big = tile_named(256, 256, 32);
+  const TileEntry* wide = tile_named(256, 192, 32);
+  if (count(big) >= 192 || count(wide) >= 192) return cost(wide) < cost(big) ? wide : big;
+  if (count(tile_named(128, 128, 64)) >= 128) return tile_named(128, 128, 64);
+  return tile_named(64, 64, 64);
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -560,6 +610,9 @@ trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank, int32_t* in_bits
   if (!tile) return fail(TRT_ERR_NULL, "tile must be non-null");
   const TileEntry* e = find_tile(tile);
   if (!e) return fail(TRT_ERR_UNSUPPORTED, "no compiled kernel for the requested tile");
+  if (e->rank < 0)
+    return fail(TRT_ERR_UNSUPPORTED,
+                "this tile's ownership is integer-affine, not GF(2)-linear; it has no rank");
   if (rank) *rank = e->rank;
   if (in_bits) *in_bits = e->in_bits;
   if (out_bits) *out_bits = e->out_bits;
