@@ -22,7 +22,7 @@ from . import build as _build
 
 F16 = 1
 BF16 = 2
-F32 = 3          # output / epilogue-operand dtype only
+F32 = 3          # binary32: inputs, outputs, epilogue operands
 
 _lib = None
 
@@ -122,14 +122,15 @@ def gemm_block(M, N, K, A, lda, opA, B, ldb, opB, in_dtype, bias=None,
                m_range=None, n_range=None, threads=None) -> np.ndarray:
     """fp64 reference of the block m_range x n_range of epilogue(A.B).
 
-    A, B are flat uint16 buffers of raw bits of `in_dtype`; scale [M], bias
+    A, B are flat buffers of raw bits of `in_dtype` (uint16, or uint32 for
+    F32); scale [M], bias
     [N] and R are flat buffers of raw bits of the output dtype (uint32 for
     F32), addressed exactly as the library addresses them (leading
     dimensions in elements, explicit op flags).  Returns an
     (m_hi-m_lo, n_hi-n_lo) float64 array, unrounded.
     """
     od = out_dtype or in_dtype
-    A = _u16(A, "A"); B = _u16(B, "B")
+    A = _raw(A, "A", in_dtype); B = _raw(B, "B", in_dtype)
     bias = _raw(bias, "bias", od); R = _raw(R, "R", od); scale = _raw(scale, "scale", od)
     m_lo, m_hi = m_range if m_range is not None else (0, M)
     n_lo, n_hi = n_range if n_range is not None else (0, N)
@@ -149,7 +150,7 @@ def gemm_cells(M, N, K, A, lda, opA, B, ldb, opB, in_dtype, ms, ns, bias=None,
                threads=None) -> np.ndarray:
     """fp64 reference of the scattered cells (ms[i], ns[i]), one by one."""
     od = out_dtype or in_dtype
-    A = _u16(A, "A"); B = _u16(B, "B")
+    A = _raw(A, "A", in_dtype); B = _raw(B, "B", in_dtype)
     bias = _raw(bias, "bias", od); R = _raw(R, "R", od); scale = _raw(scale, "scale", od)
     ms = np.ascontiguousarray(ms, dtype=np.int64)
     ns = np.ascontiguousarray(ns, dtype=np.int64)

@@ -21,7 +21,8 @@
  * dtype: binary16, bfloat16 or binary32.
  *
  * The oracle takes the sum in fp64 instead of fp32: every product of two
- * 16-bit floats is exact in fp64, and the k order is ascending for every
+ * 16-bit floats is exact in fp64 (of two binary32 values, within one fp64
+ * rounding), and the k order is ascending for every
  * cell, so the result does not depend on thread count or loop nesting.
  * Build with -O2 -ffp-contract=off and without fast-math so that no fused
  * multiply-add or reassociation changes a single rounding.
@@ -162,14 +163,16 @@ void orc_decode_array(const void* h, double* out, int64_t n, int dtype) {
 
 /* ---- the GEMM and its epilogue ------------------------------------------ */
 
-static double elem_a(const uint16_t* A, int64_t lda, int opA, int64_t m,
+/* Operand elements: binary16 / bfloat16 patterns, or binary32 words when
+ * in_dt is ORC_F32. */
+static double elem_a(const void* A, int64_t lda, int opA, int64_t m,
                      int64_t k, int dt) {
-  return decode(opA ? A[k * lda + m] : A[m * lda + k], dt);
+  return decode_at(A, opA ? k * lda + m : m * lda + k, dt);
 }
 
-static double elem_b(const uint16_t* B, int64_t ldb, int opB, int64_t k,
+static double elem_b(const void* B, int64_t ldb, int opB, int64_t k,
                      int64_t n, int dt) {
-  return decode(opB ? B[n * ldb + k] : B[k * ldb + n], dt);
+  return decode_at(B, opB ? n * ldb + k : k * ldb + n, dt);
 }
 
 /* Epilogue of one cell, in fp64: y = acc; y *= scale(m); y += bias(n);
@@ -196,8 +199,8 @@ static double epilogue(double acc, int64_t m, int64_t n, const void* scale,
  * inner loop does not change the order of any single cell's sum.
  * Returns 0, or -1 on an argument error.
  */
-int orc_gemm_block(int64_t M, int64_t N, int64_t K, const uint16_t* A,
-                   int64_t lda, int opA, const uint16_t* B, int64_t ldb,
+int orc_gemm_block(int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, int opA, const void* B, int64_t ldb,
                    int opB, int in_dt, const void* scale, const void* bias,
                    int relu, const void* R, int64_t ldr, int out_dt, int64_t m_lo,
                    int64_t m_hi, int64_t n_lo, int64_t n_hi, double* out,
@@ -235,8 +238,8 @@ int orc_gemm_block(int64_t M, int64_t N, int64_t K, const uint16_t* A,
 /* Reference values of scattered cells (ms[i], ns[i]), one by one, with the
  * same per-cell order (k ascending).  Used to sample outputs of shapes too
  * large for a full oracle run. */
-int orc_gemm_cells(int64_t M, int64_t N, int64_t K, const uint16_t* A,
-                   int64_t lda, int opA, const uint16_t* B, int64_t ldb,
+int orc_gemm_cells(int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, int opA, const void* B, int64_t ldb,
                    int opB, int in_dt, const void* scale, const void* bias,
                    int relu, const void* R, int64_t ldr, int out_dt,
                    const int64_t* ms, const int64_t* ns, int64_t count,

@@ -407,3 +407,42 @@ def test_accept_rule_f32_output():
     nan = bits.copy()
     nan[0, 0] = 0x7FC00000
     assert not oracle.accept(nan, Cref, F32)["ok"]
+
+
+# ---- binary32 inputs ------------------------------------------------------------
+
+def f32_bits(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32).view(np.uint32))
+
+
+def test_f32_inputs_identity_and_ones():
+    rng = np.random.default_rng(23)
+    A = rng.standard_normal((5, 7)).astype(np.float32)
+    C = gemm(5, 7, 7, f32_bits(A), f32_bits(np.eye(7)), dt=F32, out_dtype=F32)
+    assert np.array_equal(C, A.astype(np.float64))
+    C = gemm(3, 4, 11, f32_bits(np.ones((3, 11))), f32_bits(np.ones((11, 4))), dt=F32)
+    assert np.array_equal(C, np.full((3, 4), 11.0))
+
+
+def test_f32_inputs_brute_force():
+    rng = np.random.default_rng(24)
+    M, N, K = 4, 5, 9
+    a = rng.uniform(-3, 3, (M, K)).astype(np.float32)
+    b = rng.uniform(-3, 3, (K, N)).astype(np.float32)
+    C = gemm(M, N, K, f32_bits(a), f32_bits(b), dt=F32, out_dtype=F32)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(a[m, k])) * Fraction(float(b[k, n])) for k in range(K))
+            # each binary32 product is exact in fp64 up to its 48-bit width; K additions
+            bound = 2 * K * 2.0 ** -53 * sum(abs(float(a[m, k]) * float(b[k, n])) for k in range(K))
+            assert abs(Fraction(C[m, n]) - exact) <= Fraction(bound)
+
+
+def test_f32_transposed_storage_bit_identical():
+    rng = np.random.default_rng(25)
+    a = rng.standard_normal((6, 8)).astype(np.float32)
+    b = rng.standard_normal((8, 5)).astype(np.float32)
+    base = gemm(6, 5, 8, f32_bits(a), f32_bits(b), dt=F32, out_dtype=F32)
+    t = gemm(6, 5, 8, f32_bits(a.T.copy()), f32_bits(b.T.copy()), opA=1, opB=1, dt=F32,
+             out_dtype=F32)
+    assert np.array_equal(base, t)
