@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s (fp16→fp32 acc) at 4096³ + % of MFMA peak (rocprof)"
-PEAK_TFLOPS = {1: 2516.6, 2: 2516.6}   # dense f16 / bf16 matrix-core peak
+PEAK_TFLOPS = {1: 2516.6, 2: 2516.6, 3: 157.3}   # dense f16 / bf16 / f32 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 WORKLOADS = ("square", "epilogue", "ragged", "skinny")
@@ -360,7 +360,7 @@ def main():
         roofline["rocprof_mfma"] = {"tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
                                     "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
                                     "flops_counted": m["flops_per_launch"]}
-    if not args.no_mfma_loop and w.name != "skinny":
+    if not args.no_mfma_loop and w.name != "skinny" and w.dtype != W.F32:
         a_rows = host["A"].reshape(w.a_rows, w.lda_)[:, :w.a_cols].reshape(-1)   # no padding
         ml = mfma_loop_tflops(trt, torch, a_rows, w.dtype, kern_ms, args.warmup + args.steps)
         roofline["mfma_loop_tflops"] = round(ml, 1)

@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 5
+#define TRT_ABI_VERSION 6
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -44,9 +44,10 @@ typedef enum {
   TRT_ERR_ARG = 9          /* any other invalid argument (op flag, map id...)  */
 } trt_status;
 
-/* Element types.  Inputs (A, B) are IEEE binary16 or bfloat16; the output
- * C and the epilogue operands (bias, residual, row scale), which share the
- * output dtype, may also be IEEE binary32. */
+/* Element types: IEEE binary16, bfloat16 or binary32, for the inputs (A and
+ * B share one dtype) and, independently, for the output C and the epilogue
+ * operands (bias, residual, row scale), which share the output dtype.
+ * binary32 inputs run on their own 128x128x32 tile. */
 typedef enum { TRT_F16 = 1, TRT_BF16 = 2, TRT_F32 = 3 } trt_dtype;
 
 /* Storage of an operand.  An operand is never transposed implicitly
@@ -94,11 +95,10 @@ typedef struct {
  * writes never overlap each other.  C's byte range must not meet the byte
  * range of A, B, bias, residual or row_scale -- an in-place residual is
  * rejected, since safety that cannot be proven is an error.  A, B, C must be
- * non-NULL; A and B 2-byte aligned, C and the epilogue operands aligned to
- * the output element (2 or 4 bytes).  in_dtype is TRT_F16 or TRT_BF16;
- * out_dtype is TRT_F16, TRT_BF16 or TRT_F32, independently of in_dtype
- * (otherwise TRT_ERR_DTYPE).  Elements of C outside [0,M) x [0,N) (the ldc padding) are never
- * written.  Elements of A and B outside the logical operands (the lda/ldb
+ * non-NULL; A and B aligned to the input element, C and the epilogue operands
+ * to the output element (2 or 4 bytes).  in_dtype and out_dtype are each
+ * TRT_F16, TRT_BF16 or TRT_F32 (otherwise TRT_ERR_DTYPE).  Elements of C
+ * outside [0,M) x [0,N) (the ldc padding) are never written.  Elements of A and B outside the logical operands (the lda/ldb
  * padding) never influence C, and no byte outside an operand's extent
  * ((rows-1)*ld + cols elements from its base) is ever read.
  *
@@ -117,7 +117,10 @@ trt_status trt_gemm(int64_t M, int64_t N, int64_t K,
 /*
  * trt_gemm_tiled -- trt_gemm with an explicit workgroup tile.  tile must name
  * a compiled instance (see trt_tile_at); otherwise TRT_ERR_UNSUPPORTED and
- * nothing is enqueued.  tile == NULL behaves as trt_gemm.
+ * nothing is enqueued.  tile == NULL behaves as trt_gemm.  With binary32
+ * inputs the tile must be NULL or 128x128x32: that path has one kernel, a
+ * 2x2-wave tile of 16x16x4 f32 matrix-core fragments, double-buffered
+ * through LDS (not listed by trt_tile_at).
  */
 trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K,
                           const void* A, int64_t lda, int32_t opA,

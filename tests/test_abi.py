@@ -71,8 +71,8 @@ def test_valid_call():
     (dict(ldc=63), trt.ERR_STRIDE),
     (dict(A=0), trt.ERR_NULL), (dict(B=0), trt.ERR_NULL), (dict(C=0), trt.ERR_NULL),
     (dict(A=BASE + 1), trt.ERR_ALIGN), (dict(C=BASE * 3 + 1), trt.ERR_ALIGN),
-    (dict(in_dtype=3, out_dtype=3), trt.ERR_DTYPE),
-    (dict(in_dtype=trt.F32, out_dtype=trt.F32), trt.ERR_DTYPE),
+    (dict(in_dtype=4, out_dtype=3), trt.ERR_DTYPE),
+    (dict(in_dtype=0, out_dtype=trt.F16), trt.ERR_DTYPE),
     (dict(opA=2), trt.ERR_ARG), (dict(opB=-1), trt.ERR_ARG),
     # C overlapping an input: any byte in common is an error
     (dict(C=BASE + 64 * 2), trt.ERR_OVERLAP),
@@ -105,6 +105,13 @@ def test_in_place_residual_rejected():
 def test_overlapping_input_rows_are_legal():
     # lda smaller than the row: rows overlap, which is fine for inputs
     assert status(lda=1) == trt.OK
+
+
+def test_workgroup_count_limit():
+    # a 2^30 x 2^30 output is 2^44 tiles of 256x256: more than one launch holds
+    big = 1 << 30
+    assert status(M=big, N=big, ldc=big, C=1 << 40) == trt.ERR_SIZE
+    assert status(M=big, N=64, ldc=64, C=1 << 40) == trt.OK
 
 
 def test_unknown_tile_rejected():
@@ -265,8 +272,31 @@ def test_output_dtypes_accepted():
     for i in (trt.F16, trt.BF16):
         for o in (trt.F16, trt.BF16, trt.F32):
             assert status(in_dtype=i, out_dtype=o) == trt.OK, (i, o)
-    assert status(in_dtype=trt.F32, out_dtype=trt.F32) == trt.ERR_DTYPE
     assert status(in_dtype=trt.F16, out_dtype=4) == trt.ERR_DTYPE
+
+
+def test_f32_inputs_accepted():
+    # binary32 operands with every output dtype
+    for o in (trt.F16, trt.BF16, trt.F32):
+        assert status(in_dtype=trt.F32, out_dtype=o) == trt.OK, o
+    assert status(in_dtype=trt.F32, out_dtype=trt.F32, tile=(128, 128, 32)) == trt.OK
+
+
+def test_f32_inputs_alignment_extent_and_tile():
+    # A and B are aligned to the 4-byte input element
+    assert status(in_dtype=trt.F32, A=BASE + 2) == trt.ERR_ALIGN
+    assert status(in_dtype=trt.F32, B=BASE * 2 + 2) == trt.ERR_ALIGN
+    assert status(in_dtype=trt.F16, A=BASE + 2) == trt.OK
+    # A of 4-byte elements spans 4*(63*32 + 32) bytes
+    assert status(in_dtype=trt.F32, C=BASE + 4 * 2048) == trt.OK
+    assert status(in_dtype=trt.F32, C=BASE + 4 * 2048 - 2) == trt.ERR_OVERLAP
+    # transposed B [N][ldb] of 4-byte elements spans 4*(63*ldb + 32)
+    assert status(in_dtype=trt.F32, opB=1, ldb=32, C=BASE * 2 + 4 * (63 * 32 + 32)) == trt.OK
+    assert status(in_dtype=trt.F32, opB=1, ldb=32,
+                  C=BASE * 2 + 4 * (63 * 32 + 32) - 4) == trt.ERR_OVERLAP
+    # binary32 operands run on the 128x128x32 tile only
+    assert status(in_dtype=trt.F32, tile=(256, 256, 32)) == trt.ERR_UNSUPPORTED
+    assert status(in_dtype=trt.F32, tile=(16, 64, 32)) == trt.ERR_UNSUPPORTED
 
 
 def test_f32_output_alignment_and_extent():

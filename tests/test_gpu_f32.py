@@ -1,0 +1,112 @@
+"""GPU parity of the GEMM on binary32 operands against the oracle.
+
+The register-tile GEMM of "My Triton From Scratch, Part 16: Register Tiles"
+computes in f32 throughout (section "What Version 16 does not optimize");
+the library runs it on the f32 matrix cores with the same fused epilogue
+("Named layouts", section "Contract").  Exact mode (integer operands) must be
+bit-exact; random operands meet |C - Cref| <= 1e-2 + 1e-2 |Cref|.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import thread_register_tile_amd as trt
+import workloads as W
+from gpu_util import Run, assert_accept, reference_block, reference_cells, sample_cells
+
+pytestmark = pytest.mark.gpu
+
+F32_TILE = (128, 128, 32)
+
+
+def f32_case(M, N, K, opA, opB, pad, epi, seed, dist="uniform", out_dtype=W.F32):
+    lda = (M if opA else K) + pad
+    ldb = (K if opB else N) + pad
+    return W.Workload("f32-small", M, N, K, opA=opA, opB=opB, lda=lda, ldb=ldb, dtype=W.F32,
+                      out_dtype=out_dtype, bias=epi, relu=epi, residual=epi,
+                      row_scale=epi, dist=dist, scale=1.0, seed=seed)
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("pad", [0, 4, 3])   # 3: rows not 16-byte aligned -> element loads
+def test_f32_inputs_ragged_tolerance(ops, pad):
+    # several tiles, ragged M and N, a partial last K step
+    w = f32_case(2 * 128 + 37, 2 * 128 + 19, 3 * 32 + 9, ops[0], ops[1], pad,
+                 epi=(ops[0] + pad) % 2 == 0, seed=200 + pad)
+    run = Run(w)
+    run.launch()
+    assert_accept(run.result(), reference_block(w, run.host), W.F32, what=f"{ops} pad={pad}")
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("odt", [W.F32, W.F16, W.BF16])
+def test_f32_inputs_exact_mode(ops, odt):
+    # integer operands: every partial sum is exact in f32, so C is bit-exact
+    w = f32_case(128 + 45, 3 * 128 + 7, 4 * 32 + 20, ops[0], ops[1], 4, True, seed=210,
+                 dist="ternary", out_dtype=odt)
+    run = Run(w, ldc=w.N + 4)
+    run.launch()
+    assert_accept(run.result(), reference_block(w, run.host), odt, exact=True,
+                  what=f"{ops} out={odt}")
+
+
+def test_f32_inputs_random_shapes_exact():
+    rng = np.random.default_rng(23)
+    for trial in range(16):
+        M, N = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+        K = int(rng.integers(1, 200))
+        opA, opB = trial % 2, (trial // 2) % 2
+        w = f32_case(M, N, K, opA, opB, int(rng.integers(0, 6)), bool(trial % 3), seed=300 + trial,
+                     dist="ternary")
+        run = Run(w, ldc=N + trial % 5)
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), W.F32, exact=True,
+                      what=f"M={M} N={N} K={K} op={opA}{opB}")
+
+
+def test_f32_inputs_explicit_tile():
+    w = replace(f32_case(130, 70, 40, 0, 0, 0, False, seed=220), tile=F32_TILE)
+    run = Run(w)
+    run.launch()
+    assert_accept(run.result(), reference_block(w, run.host), W.F32, what="explicit tile")
+
+
+def test_f32_binding_with_torch_tensors():
+    import torch
+    g = torch.Generator().manual_seed(5)
+    A = torch.randn(300, 200, generator=g).cuda()
+    B = torch.randn(200, 150, generator=g).cuda()
+    bias = torch.randn(150, generator=g).cuda()
+    C = trt.gemm(A, B, bias=bias, relu=True)
+    assert C.dtype == torch.float32
+    torch.cuda.synchronize()
+    Ab = A.cpu().numpy().view(np.uint32).reshape(-1)
+    Bb = B.cpu().numpy().view(np.uint32).reshape(-1)
+    ref = oracle.gemm_block(300, 150, 200, Ab, 200, 0, Bb, 150, 0, W.F32,
+                            bias=bias.cpu().numpy().view(np.uint32), relu=True, out_dtype=W.F32)
+    assert_accept(C.cpu().numpy().view(np.uint32), ref, W.F32, what="binding")
+
+
+def test_f32square_full_size():
+    w = W.F32SQUARE
+    run = Run(w)
+    run.launch()
+    C = run.result()
+    ms, ns = sample_cells(w, 1500, seed=w.seed)
+    assert_accept(C[ms, ns], reference_cells(w, run.host, ms, ns), W.F32, what="f32square")
+    for m0, n0 in [(0, 0), (w.M - 48, w.N - 80)]:
+        mr, nr = (m0, m0 + 48), (n0, n0 + 80)
+        assert_accept(C[mr[0]:mr[1], nr[0]:nr[1]], reference_block(w, run.host, mr, nr), W.F32,
+                      what="f32square block")
+
+
+def test_f32square_exact_mode():
+    w = replace(W.F32SQUARE, dist="ternary", seed=79)
+    run = Run(w)
+    run.launch()
+    C = run.result()
+    ms, ns = sample_cells(w, 400, seed=3)
+    assert_accept(C[ms, ns], reference_cells(w, run.host, ms, ns), W.F32, exact=True,
+                  what="f32square exact")

@@ -237,7 +237,8 @@ def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, row_sc
     """C = relu((A.B) * row_scale[:, None] + bias) + residual on the GPU, in one kernel.
 
     A is [M, K] (opA="N") or its transpose stored as [K, M] (opA="T"); B is
-    [K, N] (opB="N") or stored as [N, K] (opB="T").  Tensors may be
+    [K, N] (opB="N") or stored as [N, K] (opB="T"); A and B share one dtype,
+    float16, bfloat16 or float32.  Tensors may be
     row-padded views (unit inner stride, any row stride).  bias is [N],
     row_scale [M], residual [M, N], all of the output dtype: out's dtype if
     out is given, else out_dtype (a torch dtype: float16, bfloat16 or

@@ -1,0 +1,145 @@
+// gemm_f32.hpp -- the GEMM on binary32 operands for gfx950.
+//
+// The pages' register-tile GEMM computes in f32 on general-purpose lanes ("My
+// Triton From Scratch, Part 16: Register Tiles", section "What Version 16
+// does not optimize"); on gfx950 binary32 products run on the matrix cores as
+// v_mfma_f32_16x16x4_f32.  Workgroup tile 128x128 with a K step of 32, 2x2
+// waves of 64x64, 4x4 fragments of 16x16: the ownership map and the fused
+// epilogue are those of the generic kernel's 16x16 tiles (Tile<128, 128, 32,
+// 2, 2, 16>), so it reuses epilogue_store.
+//
+// Operand tiles are staged k-contiguous in LDS, A as [128 m][32 k] and B as
+// [128 n][32 k], rows padded to 36 floats so that the 16 lanes reading one k
+// group of 16 rows hit 16 distinct 16-byte bank groups.  Matrix-core step kk
+// (0..7) of a K step takes k = 8*(lane/16) + kk: each lane reads its 8 k of
+// a fragment row as two 16-byte LDS loads.  Storage with k contiguous in
+// global memory is copied as 16-byte vectors; storage with m (or n)
+// contiguous is loaded as 16-byte vectors along m and written to LDS
+// transposed, one element at a time.  Out-of-range rows and k are zero.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace trt {
+
+using TileF32 = Tile<128, 128, 32, 2, 2, 16>;
+
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One operand's copy: R rows (m or n) x 32 k per K step.  KC: k contiguous
+// in global memory (element (r, k) at X[r*ld + k]); else (r, k) at X[k*ld + r].
+template <int R, bool KC, bool VEC>
+struct F32Operand {
+  static constexpr int KP = 36;                      // LDS row pitch in floats
+  static constexpr int CH = R * 32 / 4 / 256;        // float4 chunks per thread
+  f32x4 v[CH];
+
+  __device__ __forceinline__ void load(const float* X, int64_t ld, int r0, int rows, int k0,
+                                       int K, int t, bool full) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = t + 256 * i;
+      // KC: chunk = (row, 4 consecutive k); else (k, 4 consecutive rows)
+      const int r = KC ? c / 8 : 4 * (c % (R / 4));
+      const int k = KC ? 4 * (c % 8) : c / (R / 4);
+      const int64_t base = KC ? (int64_t)(r0 + r) * ld + k0 + k : (int64_t)(k0 + k) * ld + r0 + r;
+      if (VEC && full) {
+        v[i] = *reinterpret_cast<const f32x4*>(X + base);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = KC ? (r0 + r < rows && k0 + k + e < K) : (r0 + r + e < rows && k0 + k < K);
+          v[i][e] = ok ? X[base + e] : 0.f;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(float* lds, int t) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = t + 256 * i;
+      if (KC) {
+        *reinterpret_cast<f32x4*>(lds + (c / 8) * KP + 4 * (c % 8)) = v[i];
+      } else {
+        const int r = 4 * (c % (R / 4)), k = c / (R / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds[(r + e) * KP + k] = v[i][e];
+      }
+    }
+  }
+};
+
+template <bool A_KC, bool B_KC, bool VEC>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+  using TL = TileF32;
+  constexpr int KP = 36, BM = TL::BM, BN = TL::BN, FM = TL::FM, FN = TL::FN;
+  static_assert(FM == 4 && FN == 4 && TL::THREADS == 256, "2x2 waves of 4x4 fragments");
+  __shared__ __attribute__((aligned(16))) float lds[2][(BM + BN) * KP];
+  const float* A = reinterpret_cast<const float*>(p.A);
+  const float* B = reinterpret_cast<const float*>(p.B);
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  int tm, tn;
+  tile_of<8>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const bool full_mn = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+
+  F32Operand<BM, A_KC, VEC> a;
+  F32Operand<BN, B_KC, VEC> b;
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (p.K + 31) / 32;
+  auto load_step = [&](int kt) {
+    const int k0 = kt * 32;
+    const bool full = full_mn && k0 + 32 <= p.K;
+    a.load(A, p.lda, m0, p.M, k0, p.K, t, full);
+    b.load(B, p.ldb, n0, p.N, k0, p.K, t, full);
+  };
+  const int wrow = (wave / TL::WN) * TL::WTM, wcol = (wave % TL::WN) * TL::WTN;
+  const int fr = lane & 15, g = lane >> 4;
+
+  load_step(0);
+  a.store(lds[0], t);
+  b.store(lds[0] + BM * KP, t);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_step(kt + 1);
+    const float* la = lds[cur];
+    const float* lb = lds[cur] + BM * KP;
+    f32x4 af[FM][2], bf[FN][2];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        af[i][h] = *reinterpret_cast<const f32x4*>(la + (wrow + 16 * i + fr) * KP + 8 * g + 4 * h);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        bf[j][h] = *reinterpret_cast<const f32x4*>(lb + (wcol + 16 * j + fr) * KP + 8 * g + 4 * h);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mfma16_f32(bf[j][kk / 4][kk % 4], af[i][kk / 4][kk % 4], acc[i][j]);
+    if (kt + 1 < nk) {
+      a.store(lds[cur ^ 1], t);
+      b.store(lds[cur ^ 1] + BM * KP, t);
+    }
+    __syncthreads();
+  }
+  epilogue_store<TL>(p, acc, m0, n0, lane, wave);
+}
+
+}  // namespace trt

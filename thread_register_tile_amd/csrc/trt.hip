@@ -498,8 +498,18 @@ trt_status trt_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
   const trt_status s = trt::validate_gemm(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
                                           out_dtype, epi, msg);
   if (s != TRT_OK) return fail(s, msg);
-  if (tile && !find_tile(tile))
+  if (in_dtype == TRT_F32) {
+    // binary32 operands run on one tile of their own
+    if (tile && !(tile->bm == 128 && tile->bn == 128 && tile->bk == 32))
+      return fail(TRT_ERR_UNSUPPORTED, "binary32 operands run on the 128x128x32 tile only");
+  } else if (tile && !find_tile(tile)) {
     return fail(TRT_ERR_UNSUPPORTED, "no compiled kernel for the requested tile");
+  }
+  // one workgroup per output tile, counted in 32 bits by the launch
+  const TileEntry* e = in_dtype == TRT_F32 ? nullptr : (tile ? find_tile(tile) : choose_tile(M, N));
+  const int64_t bm = e ? e->bm : 128, bn = e ? e->bn : 128;
+  if (((M + bm - 1) / bm) * ((N + bn - 1) / bn) > INT32_MAX)
+    return fail(TRT_ERR_SIZE, "more than 2^31-1 output tiles in one launch");
   g_err.clear();
   return TRT_OK;
 }
@@ -511,7 +521,7 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   const trt_status s =
       trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, tile);
   if (s != TRT_OK) return s;
-  const TileEntry* e = tile ? find_tile(tile) : choose_tile(M, N);
+  const TileEntry* e = in_dtype == TRT_F32 ? nullptr : (tile ? find_tile(tile) : choose_tile(M, N));
 
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(A);
@@ -529,19 +539,24 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   a.K = (int32_t)K;
   a.relu = (epi && epi->relu) ? 1 : 0;
   a.out_dt = out_dtype;
+  const int64_t isz = trt::elem_bytes(in_dtype);
   int64_t sa = 0, sb = 0;
-  trt::span_bytes(opA ? K : M, opA ? M : K, lda, sa);
-  trt::span_bytes(opB ? N : K, opB ? K : N, ldb, sb);
+  trt::span_bytes(opA ? K : M, opA ? M : K, lda, sa, isz);
+  trt::span_bytes(opB ? N : K, opB ? K : N, ldb, sb, isz);
   a.a_bytes = sa;
   a.b_bytes = sb;
   // 16-byte operand vectors need 16-byte aligned bases and rows.
-  const bool vec = aligned(A, 16) && aligned(B, 16) && lda % 8 == 0 && ldb % 8 == 0;
+  const int64_t per16 = 16 / isz;
+  const bool vec = aligned(A, 16) && aligned(B, 16) && lda % per16 == 0 && ldb % per16 == 0;
   // Epilogue vectors of 4 output elements (8 or 16 bytes) need aligned C,
   // bias and residual rows.
   const uintptr_t va = 4 * (uintptr_t)trt::elem_bytes(out_dtype);
   a.epi_vec = aligned(C, va) && ldc % 4 == 0 && (!a.bias || aligned(a.bias, va)) &&
               (!a.R || (aligned(a.R, va) && a.ldr % 4 == 0));
-  e->launch(a, in_dtype, opA, opB, vec, static_cast<hipStream_t>(stream));
+  if (in_dtype == TRT_F32)
+    trt::launch_f32(a, opA, opB, vec, static_cast<hipStream_t>(stream));
+  else
+    e->launch(a, in_dtype, opA, opB, vec, static_cast<hipStream_t>(stream));
   return check_launch("gemm launch");
 }
 

@@ -65,8 +65,8 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
     msg = "opB must be TRT_OP_N or TRT_OP_T";
     return TRT_ERR_ARG;
   }
-  if (in_dtype != TRT_F16 && in_dtype != TRT_BF16) {
-    msg = "in_dtype must be TRT_F16 or TRT_BF16";
+  if (in_dtype != TRT_F16 && in_dtype != TRT_BF16 && in_dtype != TRT_F32) {
+    msg = "in_dtype must be TRT_F16, TRT_BF16 or TRT_F32";
     return TRT_ERR_DTYPE;
   }
   if (out_dtype != TRT_F16 && out_dtype != TRT_BF16 && out_dtype != TRT_F32) {
@@ -88,15 +88,15 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
     msg = "A, B and C must be non-null";
     return TRT_ERR_NULL;
   }
-  // every pointer aligned to its element: 2 bytes for A and B, the output
-  // element for C and the epilogue operands
-  const int64_t osz = elem_bytes(out_dtype);
+  // every pointer aligned to its element: the input element for A and B,
+  // the output element for C and the epilogue operands
+  const int64_t isz = elem_bytes(in_dtype), osz = elem_bytes(out_dtype);
   const void* in_ptrs[2] = {A, B};
   const void* out_ptrs[4] = {C, has_bias ? epi->bias : nullptr, has_res ? epi->residual : nullptr,
                              has_scale ? epi->row_scale : nullptr};
   for (const void* q : in_ptrs)
-    if (reinterpret_cast<uintptr_t>(q) & 1u) {
-      msg = "A and B must be 2-byte aligned";
+    if (reinterpret_cast<uintptr_t>(q) & (uintptr_t)(isz - 1)) {
+      msg = "A and B must be aligned to the input element";
       return TRT_ERR_ALIGN;
     }
   for (const void* q : out_ptrs)
@@ -105,8 +105,8 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
       return TRT_ERR_ALIGN;
     }
   int64_t sa, sb, sc, sr = 0;
-  const bool ok = span_bytes(opA ? K : M, opA ? M : K, lda, sa) &&
-                  span_bytes(opB ? N : K, opB ? K : N, ldb, sb) &&
+  const bool ok = span_bytes(opA ? K : M, opA ? M : K, lda, sa, isz) &&
+                  span_bytes(opB ? N : K, opB ? K : N, ldb, sb, isz) &&
                   span_bytes(M, N, ldc, sc, osz) &&
                   (!has_res || span_bytes(M, N, epi->ldr, sr, osz));
   if (!ok) {

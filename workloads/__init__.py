@@ -22,7 +22,7 @@ import numpy as np
 
 F16 = 1
 BF16 = 2
-F32 = 3                 # output / epilogue-operand type only
+F32 = 3                 # binary32
 DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32"}
 ELEM_BYTES = {F16: 2, BF16: 2, F32: 4}
 
@@ -40,7 +40,7 @@ class Workload:
     lda: Optional[int] = None
     ldb: Optional[int] = None
     ldc: Optional[int] = None
-    dtype: int = F16       # input type of A and B
+    dtype: int = F16       # input type of A and B (F16, BF16 or F32)
     out_dtype: Optional[int] = None   # output type (C, bias, residual, row scale); None: dtype
     row_scale: bool = False
     bias: bool = False
@@ -94,7 +94,7 @@ class Workload:
     @property
     def algorithmic_bytes(self):
         o = ELEM_BYTES[self.odt]
-        b = 2 * (self.M * self.K + self.K * self.N) + o * self.M * self.N
+        b = ELEM_BYTES[self.dtype] * (self.M * self.K + self.K * self.N) + o * self.M * self.N
         if self.bias:
             b += o * self.N
         if self.residual:
@@ -122,7 +122,12 @@ SKINNY = Workload("skinny", 16, 16384, 16384, dtype=F16, dist="normal",
 ROWSCALE = Workload("rowscale", 8192, 8192, 4096, dtype=BF16, out_dtype=F32, row_scale=True,
                     bias=True, relu=True, residual=True, dist="uniform", scale=1.0, seed=6)
 
-CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY, ROWSCALE)}
+# The square shape with binary32 operands and output: the register-tile dot
+# of "My Triton From Scratch, Part 12: CUDA Tile Layouts" computes in f32
+# throughout (section "What Version 16 does not optimize").
+F32SQUARE = Workload("f32square", 4096, 4096, 4096, dtype=F32, dist="normal", scale=8.0, seed=8)
+
+CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY, ROWSCALE, F32SQUARE)}
 
 
 def shrink(w: Workload, M=None, N=None, K=None, **kw) -> Workload:
@@ -187,7 +192,7 @@ def _padded(w: Workload, tensor_id: int, rows: int, cols: int, ld: int, dtype=No
 
 
 def make_inputs(w: Workload) -> dict:
-    """Raw host buffers for a workload: A, B (flat uint16 of the input type)
+    """Raw host buffers for a workload: A, B (flat raw bits of the input type)
     and, if enabled, bias [N], residual [M, N] (leading dimension N) and row
     scale [M] (flat, of the output type: uint16, or uint32 for F32)."""
     out = {
