@@ -150,8 +150,8 @@ def mfma_loop_tflops(trt, torch, host_a, dtype, kern_ms, launches):
     the workload's own A data, each launch sized to last about as long as one
     GEMM launch and run as many times as the GEMM was (warmup + timed)."""
     import numpy as np
-    words = np.resize(host_a, trt.MFMA_PROBE_OPERAND_BYTES // 2)   # repeats a short input
-    ops = torch.from_numpy(words.view(np.int16)).cuda()
+    words = np.resize(host_a, trt.MFMA_PROBE_OPERAND_BYTES // host_a.itemsize)  # repeats a short input
+    ops = torch.from_numpy(words.view(np.int8)).cuda()
     sink = torch.empty(trt.MFMA_PROBE_SINK_BYTES // 4, dtype=torch.float32, device="cuda")
     iters = max(1, int(kern_ms * 1e-3 * 1.8e9 / (32 * 32)))   # 32 products of 32 cycles per round
     stream = torch.cuda.current_stream()
@@ -164,7 +164,7 @@ def mfma_loop_tflops(trt, torch, host_a, dtype, kern_ms, launches):
     e1.record(stream)
     torch.cuda.synchronize()
     s = e0.elapsed_time(e1) / 20 * 1e-3
-    return trt.mfma_loop_probe_flops(iters) / s / 1e12
+    return trt.mfma_loop_probe_flops(iters, dtype) / s / 1e12
 
 
 def bench_reduce(args, trt, torch, np, W):
@@ -360,7 +360,7 @@ def main():
         roofline["rocprof_mfma"] = {"tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
                                     "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
                                     "flops_counted": m["flops_per_launch"]}
-    if not args.no_mfma_loop and w.name != "skinny" and w.dtype != W.F32:
+    if not args.no_mfma_loop and w.name != "skinny":
         a_rows = host["A"].reshape(w.a_rows, w.lda_)[:, :w.a_cols].reshape(-1)   # no padding
         ml = mfma_loop_tflops(trt, torch, a_rows, w.dtype, kern_ms, args.warmup + args.steps)
         roofline["mfma_loop_tflops"] = round(ml, 1)

@@ -347,6 +347,18 @@ def mfma16_c(lane, reg):
     return (4 * (lane // 16) + reg, lane % 16)           # (row, col)
 
 
+# v_mfma_f32_16x16x4_f32: operand A (16 rows x 4 k): lane l holds row l % 16,
+# k = l // 16; operand B (4 k x 16 cols): column l % 16, same k; the result
+# registers are those of the 16x16x32 shape (mfma16_c).
+
+def mfma16f32_a(lane):
+    return (lane % 16, lane // 16)                       # (row, k)
+
+
+def mfma16f32_b(lane):
+    return (lane // 16, lane % 16)                       # (k, col)
+
+
 # v_mfma_f32_32x32x16_{f16,bf16}: operand 0 (32 rows x 16 k): lane l holds
 # row l % 32, k = 8*(l // 32) + e; operand 1 (16 k x 32 cols): column l % 32,
 # same k rule; result (32 x 32): lane l, register r holds row

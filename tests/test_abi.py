@@ -245,7 +245,7 @@ def test_read_probe_rejections(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(ops=0), trt.ERR_NULL), (dict(sink=0), trt.ERR_NULL),
-    (dict(dtype=3), trt.ERR_DTYPE), (dict(iters=0), trt.ERR_ARG),
+    (dict(dtype=4), trt.ERR_DTYPE), (dict(iters=0), trt.ERR_ARG),
     (dict(sink_bytes=trt.MFMA_PROBE_SINK_BYTES - 64), trt.ERR_SIZE),
     (dict(ops=BASE + 8), trt.ERR_ALIGN), (dict(sink=BASE * 8 + 32), trt.ERR_ALIGN),
     (dict(sink=BASE + 4096), trt.ERR_OVERLAP),

@@ -4,9 +4,10 @@ Neither is part of the GEMM; the benchmark reports their rates as context.
 trt_hbm_read_probe (a plain streaming read) is pinned by a property that holds
 at any size: the XOR of the per-workgroup digests equals the XOR of all
 16-byte words read, computed here with numpy.  trt_mfma_loop_probe (matrix
-cores only) is pinned by recomputing every thread's sum of accumulators on
-the host from the operand words and the documented 32x32x16 fragment maps,
-with operands in {-1, 0, 1} so that every fp32 sum is exact.
+cores only) is pinned by recomputing every thread's sums of accumulators on
+the host from the operand words and the documented fragment maps (32x32x16
+for 16-bit types, 16x16x4 for binary32), with operands in {-1, 0, 1} so that
+every fp32 sum is exact.
 """
 import numpy as np
 import pytest
@@ -79,5 +80,33 @@ def test_mfma_loop_probe_sums(dtype):
     assert np.array_equal(got, np.broadcast_to(exp, got.shape))
 
 
+def _fragment_product_f32(r0, r1):
+    """Result registers [64, 4] of one 16x16x4 f32 instruction whose operand
+    0 / operand 1 registers are r0 / r1 ([64] values)."""
+    X = np.zeros((16, 4)); Y = np.zeros((4, 16))
+    for l in range(64):
+        X[L.mfma16f32_a(l)] = r0[l]
+        Y[L.mfma16f32_b(l)] = r1[l]
+    D = X @ Y
+    return np.array([[D[L.mfma16_c(l, r)] for r in range(4)] for l in range(64)])
+
+
+def test_mfma_loop_probe_sums_f32():
+    rng = np.random.default_rng(9)
+    vals = rng.integers(-1, 2, size=(1024, 4)).astype(np.float64)   # 1024 words of 4 values
+    ops = torch.from_numpy(W.to_bits(vals, W.F32).view(np.int32).reshape(-1)).cuda()
+    iters = 3
+    sums = trt.mfma_loop_probe(ops, iters, W.F32).cpu().numpy()
+    word = lambda base, i, e: vals[base + 64 * i: base + 64 * i + 64, e]   # [64 lanes]
+    exp = np.zeros((64, 16))
+    for q in range(16):
+        d = (_fragment_product_f32(word(256, q % 4, q // 4), word(0, q // 4, q % 4)) +
+             _fragment_product_f32(word(768, q % 4, q // 4), word(512, q // 4, q % 4)))
+        exp[:, q] = iters * d.sum(axis=1)      # output q: the sum of accumulator q's registers
+    got = sums.reshape(256 * 4, 64, 16)
+    assert np.array_equal(got, np.broadcast_to(exp, got.shape))
+
+
 def test_mfma_loop_probe_flops():
     assert trt.mfma_loop_probe_flops(1) == 1024 * 32 * 32768
+    assert trt.mfma_loop_probe_flops(1, W.F32) == 1024 * 32 * 2048

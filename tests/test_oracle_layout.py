@@ -182,6 +182,15 @@ def test_mfma16_maps_are_bijections():
             assert L.mfma16_a(l, e)[1] == L.mfma16_b(l, e)[0]
 
 
+def test_mfma16f32_maps_are_bijections():
+    a = {L.mfma16f32_a(l) for l in range(64)}
+    b = {L.mfma16f32_b(l) for l in range(64)}
+    assert a == {(i, k) for i in range(16) for k in range(4)}
+    assert b == {(k, j) for k in range(4) for j in range(16)}
+    for l in range(64):
+        assert L.mfma16f32_a(l)[1] == L.mfma16f32_b(l)[0]
+
+
 TILE_CONFIGS = [(16, 64, 32, 1, 1), (64, 64, 64, 2, 2), (128, 128, 64, 2, 2),
                 (256, 256, 64, 2, 2), (256, 128, 64, 2, 2), (128, 256, 64, 2, 2),
                 (256, 256, 64, 2, 4), (256, 256, 32, 2, 2, 32), (128, 128, 32, 2, 2, 32),

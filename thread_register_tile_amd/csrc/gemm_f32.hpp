@@ -8,14 +8,19 @@
 // epilogue are those of the generic kernel's 16x16 tiles (Tile<128, 128, 32,
 // 2, 2, 16>), so it reuses epilogue_store.
 //
-// Operand tiles are staged k-contiguous in LDS, A as [128 m][32 k] and B as
-// [128 n][32 k], rows padded to 36 floats so that the 16 lanes reading one k
-// group of 16 rows hit 16 distinct 16-byte bank groups.  Matrix-core step kk
-// (0..7) of a K step takes k = 8*(lane/16) + kk: each lane reads its 8 k of
-// a fragment row as two 16-byte LDS loads.  Storage with k contiguous in
-// global memory is copied as 16-byte vectors; storage with m (or n)
-// contiguous is loaded as 16-byte vectors along m and written to LDS
-// transposed, one element at a time.  Out-of-range rows and k are zero.
+// Both operand tiles are staged k-contiguous in LDS, A as [128 m][32 k] and
+// B as [128 n][32 k], rows of 32 floats (eight 16-byte chunks) with chunk kc
+// of row r stored at chunk kc ^ sw(r), sw(r) = ((r >> 1) ^ (r >> 3)) & 7.
+// Matrix-core step kk (0..7) of a K step takes k = 8*(lane/16) + kk: each
+// lane reads its 8 k of a fragment row as two 16-byte LDS loads, and the 16
+// lanes of a k group (16 consecutive rows) meet 16 distinct 16-byte bank
+// groups.  Storage with k contiguous in global memory is copied as 16-byte
+// chunks (row c/8, chunk c%8: one row pair per 16 lanes, conflict-free
+// writes).  Storage with m (or n) contiguous is read as a 4x4 block per
+// thread -- four k rows of four consecutive m, the 32 lanes of a half-wave
+// covering 512 contiguous bytes of one k row -- transposed in registers
+// and written as four k-contiguous chunks (two lanes per bank group, the
+// least for rows of one parity).  Out-of-range rows and k are zero.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -28,22 +33,28 @@ __device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// One operand's copy: R rows (m or n) x 32 k per K step.  KC: k contiguous
-// in global memory (element (r, k) at X[r*ld + k]); else (r, k) at X[k*ld + r].
-template <int R, bool KC, bool VEC>
+__device__ __forceinline__ int f32_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 7; }
+
+// Float offset of chunk kc (4 floats of k) of LDS row r.
+__device__ __forceinline__ int f32_slot(int r, int kc) { return r * 32 + 4 * (kc ^ f32_swz(r)); }
+
+// One operand's copy: 128 rows (m or n) x 32 k per K step, four 16-byte
+// chunks per thread.  KC: k contiguous in global memory (element (r, k) at
+// X[r*ld + k]); else (r, k) at X[k*ld + r].
+template <bool KC, bool VEC>
 struct F32Operand {
-  static constexpr int KP = 36;                      // LDS row pitch in floats
-  static constexpr int CH = R * 32 / 4 / 256;        // float4 chunks per thread
-  f32x4 v[CH];
+  static constexpr int R = 128;
+  f32x4 v[4];
 
   __device__ __forceinline__ void load(const float* X, int64_t ld, int r0, int rows, int k0,
                                        int K, int t, bool full) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      // KC: chunk c = (row c/8, k 4*(c%8)..+3); else k row 4*(t/32) + i,
+      // rows 4*(t%32)..+3
       const int c = t + 256 * i;
-      // KC: chunk = (row, 4 consecutive k); else (k, 4 consecutive rows)
-      const int r = KC ? c / 8 : 4 * (c % (R / 4));
-      const int k = KC ? 4 * (c % 8) : c / (R / 4);
+      const int r = KC ? c / 8 : 4 * (t % 32);
+      const int k = KC ? 4 * (c % 8) : 4 * (t / 32) + i;
       const int64_t base = KC ? (int64_t)(r0 + r) * ld + k0 + k : (int64_t)(k0 + k) * ld + r0 + r;
       if (VEC && full) {
         v[i] = *reinterpret_cast<const f32x4*>(X + base);
@@ -59,14 +70,15 @@ struct F32Operand {
 
   __device__ __forceinline__ void store(float* lds, int t) const {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = t + 256 * i;
+    for (int i = 0; i < 4; ++i) {
       if (KC) {
-        *reinterpret_cast<f32x4*>(lds + (c / 8) * KP + 4 * (c % 8)) = v[i];
+        const int c = t + 256 * i;
+        *reinterpret_cast<f32x4*>(lds + f32_slot(c / 8, c % 8)) = v[i];
       } else {
-        const int r = 4 * (c % (R / 4)), k = c / (R / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lds[(r + e) * KP + k] = v[i][e];
+        // row 4*(t%32) + i of the block: element i of each of the four k rows
+        const int r = 4 * (t % 32) + i;
+        const f32x4 w = {v[0][i], v[1][i], v[2][i], v[3][i]};
+        *reinterpret_cast<f32x4*>(lds + f32_slot(r, t / 32)) = w;
       }
     }
   }
@@ -75,9 +87,9 @@ struct F32Operand {
 template <bool A_KC, bool B_KC, bool VEC>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   using TL = TileF32;
-  constexpr int KP = 36, BM = TL::BM, BN = TL::BN, FM = TL::FM, FN = TL::FN;
+  constexpr int BM = TL::BM, BN = TL::BN, FM = TL::FM, FN = TL::FN;
   static_assert(FM == 4 && FN == 4 && TL::THREADS == 256, "2x2 waves of 4x4 fragments");
-  __shared__ __attribute__((aligned(16))) float lds[2][(BM + BN) * KP];
+  __shared__ __attribute__((aligned(16))) float lds[2][(BM + BN) * 32];
   const float* A = reinterpret_cast<const float*>(p.A);
   const float* B = reinterpret_cast<const float*>(p.B);
 
@@ -88,8 +100,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const bool full_mn = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
-  F32Operand<BM, A_KC, VEC> a;
-  F32Operand<BN, B_KC, VEC> b;
+  static_assert(BM == F32Operand<true, true>::R && BN == F32Operand<true, true>::R, "128-row operands");
+  F32Operand<A_KC, VEC> a;
+  F32Operand<B_KC, VEC> b;
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -108,24 +121,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 
   load_step(0);
   a.store(lds[0], t);
-  b.store(lds[0] + BM * KP, t);
+  b.store(lds[0] + BM * 32, t);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_step(kt + 1);
     const float* la = lds[cur];
-    const float* lb = lds[cur] + BM * KP;
+    const float* lb = lds[cur] + BM * 32;
     f32x4 af[FM][2], bf[FN][2];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        af[i][h] = *reinterpret_cast<const f32x4*>(la + (wrow + 16 * i + fr) * KP + 8 * g + 4 * h);
+        af[i][h] = *reinterpret_cast<const f32x4*>(la + f32_slot(wrow + 16 * i + fr, 2 * g + h));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        bf[j][h] = *reinterpret_cast<const f32x4*>(lb + (wcol + 16 * j + fr) * KP + 8 * g + 4 * h);
+        bf[j][h] = *reinterpret_cast<const f32x4*>(lb + f32_slot(wcol + 16 * j + fr, 2 * g + h));
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
           acc[i][j] = mfma16_f32(bf[j][kk / 4][kk % 4], af[i][kk / 4][kk % 4], acc[i][j]);
     if (kt + 1 < nk) {
       a.store(lds[cur ^ 1], t);
-      b.store(lds[cur ^ 1] + BM * KP, t);
+      b.store(lds[cur ^ 1] + BM * 32, t);
     }
     __syncthreads();
   }

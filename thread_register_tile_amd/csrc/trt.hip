@@ -366,10 +366,12 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const trt::u32x4* __restr
 }
 
 // Matrix-core yardstick: every wave of 256 workgroups x 4 waves (one per
-// SIMD) runs `iters` rounds of 32 v_mfma_f32_32x32x16 on operand registers
+// SIMD) runs `iters` rounds of 32 matrix-core products of 32 cycles each
+// (v_mfma_f32_32x32x16 for 16-bit types, v_mfma_f32_16x16x4_f32 for
+// binary32, the instructions the GEMM kernels issue) on operand registers
 // taken from caller data, 16 independent accumulators, nothing else in the
-// loop; each thread then writes the sum of its accumulators (so no product
-// is dead).  Timing it gives the rate the matrix cores sustain on this part
+// loop; each thread then writes sums of its accumulators (so no product is
+// dead).  Timing it gives the rate the matrix cores sustain on this part
 // under the same data and power conditions as the GEMM.
 constexpr int kMfmaProbeBlocks = 256;
 template <int DT>
@@ -383,6 +385,33 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const trt::u32x4* __r
     b[i] = src[256 + i * 64 + lane];
     a1[i] = src[512 + i * 64 + lane];
     b1[i] = src[768 + i * 64 + lane];
+  }
+  if constexpr (DT == trt::DT_F32) {
+    // 16 accumulators of 4 lanes' worth; element e of sum g collects
+    // accumulator 4g + e's register sums
+    trt::f32x4 acc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = trt::f32x4{};
+    // the element goes through a scalar first: a bit cast applied to a
+    // vector subscript directly reads element 0 whatever the index
+    auto f = [](trt::u32x4 v, int e) {
+      const uint32_t w = v[e];
+      return __builtin_bit_cast(float, w);
+    };
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(f(b[q % 4], q / 4), f(a[q / 4], q % 4), acc[q], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(f(b1[q % 4], q / 4), f(a1[q / 4], q % 4), acc[q], 0, 0, 0);
+    }
+    trt::f32x16 out{};
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      out[q] = acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3];
+    sink[(int64_t)blockIdx.x * 256 + t] = out;
+    return;
   }
   trt::f32x16 acc[16];
 #pragma unroll
@@ -684,8 +713,8 @@ trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink, int64_t 
 trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iters, float* sink,
                                int64_t sink_bytes, void* stream) {
   if (!operands || !sink) return fail(TRT_ERR_NULL, "operands and sink must be non-null");
-  if (dtype != TRT_F16 && dtype != TRT_BF16)
-    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16 or TRT_BF16");
+  if (dtype != TRT_F16 && dtype != TRT_BF16 && dtype != TRT_F32)
+    return fail(TRT_ERR_DTYPE, "dtype must be TRT_F16, TRT_BF16 or TRT_F32");
   if (iters < 1) return fail(TRT_ERR_ARG, "iters must be positive");
   if (sink_bytes < TRT_MFMA_PROBE_SINK_BYTES)
     return fail(TRT_ERR_SIZE, "sink must hold TRT_MFMA_PROBE_SINK_BYTES bytes");
@@ -700,6 +729,9 @@ trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iter
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == TRT_F16)
     hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_F16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
+                       iters, dst);
+  else if (dtype == TRT_F32)
+    hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_F32>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
                        iters, dst);
   else
     hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_BF16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,

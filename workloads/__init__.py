@@ -123,7 +123,7 @@ ROWSCALE = Workload("rowscale", 8192, 8192, 4096, dtype=BF16, out_dtype=F32, row
                     bias=True, relu=True, residual=True, dist="uniform", scale=1.0, seed=6)
 
 # The square shape with binary32 operands and output: the register-tile dot
-# of "My Triton From Scratch, Part 12: CUDA Tile Layouts" computes in f32
+# of "My Triton From Scratch, Part 16: Register Tiles" computes in f32
 # throughout (section "What Version 16 does not optimize").
 F32SQUARE = Workload("f32square", 4096, 4096, 4096, dtype=F32, dist="normal", scale=8.0, seed=8)
 
