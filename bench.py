@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s (fp16→fp32 acc) at 4096³ + % of MFMA peak (rocprof)"
 PEAK_TFLOPS = {1: 2516.6, 2: 2516.6, 3: 157.3}   # dense f16 / bf16 / f32 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+# fp32 fused multiply-add on the vector lanes, one per lane per cycle (the
+# library is built without packed fp32): 256 CUs x 4 SIMDs x 16 lanes x 2
+# FLOP x 2.4 GHz
+PEAK_VALU_F32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 WORKLOADS = ("square", "epilogue", "ragged", "skinny")
 
@@ -296,7 +300,18 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
+    def step_regtile():
+        lm, ln, mt = w.regtile
+        trt.gemm_regtile_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, w.opA, B.data_ptr(), w.ldb_,
+                             w.opB, C.data_ptr(), w.ldc_, w.dtype, w.odt, lm, ln, mt,
+                             bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
+                             residual=R.data_ptr() if R is not None else 0,
+                             ldr=w.ldr_ if R is not None else 0,
+                             scale=scale.data_ptr() if scale is not None else 0, stream=sptr)
+
     def step():
+        if w.regtile is not None:
+            return step_regtile()
         trt.gemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, w.opA, B.data_ptr(), w.ldb_, w.opB,
                      C.data_ptr(), w.ldc_, w.dtype, w.odt,
                      bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
@@ -355,12 +370,17 @@ def main():
         roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "tflops": round(achieved, 2)})
+    if w.regtile is not None:
+        roofline.update({"bound": "alu", "peak": round(PEAK_VALU_F32_TFLOPS, 1),
+                         "frac": round(achieved / PEAK_VALU_F32_TFLOPS, 4),
+                         "regtile": {"lm": w.regtile[0], "ln": w.regtile[1],
+                                     "thread_shape": trt.regtile_thread_shape(*w.regtile)}})
     if counters and "mfma" in counters:
         m = counters["mfma"]
         roofline["rocprof_mfma"] = {"tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
                                     "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
                                     "flops_counted": m["flops_per_launch"]}
-    if not args.no_mfma_loop and w.name != "skinny":
+    if not args.no_mfma_loop and w.name != "skinny" and w.regtile is None:
         a_rows = host["A"].reshape(w.a_rows, w.lda_)[:, :w.a_cols].reshape(-1)   # no padding
         ml = mfma_loop_tflops(trt, torch, a_rows, w.dtype, kern_ms, args.warmup + args.steps)
         roofline["mfma_loop_tflops"] = round(ml, 1)
@@ -430,7 +450,9 @@ def main():
                    "out_dtype": W.DTYPE_NAMES[w.odt],
                    "epilogue": {"bias": w.bias, "relu": w.relu, "residual": w.residual,
                                 "row_scale": w.row_scale},
-                   "tile": list(tile) if tile else "auto", "csrc_digest": csrc_digest()},
+                   "tile": (f"vector-lane register tile {w.regtile[0]}x{w.regtile[1]}" if w.regtile
+                            else list(tile) if tile else "auto"),
+                   "csrc_digest": csrc_digest()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,

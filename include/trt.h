@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 7
+#define TRT_ABI_VERSION 8
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -301,6 +301,56 @@ trt_status trt_gf2_sublayout(int32_t nin, int32_t nout, const uint32_t* cols,
  * TRT_ERR_ARG if some value of R is not a value of S. */
 trt_status trt_gf2_invert_and_compose(int32_t r_nin, int32_t t_bits, const uint32_t* r,
                                       int32_t s_nin, const uint32_t* s, uint32_t* q);
+
+/*
+ * Register tiles of any logical shape ("My Triton From Scratch, Part 16:
+ * Register Tiles").  A logical [lm, ln] C tile is computed by a physical
+ * thread shape [tm, tn], each thread holding a register tile of
+ * [lm/tm, ln/tn] accumulators.
+ *
+ * trt_regtile_thread_shape -- the deterministic thread-shape policy (section
+ * "Choosing the physical thread shape"): of the pairs (a, b) with a dividing
+ * lm, b dividing ln and a*b <= max_threads, the largest by (a*b, min(a, b),
+ * b).  max_threads = 32 gives the pages' one-warp results, for example
+ * (3, 17) -> (1, 17) and (16, 32) -> (4, 8); the GEMM below allows up to one
+ * 64-lane wavefront.  Host only.  Errors: TRT_ERR_NULL, TRT_ERR_SIZE (lm or
+ * ln < 1), TRT_ERR_ARG (max_threads < 1).
+ */
+trt_status trt_regtile_thread_shape(int32_t lm, int32_t ln, int32_t max_threads,
+                                    int32_t* tm, int32_t* tn);
+
+/*
+ * trt_regtile_owner -- the strided ownership of a register tile (section "A
+ * strided ownership rule"): thread t = ti*tn + tj, register r = ri*rn + rj
+ * (rn = ln/tn) owns logical (ti + ri*tm, tj + rj*tn); writes rows[x],
+ * cols[x] for x = t*(lm/tm * ln/tn) + r (caller arrays of n = lm*ln) and
+ * checks that every logical element is owned exactly once.  Host only; it
+ * is the map the register-tile GEMM's kernel evaluates.  Errors:
+ * TRT_ERR_SIZE (a shape < 1, lm*ln > 2^24, n != lm*ln), TRT_ERR_ARG (tm does
+ * not divide lm or tn does not divide ln), TRT_ERR_NULL.
+ */
+trt_status trt_regtile_owner(int32_t lm, int32_t ln, int32_t tm, int32_t tn,
+                             int32_t* rows, int32_t* cols, int64_t n);
+
+/*
+ * trt_gemm_regtile -- trt_gemm computed with a register tile of logical
+ * shape [lm, ln] on general-purpose vector lanes instead of the matrix
+ * cores (section "Register-valued loop-carried accumulators"): one 64-lane
+ * wavefront per output tile, thread shape trt_regtile_thread_shape(lm, ln,
+ * max_threads), each thread accumulating its registers with fp32 fused
+ * multiply-adds over K, then the same fused epilogue and rounding as
+ * trt_gemm.  Any positive lm, ln (no power of two needed) with at most 8
+ * registers per axis: lm/tm <= 8 and ln/tn <= 8, otherwise
+ * TRT_ERR_UNSUPPORTED.  max_threads in [1, 64] (TRT_ERR_ARG).  Arguments,
+ * dtypes, validation and errors otherwise as trt_gemm; enqueued on `stream`.
+ */
+trt_status trt_gemm_regtile(int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, int32_t opA,
+                            const void* B, int64_t ldb, int32_t opB,
+                            void* C, int64_t ldc,
+                            int32_t in_dtype, int32_t out_dtype,
+                            const trt_epilogue* epi, int32_t lm, int32_t ln,
+                            int32_t max_threads, void* stream);
 
 /*
  * trt_block_reduce -- the rank-1 block reduction ("My Triton From Scratch,

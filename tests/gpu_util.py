@@ -46,6 +46,17 @@ class Run:
 
     def launch(self, tile=None):
         w = self.w
+        if w.regtile is not None:
+            lm, ln, mt = w.regtile
+            trt.gemm_regtile_raw(
+                w.M, w.N, w.K, self.A.data_ptr(), w.lda_, w.opA, self.B.data_ptr(), w.ldb_,
+                w.opB, self.c_ptr(), self.ldc, w.dtype, w.odt, lm, ln, mt,
+                bias=self.bias.data_ptr() if self.bias is not None else 0, relu=w.relu,
+                residual=self.R.data_ptr() if self.R is not None else 0,
+                ldr=w.ldr_ if self.R is not None else 0,
+                scale=self.scale.data_ptr() if self.scale is not None else 0,
+                stream=torch.cuda.current_stream().cuda_stream)
+            return
         trt.gemm_raw(w.M, w.N, w.K, self.A.data_ptr(), w.lda_, w.opA, self.B.data_ptr(),
                      w.ldb_, w.opB, self.c_ptr(), self.ldc, w.dtype, w.odt,
                      bias=self.bias.data_ptr() if self.bias is not None else 0,

@@ -393,3 +393,72 @@ def test_block_reduce_rejections(kw, code):
         trt.block_reduce_raw(a["x"], a["n"], a["block"], a["dtype"], a["op"], a["out"])
     assert e.value.status == code
     assert trt.last_error() != ""
+
+
+# ---- register tiles of any logical shape ("My Triton From Scratch, Part 16:
+# Register Tiles", sections "Choosing the physical thread shape" and "A strided
+# ownership rule") ---------------------------------------------------------------
+
+def test_regtile_policy_matches_pages(golden):
+    g = golden("dot_policy.json")
+    for out, threads, regs in g["table"]:
+        tm, tn = trt.regtile_thread_shape(out[0], out[1], g["max_threads"])
+        assert (tm, tn) == tuple(threads), out
+        assert (out[0] // tm, out[1] // tn) == tuple(regs), out
+
+
+@pytest.mark.parametrize("max_threads", [1, 6, 32, 64])
+def test_regtile_policy_matches_oracle(max_threads):
+    for lm in range(1, 41):
+        for ln in list(range(1, 41)) + [64, 96, 100, 127, 128, 192, 512]:
+            assert trt.regtile_thread_shape(lm, ln, max_threads) == \
+                L.dot_thread_shape((lm, ln), max_threads), (lm, ln)
+
+
+@pytest.mark.parametrize("lm,ln,mt", [(3, 17, 32), (3, 17, 64), (8, 8, 32), (16, 32, 32),
+                                      (48, 80, 64), (64, 64, 64), (5, 7, 64), (1, 64, 32),
+                                      (96, 1, 64), (24, 40, 64)])
+def test_regtile_owner_matches_oracle(lm, ln, mt):
+    tm, tn = trt.regtile_thread_shape(lm, ln, mt)
+    rm, rn = lm // tm, ln // tn
+    rows, cols = trt.regtile_owner(lm, ln, tm, tn)
+    exp = [L.regtile_coordinate((lm, ln), (tm, tn), (t // tn, t % tn), (r // rn, r % rn))
+           for t in range(tm * tn) for r in range(rm * rn)]
+    assert list(zip(rows.tolist(), cols.tolist())) == exp
+    # exactly once
+    assert len(set(exp)) == lm * ln
+
+
+def test_regtile_errors():
+    import ctypes
+    lib = trt.lib()
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.trt_regtile_thread_shape(0, 4, 32, ctypes.byref(a), ctypes.byref(b)) == trt.ERR_SIZE
+    assert lib.trt_regtile_thread_shape(4, 4, 0, ctypes.byref(a), ctypes.byref(b)) == trt.ERR_ARG
+    assert lib.trt_regtile_thread_shape(4, 4, 32, None, ctypes.byref(b)) == trt.ERR_NULL
+    buf = np.zeros(64, dtype=np.int32)
+    p = buf.ctypes.data
+    assert lib.trt_regtile_owner(8, 8, 3, 8, p, p, 64) == trt.ERR_ARG      # 3 does not divide 8
+    assert lib.trt_regtile_owner(8, 8, 4, 8, p, p, 63) == trt.ERR_SIZE
+    assert lib.trt_regtile_owner(8, 8, 4, 8, None, p, 64) == trt.ERR_NULL
+    assert lib.trt_regtile_owner(8, 0, 4, 8, p, p, 0) == trt.ERR_SIZE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lm=0), trt.ERR_SIZE), (dict(max_threads=0), trt.ERR_ARG),
+    (dict(max_threads=65), trt.ERR_ARG),
+    (dict(lm=128, ln=128), trt.ERR_UNSUPPORTED),        # (8, 8) threads -> 16 registers per axis
+    (dict(lm=9, ln=1, max_threads=1), trt.ERR_UNSUPPORTED),
+    (dict(M=0), trt.ERR_SIZE), (dict(in_dtype=5), trt.ERR_DTYPE),
+    (dict(C=BASE), trt.ERR_OVERLAP),
+])
+def test_gemm_regtile_errors_before_device_work(kw, code):
+    a = dict(M=64, N=64, K=32, A=BASE, lda=32, opA=0, B=BASE * 2, ldb=64, opB=0,
+             C=BASE * 3, ldc=64, in_dtype=trt.F16, out_dtype=trt.F16, lm=16, ln=16,
+             max_threads=64)
+    a.update(kw)
+    with pytest.raises(trt.TrtError) as e:
+        trt.gemm_regtile_raw(a["M"], a["N"], a["K"], a["A"], a["lda"], a["opA"], a["B"],
+                             a["ldb"], a["opB"], a["C"], a["ldc"], a["in_dtype"],
+                             a["out_dtype"], a["lm"], a["ln"], a["max_threads"])
+    assert e.value.status == code

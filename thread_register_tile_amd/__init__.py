@@ -112,6 +112,13 @@ def lib():
         L.trt_gf2_invert_and_compose.restype = i32
         L.trt_block_reduce.argtypes = [vp, i64, i64, i32, i32, vp, vp]
         L.trt_block_reduce.restype = i32
+        i32p = ctypes.POINTER(i32)
+        L.trt_regtile_thread_shape.argtypes = [i32, i32, i32, i32p, i32p]
+        L.trt_regtile_thread_shape.restype = i32
+        L.trt_regtile_owner.argtypes = [i32, i32, i32, i32, vp, vp, i64]
+        L.trt_regtile_owner.restype = i32
+        L.trt_gemm_regtile.argtypes = gemm_args + [i32, i32, i32, vp]
+        L.trt_gemm_regtile.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
         L.trt_last_error.argtypes = []
@@ -392,6 +399,41 @@ def gf2_invert_and_compose(R, S, t_bits):
 
 
 # ---- the rank-1 block reduction ---------------------------------------------------
+
+# ---- register tiles of any logical shape -------------------------------------
+
+REGTILE_MAX_THREADS = 64     # one wavefront per tile
+REGTILE_MAX_REGS = 8         # registers per axis
+
+
+def regtile_thread_shape(lm, ln, max_threads=REGTILE_MAX_THREADS):
+    """trt_regtile_thread_shape: the physical thread shape (tm, tn) the
+    deterministic policy picks for a logical (lm, ln) tile."""
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().trt_regtile_thread_shape(lm, ln, max_threads, ctypes.byref(tm),
+                                          ctypes.byref(tn)))
+    return tm.value, tn.value
+
+
+def regtile_owner(lm, ln, tm, tn):
+    """trt_regtile_owner: (rows, cols) int32 arrays indexed by
+    thread * registers_per_thread + register."""
+    import numpy as np
+    n = lm * ln
+    rows = np.empty(max(n, 1), dtype=np.int32)
+    cols = np.empty(max(n, 1), dtype=np.int32)
+    _check(lib().trt_regtile_owner(lm, ln, tm, tn, rows.ctypes.data, cols.ctypes.data, n))
+    return rows[:n], cols[:n]
+
+
+def gemm_regtile_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, lm, ln,
+                     max_threads=REGTILE_MAX_THREADS, bias=0, relu=False, residual=0, ldr=0,
+                     scale=0, stream=0):
+    """trt_gemm_regtile on raw device addresses (ints).  Raises TrtError."""
+    _check(lib().trt_gemm_regtile(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
+                                  out_dtype, _epi(bias, relu, residual, ldr, scale), lm, ln,
+                                  max_threads, stream or None))
+
 
 REDUCE_SUM, REDUCE_MAX, REDUCE_MIN = 0, 1, 2
 

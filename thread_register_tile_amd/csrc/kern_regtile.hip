@@ -1,0 +1,45 @@
+// kern_regtile.hip -- instances of the register-tile GEMM on vector lanes:
+// three input types x register bounds {1, 2, 4, 8} per axis.
+#include "regtile.hpp"
+#include "tiles.hpp"
+
+namespace trt {
+
+namespace {
+
+int reg_bound(int r) { return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
+
+template <int DT, int MRM>
+void launch_rn(const RegtileArgs& a, int mrn, dim3 grid, size_t lds, hipStream_t s) {
+  switch (mrn) {
+    case 1: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 1>), grid, dim3(kRegtileThreads), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 2>), grid, dim3(kRegtileThreads), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 4>), grid, dim3(kRegtileThreads), lds, s, a); break;
+    default: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 8>), grid, dim3(kRegtileThreads), lds, s, a); break;
+  }
+}
+
+template <int DT>
+void launch_dt(const RegtileArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  const int mrm = reg_bound(a.rm), mrn = reg_bound(a.rn);
+  switch (mrm) {
+    case 1: launch_rn<DT, 1>(a, mrn, grid, lds, s); break;
+    case 2: launch_rn<DT, 2>(a, mrn, grid, lds, s); break;
+    case 4: launch_rn<DT, 4>(a, mrn, grid, lds, s); break;
+    default: launch_rn<DT, 8>(a, mrn, grid, lds, s); break;
+  }
+}
+
+}  // namespace
+
+void launch_regtile(RegtileArgs a, int dt, hipStream_t s) {
+  a.g.tiles_m = (int)((a.g.M + a.lm - 1) / a.lm);
+  a.g.tiles_n = (int)((a.g.N + a.ln - 1) / a.ln);
+  const dim3 grid((unsigned)((int64_t)a.g.tiles_m * a.g.tiles_n));
+  const size_t lds = sizeof(float) * kRegtileBK * (a.lm + a.ln);
+  if (dt == DT_F16) launch_dt<DT_F16>(a, grid, lds, s);
+  else if (dt == DT_BF16) launch_dt<DT_BF16>(a, grid, lds, s);
+  else launch_dt<DT_F32>(a, grid, lds, s);
+}
+
+}  // namespace trt

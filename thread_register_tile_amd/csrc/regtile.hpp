@@ -1,0 +1,157 @@
+// regtile.hpp -- register tiles of any logical shape, and the GEMM that runs
+// them on general-purpose vector lanes.
+//
+// "My Triton From Scratch, Part 16: Register Tiles": a program instance owns
+// a logical C tile of (lm, ln) results; a physical thread shape (tm, tn)
+// cooperates on it, each thread holding a register tile of (lm/tm, ln/tn)
+// accumulators.  Section "A strided ownership rule": thread (ti, tj),
+// register (ri, rj) owns logical (ti + ri*tm, tj + rj*tn), which covers the
+// tile exactly once whenever tm divides lm and tn divides ln -- so it needs
+// no power-of-two sizes, unlike the GF(2) maps of the matrix-core tiles.
+// Section "Choosing the physical thread shape": among divisor pairs (a of
+// lm, b of ln) with a*b at most a thread budget, the largest by (a*b,
+// min(a, b), b).  The pages' budget is one 32-thread warp; here it is at
+// most one 64-lane wavefront.
+//
+// The kernel: one wavefront per logical tile.  Each K step of 16 stages the
+// [lm x 16] A tile and the [16 x ln] B tile in LDS as fp32, copied by all 64
+// lanes in the order in which each operand is contiguous in global memory.
+// Lanes t < tm*tn then read their lm/tm values of A and ln/tn values of B
+// per k and update every accumulator with one fp32 fused multiply-add.  The
+// epilogue is the fused one of the matrix-core kernels, one element at a
+// time.  Registers per axis are bounded (kRegtileMaxRegs) so that every
+// accumulator index is a compile-time constant; the kernel is instantiated
+// for register bounds MRM x MRN in {1, 2, 4, 8}, the launch taking the
+// smallest bounds that hold (lm/tm, ln/tn).
+#pragma once
+
+#include <stdint.h>
+
+#include "gemm_kernel.hpp"
+
+namespace trt {
+
+constexpr int kRegtileThreads = 64;   // one wavefront per tile
+constexpr int kRegtileMaxRegs = 8;    // registers per axis
+constexpr int kRegtileBK = 16;        // K step
+
+// The thread-shape policy: false if lm, ln or max_threads is not positive.
+inline bool regtile_thread_shape(int64_t lm, int64_t ln, int64_t max_threads, int& tm, int& tn) {
+  if (lm < 1 || ln < 1 || max_threads < 1) return false;
+  int64_t best_p = 0, best_min = 0, best_b = 0;
+  for (int64_t a = 1; a <= lm && a <= max_threads; ++a) {
+    if (lm % a) continue;
+    for (int64_t b = 1; b <= ln && a * b <= max_threads; ++b) {
+      if (ln % b) continue;
+      const int64_t p = a * b, mn = a < b ? a : b;
+      if (p > best_p || (p == best_p && (mn > best_min || (mn == best_min && b > best_b)))) {
+        best_p = p;
+        best_min = mn;
+        best_b = b;
+        tm = (int)a;
+        tn = (int)b;
+      }
+    }
+  }
+  return true;
+}
+
+// Strided ownership: thread t = ti*tn + tj, register r = ri*rn + rj.
+__host__ __device__ __forceinline__ void regtile_coord(int t, int r, int tm, int tn, int rn,
+                                                       int& row, int& col) {
+  const int ti = t / tn, tj = t % tn, ri = r / rn, rj = r % rn;
+  row = ti + ri * tm;
+  col = tj + rj * tn;
+}
+
+struct RegtileArgs {
+  GemmArgs g;
+  int lm, ln, tm, tn, rm, rn;
+  int opA, opB;
+};
+
+template <int DT>
+__device__ __forceinline__ float regtile_in(const void* X, int64_t i) {
+  if constexpr (DT == DT_F32)
+    return static_cast<const float*>(X)[i];
+  else
+    return to_f32<DT>(static_cast<const uint16_t*>(X)[i]);
+}
+
+template <int DT, int MRM, int MRN>
+__global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileArgs p) {
+  constexpr int BK = kRegtileBK;
+  extern __shared__ float rt_lds[];
+  const GemmArgs& g = p.g;
+  const int lm = p.lm, ln = p.ln, tm = p.tm, tn = p.tn, rm = p.rm, rn = p.rn;
+  float* As = rt_lds;             // [BK][lm]
+  float* Bs = rt_lds + BK * lm;   // [BK][ln]
+
+  const int t = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  const int64_t m0 = (tile / g.tiles_n) * lm, n0 = (tile % g.tiles_n) * ln;
+  const bool active = t < tm * tn;
+  const int ti = active ? t / tn : 0, tj = active ? t % tn : 0;
+
+  float acc[MRM][MRN];
+#pragma unroll
+  for (int i = 0; i < MRM; ++i)
+#pragma unroll
+    for (int j = 0; j < MRN; ++j) acc[i][j] = 0.f;
+
+  for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+    // A tile: element (i, kk) = A[m0+i][k0+kk], k contiguous for op N
+    for (int idx = t; idx < lm * BK; idx += kRegtileThreads) {
+      const int i = p.opA ? idx % lm : idx / BK, kk = p.opA ? idx / lm : idx % BK;
+      const int64_t m = m0 + i, k = k0 + kk;
+      float v = 0.f;
+      if (m < g.M && k < g.K) v = regtile_in<DT>(g.A, p.opA ? k * g.lda + m : m * g.lda + k);
+      As[kk * lm + i] = v;
+    }
+    // B tile: element (kk, j) = B[k0+kk][n0+j], n contiguous for op N
+    for (int idx = t; idx < ln * BK; idx += kRegtileThreads) {
+      const int j = p.opB ? idx / BK : idx % ln, kk = p.opB ? idx % BK : idx / ln;
+      const int64_t n = n0 + j, k = k0 + kk;
+      float v = 0.f;
+      if (n < g.N && k < g.K) v = regtile_in<DT>(g.B, p.opB ? n * g.ldb + k : k * g.ldb + n);
+      Bs[kk * ln + j] = v;
+    }
+    __syncthreads();
+    if (active) {
+      for (int kk = 0; kk < BK; ++kk) {
+        float a[MRM], b[MRN];
+#pragma unroll
+        for (int i = 0; i < MRM; ++i) a[i] = i < rm ? As[kk * lm + ti + i * tm] : 0.f;
+#pragma unroll
+        for (int j = 0; j < MRN; ++j) b[j] = j < rn ? Bs[kk * ln + tj + j * tn] : 0.f;
+#pragma unroll
+        for (int i = 0; i < MRM; ++i)
+#pragma unroll
+          for (int j = 0; j < MRN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // the fused epilogue, one owned element at a time:
+  // y = relu(acc * scale[m] + bias[n]) + R[m][n], one rounding to the output type
+  const OutAny O{g.out_dt};
+#pragma unroll
+  for (int i = 0; i < MRM; ++i) {
+#pragma unroll
+    for (int j = 0; j < MRN; ++j) {
+      if (i >= rm || j >= rn) continue;
+      const int64_t m = m0 + ti + i * tm, n = n0 + tj + j * tn;
+      if (m >= g.M || n >= g.N) continue;
+      float y = acc[i][j];
+      if (g.scale) y *= O.ld(g.scale, m);
+      if (g.bias) y += O.ld(g.bias, n);
+      if (g.relu) y = y > 0.f ? y : 0.f;
+      if (g.R) y += O.ld(g.R, m * g.ldr + n);
+      O.st(g.C, m * g.ldc + n, y);
+    }
+  }
+}
+
+}  // namespace trt

@@ -43,6 +43,10 @@ void launch_skinny(GemmArgs a, int dt, hipStream_t s);
 // Launch the binary32-operand GEMM on its 128x128x32 tile (kern_f32.hip).
 void launch_f32(GemmArgs a, int opA, int opB, bool vec, hipStream_t s);
 
+// Launch the register-tile GEMM on vector lanes (kern_regtile.hip).
+struct RegtileArgs;
+void launch_regtile(RegtileArgs a, int dt, hipStream_t s);
+
 // Launch the rank-1 block reduction (kern_reduce.hip).
 struct ReduceArgs;
 void launch_reduce(const ReduceArgs& a, int dt, int op, hipStream_t s);

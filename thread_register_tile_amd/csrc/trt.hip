@@ -4,11 +4,13 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <vector>
 
 #include "../../include/trt.h"
 #include "gemm_kernel.hpp"
 #include "gemm_skinny.hpp"
 #include "reduce.hpp"
+#include "regtile.hpp"
 #include "tiles.hpp"
 #include "validate.hpp"
 
@@ -764,6 +766,89 @@ trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dty
   a.vec = aligned(x, 16) && (block * esz) % 16 == 0;
   trt::launch_reduce(a, dtype, op, static_cast<hipStream_t>(stream));
   return check_launch("block reduction launch");
+}
+
+trt_status trt_regtile_thread_shape(int32_t lm, int32_t ln, int32_t max_threads, int32_t* tm,
+                                    int32_t* tn) {
+  if (!tm || !tn) return fail(TRT_ERR_NULL, "tm and tn must be non-null");
+  if (lm < 1 || ln < 1) return fail(TRT_ERR_SIZE, "lm and ln must be >= 1");
+  if (max_threads < 1) return fail(TRT_ERR_ARG, "max_threads must be >= 1");
+  int a = 1, b = 1;
+  trt::regtile_thread_shape(lm, ln, max_threads, a, b);
+  *tm = a;
+  *tn = b;
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_regtile_owner(int32_t lm, int32_t ln, int32_t tm, int32_t tn, int32_t* rows,
+                             int32_t* cols, int64_t n) {
+  if (lm < 1 || ln < 1 || tm < 1 || tn < 1)
+    return fail(TRT_ERR_SIZE, "tile and thread shapes must be positive");
+  if (lm % tm || ln % tn) return fail(TRT_ERR_ARG, "the thread shape must divide the tile");
+  if ((int64_t)lm * ln > (int64_t(1) << 24)) return fail(TRT_ERR_SIZE, "lm * ln must be <= 2^24");
+  if (n != (int64_t)lm * ln) return fail(TRT_ERR_SIZE, "n must equal lm * ln");
+  if (!rows || !cols) return fail(TRT_ERR_NULL, "rows and cols must be non-null");
+  const int regs = (lm / tm) * (ln / tn), rn = ln / tn;
+  std::vector<uint8_t> seen((size_t)n, 0);
+  for (int t = 0; t < tm * tn; ++t)
+    for (int r = 0; r < regs; ++r) {
+      int row, col;
+      trt::regtile_coord(t, r, tm, tn, rn, row, col);
+      const int64_t x = (int64_t)t * regs + r;
+      rows[x] = row;
+      cols[x] = col;
+      if (row < 0 || row >= lm || col < 0 || col >= ln || seen[(size_t)row * ln + col]++)
+        return fail(TRT_ERR_ARG, "ownership is not exactly once");
+    }
+  g_err.clear();
+  return TRT_OK;
+}
+
+trt_status trt_gemm_regtile(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            int32_t opA, const void* B, int64_t ldb, int32_t opB, void* C,
+                            int64_t ldc, int32_t in_dtype, int32_t out_dtype,
+                            const trt_epilogue* epi, int32_t lm, int32_t ln,
+                            int32_t max_threads, void* stream) {
+  std::string msg;
+  const trt_status s = trt::validate_gemm(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
+                                          out_dtype, epi, msg);
+  if (s != TRT_OK) return fail(s, msg);
+  if (lm < 1 || ln < 1) return fail(TRT_ERR_SIZE, "lm and ln must be >= 1");
+  if (max_threads < 1 || max_threads > trt::kRegtileThreads)
+    return fail(TRT_ERR_ARG, "max_threads must be in [1, 64]");
+  int tm = 1, tn = 1;
+  trt::regtile_thread_shape(lm, ln, max_threads, tm, tn);
+  if (lm / tm > trt::kRegtileMaxRegs || ln / tn > trt::kRegtileMaxRegs)
+    return fail(TRT_ERR_UNSUPPORTED, "more than 8 registers per axis for this tile");
+  if (((M + lm - 1) / lm) * ((N + ln - 1) / ln) > INT32_MAX)
+    return fail(TRT_ERR_SIZE, "more than 2^31-1 output tiles in one launch");
+  trt::RegtileArgs a{};
+  a.g.A = static_cast<const uint16_t*>(A);
+  a.g.B = static_cast<const uint16_t*>(B);
+  a.g.C = C;
+  a.g.bias = epi ? epi->bias : nullptr;
+  a.g.R = epi ? epi->residual : nullptr;
+  a.g.scale = epi ? epi->row_scale : nullptr;
+  a.g.lda = lda;
+  a.g.ldb = ldb;
+  a.g.ldc = ldc;
+  a.g.ldr = (epi && epi->residual) ? epi->ldr : 0;
+  a.g.M = (int32_t)M;
+  a.g.N = (int32_t)N;
+  a.g.K = (int32_t)K;
+  a.g.relu = (epi && epi->relu) ? 1 : 0;
+  a.g.out_dt = out_dtype;
+  a.lm = lm;
+  a.ln = ln;
+  a.tm = tm;
+  a.tn = tn;
+  a.rm = lm / tm;
+  a.rn = ln / tn;
+  a.opA = opA;
+  a.opB = opB;
+  trt::launch_regtile(a, in_dtype, static_cast<hipStream_t>(stream));
+  return check_launch("register-tile gemm launch");
 }
 
 int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }

@@ -50,6 +50,7 @@ class Workload:
     scale: float = 1.0      # half-width for uniform, divisor for normal
     seed: int = 0
     tile: Optional[tuple] = None  # explicit (BM, BN, BK) tile, or None
+    regtile: Optional[tuple] = None  # (lm, ln, max_threads): the vector-lane register-tile GEMM
 
     @property
     def a_rows(self):
@@ -127,7 +128,15 @@ ROWSCALE = Workload("rowscale", 8192, 8192, 4096, dtype=BF16, out_dtype=F32, row
 # throughout (section "What Version 16 does not optimize").
 F32SQUARE = Workload("f32square", 4096, 4096, 4096, dtype=F32, dist="normal", scale=8.0, seed=8)
 
-CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY, ROWSCALE, F32SQUARE)}
+# The same shape on general-purpose vector lanes with a 64x64 register tile
+# (thread shape (8, 8), registers (8, 8)): the execution model of "My Triton
+# From Scratch, Part 16: Register Tiles", section "Register-valued
+# loop-carried accumulators", without the matrix cores.
+REGTILE = Workload("regtile", 4096, 4096, 4096, dtype=F32, dist="normal", scale=8.0, seed=9,
+                   regtile=(64, 64, 64))
+
+CONFIGS = {w.name: w for w in (TINY, SQUARE, EPILOGUE, RAGGED, SKINNY, ROWSCALE, F32SQUARE,
+                               REGTILE)}
 
 
 def shrink(w: Workload, M=None, N=None, K=None, **kw) -> Workload:
