@@ -99,23 +99,48 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
 #pragma unroll
     for (int j = 0; j < MRN; ++j) acc[i][j] = 0.f;
 
+  // Copy order: element e = t + 64*step of an operand tile is (row e/BK, k
+  // e%BK) when k is contiguous in global memory, else (row e%rows, k
+  // e/rows).  The second form steps each lane's (row, k) by the constant
+  // (64 % rows, 64 / rows) with a carry instead of dividing per element.
+  const int a_rows = p.opA ? lm : 0, b_rows = p.opB ? 0 : ln;   // 0: k contiguous
+  const int a_r0 = a_rows ? t % a_rows : t / BK, a_k0 = a_rows ? t / a_rows : t % BK;
+  const int a_dr = a_rows ? kRegtileThreads % a_rows : kRegtileThreads / BK;
+  const int a_dk = a_rows ? kRegtileThreads / a_rows : 0;
+  const int b_r0 = b_rows ? t % b_rows : t / BK, b_k0 = b_rows ? t / b_rows : t % BK;
+  const int b_dr = b_rows ? kRegtileThreads % b_rows : kRegtileThreads / BK;
+  const int b_dk = b_rows ? kRegtileThreads / b_rows : 0;
+
+  // One operand tile: `rows` rows (m or n) x BK k, element (r, kk) read
+  // from X[r*ld + k] (k contiguous) or X[k*ld + r], stored at S[kk*rows + r].
+  // Eight elements per batch are loaded before any is written, so that
+  // their global loads are in flight together.
+  auto copy = [&](const void* X, int64_t ld, bool kc, int rows, int64_t r_base, int64_t r_lim,
+                  int64_t k0, float* S, int r0, int kk0, int dr, int dk, bool carry) {
+    int r = r0, kk = kk0;
+    while (kk < BK && r < rows) {
+      float v[8];
+      int off[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in_tile = kk < BK && r < rows;
+        const int64_t gr = r_base + r, k = k0 + kk;
+        v[u] = 0.f;
+        off[u] = in_tile ? kk * rows + r : -1;
+        if (in_tile && gr < r_lim && k < g.K) v[u] = regtile_in<DT>(X, kc ? gr * ld + k : k * ld + gr);
+        r += dr;
+        kk += dk;
+        if (carry && r >= rows) { r -= rows; ++kk; }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (off[u] >= 0) S[off[u]] = v[u];
+    }
+  };
+
   for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
-    // A tile: element (i, kk) = A[m0+i][k0+kk], k contiguous for op N
-    for (int idx = t; idx < lm * BK; idx += kRegtileThreads) {
-      const int i = p.opA ? idx % lm : idx / BK, kk = p.opA ? idx / lm : idx % BK;
-      const int64_t m = m0 + i, k = k0 + kk;
-      float v = 0.f;
-      if (m < g.M && k < g.K) v = regtile_in<DT>(g.A, p.opA ? k * g.lda + m : m * g.lda + k);
-      As[kk * lm + i] = v;
-    }
-    // B tile: element (kk, j) = B[k0+kk][n0+j], n contiguous for op N
-    for (int idx = t; idx < ln * BK; idx += kRegtileThreads) {
-      const int j = p.opB ? idx / BK : idx % ln, kk = p.opB ? idx % BK : idx / ln;
-      const int64_t n = n0 + j, k = k0 + kk;
-      float v = 0.f;
-      if (n < g.N && k < g.K) v = regtile_in<DT>(g.B, p.opB ? n * g.ldb + k : k * g.ldb + n);
-      Bs[kk * ln + j] = v;
-    }
+    copy(g.A, g.lda, !p.opA, lm, m0, g.M, k0, As, a_r0, a_k0, a_dr, a_dk, a_rows != 0);
+    copy(g.B, g.ldb, p.opB, ln, n0, g.N, k0, Bs, b_r0, b_k0, b_dr, b_dk, b_rows != 0);
     __syncthreads();
     if (active) {
       for (int kk = 0; kk < BK; ++kk) {
