@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0
 # FLOP x 2.4 GHz
 PEAK_VALU_F32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
-WORKLOADS = ("square", "epilogue", "ragged", "skinny")
+WORKLOADS = ("square", "epilogue", "ragged", "skinny", "f32square", "regtile")
 
 
 def csrc_digest():
