@@ -33,7 +33,8 @@ extern "C" {
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
   TRT_OK = 0,
-  TRT_ERR_SIZE = 1,        /* M, N or K < 1, or an extent that overflows int64 */
+  TRT_ERR_SIZE = 1,        /* a size out of range, an extent that overflows,
+                              or more than 2^31-1 workgroups in one launch     */
   TRT_ERR_STRIDE = 2,      /* an input leading dimension < 1, or ldc < N       */
   TRT_ERR_NULL = 3,        /* A, B or C is NULL (or a required output buffer)  */
   TRT_ERR_ALIGN = 4,       /* a pointer not aligned to its element             */
@@ -97,10 +98,12 @@ typedef struct {
  * rejected, since safety that cannot be proven is an error.  A, B, C must be
  * non-NULL; A and B aligned to the input element, C and the epilogue operands
  * to the output element (2 or 4 bytes).  in_dtype and out_dtype are each
- * TRT_F16, TRT_BF16 or TRT_F32 (otherwise TRT_ERR_DTYPE).  Elements of C
- * outside [0,M) x [0,N) (the ldc padding) are never written.  Elements of A and B outside the logical operands (the lda/ldb
- * padding) never influence C, and no byte outside an operand's extent
- * ((rows-1)*ld + cols elements from its base) is ever read.
+ * TRT_F16, TRT_BF16 or TRT_F32 (otherwise TRT_ERR_DTYPE).  M, N, K <= 2^30
+ * and at most 2^31-1 output tiles for the chosen tile (TRT_ERR_SIZE).
+ * Elements of C outside [0,M) x [0,N) (the ldc padding) are never written.
+ * Elements of A and B outside the logical operands (the lda/ldb padding)
+ * never influence C, and no byte outside an operand's extent ((rows-1)*ld +
+ * cols elements from its base) is ever read.
  *
  * stream: a hipStream_t (NULL = the default stream).  The call enqueues one
  * kernel and returns; TRT_ERR_HIP means the launch failed, with the runtime's
