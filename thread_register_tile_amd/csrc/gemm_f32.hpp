@@ -119,37 +119,65 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   const int wrow = (wave / TL::WN) * TL::WTM, wcol = (wave % TL::WN) * TL::WTN;
   const int fr = lane & 15, g = lane >> 4;
 
+  // One K step: the first half's fragments are read, the next step's copy is
+  // issued, then the first half's 64 products run with the second half's
+  // fragment reads interleaved, and the second half's 64 products with the
+  // next step's LDS writes interleaved (the other buffer was last read
+  // before the previous barrier).  Scheduling groups fix the interleave.
+  auto frag = [&](const float* base, int row, int h) {
+    return *reinterpret_cast<const f32x4*>(base + f32_slot(row, 2 * g + h));
+  };
   load_step(0);
   a.store(lds[0], t);
   b.store(lds[0] + BM * 32, t);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_step(kt + 1);
+    const bool more = kt + 1 < nk;
     const float* la = lds[cur];
     const float* lb = lds[cur] + BM * 32;
     f32x4 af[FM][2], bf[FN][2];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) af[i][0] = frag(la, wrow + 16 * i + fr, 0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        af[i][h] = *reinterpret_cast<const f32x4*>(la + f32_slot(wrow + 16 * i + fr, 2 * g + h));
+    for (int j = 0; j < FN; ++j) bf[j][0] = frag(lb, wcol + 16 * j + fr, 0);
+    if (more) load_step(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int i = 0; i < FM; ++i) af[i][1] = frag(la, wrow + 16 * i + fr, 1);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        bf[j][h] = *reinterpret_cast<const f32x4*>(lb + f32_slot(wcol + 16 * j + fr, 2 * g + h));
+    for (int j = 0; j < FN; ++j) bf[j][1] = frag(lb, wcol + 16 * j + fr, 1);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = mfma16_f32(bf[j][kk / 4][kk % 4], af[i][kk / 4][kk % 4], acc[i][j]);
-    if (kt + 1 < nk) {
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16_f32(bf[j][0][kk], af[i][0][kk], acc[i][j]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 matrix-core products
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
       a.store(lds[cur ^ 1], t);
       b.store(lds[cur ^ 1] + BM * 32, t);
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16_f32(bf[j][1][kk], af[i][1][kk], acc[i][j]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 matrix-core products
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU (register transposes)
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // 1 LDS write
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
   epilogue_store<TL>(p, acc, m0, n0, lane, wave);
