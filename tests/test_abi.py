@@ -462,3 +462,27 @@ def test_gemm_regtile_errors_before_device_work(kw, code):
                              a["ldb"], a["opB"], a["C"], a["ldc"], a["in_dtype"],
                              a["out_dtype"], a["lm"], a["ln"], a["max_threads"])
     assert e.value.status == code
+
+
+def test_torch_wrapper_checks_epilogue_operands():
+    # the torch-level wrappers refuse mismatched epilogue operands before any
+    # device work (CPU tensors suffice: nothing reaches the library)
+    import torch
+    A = torch.zeros(8, 4, dtype=torch.float16)
+    B = torch.zeros(4, 6, dtype=torch.float16)
+    for fn in (trt.gemm, lambda *a, **k: trt.gemm_regtile(*a, lm=4, ln=6, **k)):
+        with pytest.raises(trt.TrtError) as e:
+            fn(A, B, bias=torch.zeros(6, dtype=torch.float32))
+        assert e.value.status == trt.ERR_DTYPE
+        with pytest.raises(trt.TrtError) as e:
+            fn(A, B, bias=torch.zeros(5, dtype=torch.float16))
+        assert e.value.status == trt.ERR_SIZE
+        with pytest.raises(trt.TrtError) as e:
+            fn(A, B, residual=torch.zeros(8, 5, dtype=torch.float16))
+        assert e.value.status == trt.ERR_SIZE
+        with pytest.raises(trt.TrtError) as e:
+            fn(A, B, row_scale=torch.zeros(8, dtype=torch.bfloat16))
+        assert e.value.status == trt.ERR_DTYPE
+        with pytest.raises(trt.TrtError) as e:
+            fn(A, torch.zeros(5, 6, dtype=torch.float16))
+        assert e.value.status == trt.ERR_SIZE

@@ -81,3 +81,20 @@ def test_regtile_workload_exact_mode():
     ms, ns = sample_cells(w, 400, seed=4)
     assert_accept(C[ms, ns], reference_cells(w, run.host, ms, ns), w.odt, exact=True,
                   what="regtile exact")
+
+
+def test_regtile_torch_wrapper():
+    import oracle
+    import torch
+    g = torch.Generator().manual_seed(7)
+    A = torch.randint(-1, 2, (70, 45), generator=g).to(torch.bfloat16).cuda()
+    B = torch.randint(-1, 2, (45, 33), generator=g).to(torch.bfloat16).cuda()
+    bias = torch.randint(-2, 3, (33,), generator=g).to(torch.float32).cuda()
+    C = trt.gemm_regtile(A, B, lm=3, ln=17, max_threads=32, bias=bias, relu=True,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Ab = A.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    Bb = B.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    ref = oracle.gemm_block(70, 33, 45, Ab, 45, 0, Bb, 33, 0, W.BF16,
+                            bias=bias.cpu().numpy().view(np.uint32), relu=True, out_dtype=W.F32)
+    assert_accept(C.cpu().numpy().view(np.uint32), ref, W.F32, exact=True, what="wrapper")

@@ -239,20 +239,10 @@ def _ld(t, name):
     return max(t.stride(0), 1)
 
 
-def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, row_scale=None,
-         out=None, out_dtype=None, tile=None, M=None, N=None, K=None):
-    """C = relu((A.B) * row_scale[:, None] + bias) + residual on the GPU, in one kernel.
-
-    A is [M, K] (opA="N") or its transpose stored as [K, M] (opA="T"); B is
-    [K, N] (opB="N") or stored as [N, K] (opB="T"); A and B share one dtype,
-    float16, bfloat16 or float32.  Tensors may be
-    row-padded views (unit inner stride, any row stride).  bias is [N],
-    row_scale [M], residual [M, N], all of the output dtype: out's dtype if
-    out is given, else out_dtype (a torch dtype: float16, bfloat16 or
-    float32), else A's dtype.  out, if given, is written; otherwise a new
-    [M, N] tensor is returned.  Runs on torch's current stream; no
-    synchronisation.
-    """
+def _gemm_call(A, B, opA, opB, bias, relu, residual, row_scale, out, out_dtype, M, N, K):
+    """Shapes, dtypes and raw pointers of a GEMM on torch tensors; allocates
+    `out` if it is not given.  Returns (out, positional args, keyword args)
+    for gemm_raw / gemm_regtile_raw."""
     torch = _torch()
     opa = OP_T if opA in ("T", OP_T, True) else OP_N
     opb = OP_T if opB in ("T", OP_T, True) else OP_N
@@ -268,15 +258,58 @@ def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, row_sc
         raise TrtError(ERR_DTYPE, "A and B dtypes differ")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+    odt = _dtype_code(out)
+    for name, t, need in (("bias", bias, N), ("row_scale", row_scale, M)):
+        if t is None:
+            continue
+        if t.dtype != out.dtype:
+            raise TrtError(ERR_DTYPE, f"{name} must have the output dtype {out.dtype}")
+        if not t.is_contiguous() or t.numel() < need:
+            raise TrtError(ERR_SIZE, f"{name} must be contiguous with at least {need} elements")
     ldr = 0
     if residual is not None:
+        if residual.dtype != out.dtype:
+            raise TrtError(ERR_DTYPE, f"residual must have the output dtype {out.dtype}")
+        if residual.dim() != 2 or residual.size(0) < M or residual.size(1) < N:
+            raise TrtError(ERR_SIZE, f"residual must be at least [{M}, {N}]")
         ldr = _ld(residual, "residual")
-    gemm_raw(M, N, K, A.data_ptr(), _ld(A, "A"), opa, B.data_ptr(), _ld(B, "B"), opb,
-             out.data_ptr(), _ld(out, "out"), dt, _dtype_code(out),
-             bias=bias.data_ptr() if bias is not None else 0, relu=relu,
-             residual=residual.data_ptr() if residual is not None else 0, ldr=ldr,
-             scale=row_scale.data_ptr() if row_scale is not None else 0,
-             tile=tile, stream=_stream(A.device))
+    args = (M, N, K, A.data_ptr(), _ld(A, "A"), opa, B.data_ptr(), _ld(B, "B"), opb,
+            out.data_ptr(), _ld(out, "out"), dt, odt)
+    kw = dict(bias=bias.data_ptr() if bias is not None else 0, relu=relu,
+              residual=residual.data_ptr() if residual is not None else 0, ldr=ldr,
+              scale=row_scale.data_ptr() if row_scale is not None else 0,
+              stream=_stream(A.device))
+    return out, args, kw
+
+
+def gemm(A, B, *, opA="N", opB="N", bias=None, relu=False, residual=None, row_scale=None,
+         out=None, out_dtype=None, tile=None, M=None, N=None, K=None):
+    """C = relu((A.B) * row_scale[:, None] + bias) + residual on the GPU, in one kernel.
+
+    A is [M, K] (opA="N") or its transpose stored as [K, M] (opA="T"); B is
+    [K, N] (opB="N") or stored as [N, K] (opB="T"); A and B share one dtype,
+    float16, bfloat16 or float32.  Tensors may be
+    row-padded views (unit inner stride, any row stride).  bias is [N],
+    row_scale [M], residual [M, N], all of the output dtype: out's dtype if
+    out is given, else out_dtype (a torch dtype: float16, bfloat16 or
+    float32), else A's dtype.  out, if given, is written; otherwise a new
+    [M, N] tensor is returned.  Runs on torch's current stream; no
+    synchronisation.
+    """
+    out, args, kw = _gemm_call(A, B, opA, opB, bias, relu, residual, row_scale, out, out_dtype,
+                               M, N, K)
+    gemm_raw(*args, tile=tile, **kw)
+    return out
+
+
+def gemm_regtile(A, B, *, lm, ln, max_threads=None, opA="N", opB="N", bias=None, relu=False,
+                 residual=None, row_scale=None, out=None, out_dtype=None):
+    """gemm() computed on vector lanes with a register tile of logical shape
+    (lm, ln) and the thread shape regtile_thread_shape(lm, ln, max_threads)
+    (trt_gemm_regtile).  Same arguments and result as gemm()."""
+    out, args, kw = _gemm_call(A, B, opA, opB, bias, relu, residual, row_scale, out, out_dtype,
+                               None, None, None)
+    gemm_regtile_raw(*args, lm, ln, max_threads or REGTILE_MAX_THREADS, **kw)
     return out
 
 
