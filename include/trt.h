@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 8
+#define TRT_ABI_VERSION 9
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -248,14 +248,16 @@ trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink,
 
 /*
  * trt_mfma_loop_probe -- measurement yardstick, not part of the GEMM: 256
- * workgroups of 4 waves (one wave per SIMD) each run `iters` rounds of 32
- * matrix-core products with 16 independent accumulators and no other work
- * in the loop: v_mfma_f32_32x32x16 for dtype TRT_F16 or TRT_BF16, 2^15 * 32
- * * 1024 * iters FLOP per launch; v_mfma_f32_16x16x4_f32 for TRT_F32, 2^11
- * * 32 * 1024 * iters FLOP.  Operand registers come from `operands` (device
- * buffer of TRT_MFMA_PROBE_OPERAND_BYTES, 16-byte aligned; lane l of every
- * wave reads 16-byte words l, 64+l, ..., 960+l); thread x of workgroup w
- * writes 16 fp32 sums of its accumulators to sink[16*(256w + x) ..] (device
+ * workgroups of 4 waves (one wave per SIMD) each run `iters` rounds of
+ * matrix-core products and no other work in the loop, the instruction the
+ * GEMM kernels issue: for dtype TRT_F16 or TRT_BF16, 64 v_mfma_f32_16x16x32
+ * per round on 64 independent accumulators, 2^14 * 64 * 1024 * iters FLOP
+ * per launch; for TRT_F32, 32 v_mfma_f32_16x16x4_f32 per round on 16
+ * accumulators, 2^11 * 32 * 1024 * iters FLOP.  Operand registers come from
+ * `operands` (device buffer of TRT_MFMA_PROBE_OPERAND_BYTES, 16-byte
+ * aligned; lane l of every wave reads 16-byte words l, 64+l, ..., 960+l);
+ * thread x of workgroup w writes 16 fp32 sums of its accumulators to
+ * sink[16*(256w + x) ..] (device
  * buffer of at least TRT_MFMA_PROBE_SINK_BYTES, 64-byte aligned, disjoint
  * from the operands).  Timing it gives the matrix-core rate the part
  * sustains on such data, the context for the GEMM's fraction of peak.

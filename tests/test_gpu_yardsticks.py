@@ -5,7 +5,7 @@ trt_hbm_read_probe (a plain streaming read) is pinned by a property that holds
 at any size: the XOR of the per-workgroup digests equals the XOR of all
 16-byte words read, computed here with numpy.  trt_mfma_loop_probe (matrix
 cores only) is pinned by recomputing every thread's sums of accumulators on
-the host from the operand words and the documented fragment maps (32x32x16
+the host from the operand words and the documented fragment maps (16x16x32
 for 16-bit types, 16x16x4 for binary32), with operands in {-1, 0, 1} so that
 every fp32 sum is exact.
 """
@@ -48,19 +48,15 @@ def test_read_probe_leaves_x_unchanged():
 
 
 def _fragment_product(r0, r1):
-    """Result registers [64, 16] of one 32x32x16 instruction whose operand 0 /
+    """Result registers [64, 4] of one 16x16x32 instruction whose operand 0 /
     operand 1 registers are r0 / r1 ([64, 8] values)."""
-    X = np.zeros((32, 16)); Y = np.zeros((16, 32))
+    X = np.zeros((16, 32)); Y = np.zeros((32, 16))
     for l in range(64):
         for e in range(8):
-            X[L.mfma32_a(l, e)] = r0[l, e]
-            Y[L.mfma32_b(l, e)] = r1[l, e]
+            X[L.mfma16_a(l, e)] = r0[l, e]
+            Y[L.mfma16_b(l, e)] = r1[l, e]
     D = X @ Y
-    out = np.zeros((64, 16))
-    for l in range(64):
-        for r in range(16):
-            out[l, r] = D[L.mfma32_c(l, r)]
-    return out
+    return np.array([[D[L.mfma16_c(l, r)] for r in range(4)] for l in range(64)])
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
@@ -71,10 +67,12 @@ def test_mfma_loop_probe_sums(dtype):
     iters = 3
     sums = trt.mfma_loop_probe(ops, iters, dtype).cpu().numpy()
     reg = lambda base, i: vals[base + 64 * i: base + 64 * i + 64]      # [64 lanes, 8]
+    # operand words A[i]: words 0.. (i < 4) then 512.. ; B[j]: 256.. then 768..
+    A = [reg(0, i) for i in range(4)] + [reg(512, i) for i in range(4)]
+    B = [reg(256, j) for j in range(4)] + [reg(768, j) for j in range(4)]
     exp = np.zeros((64, 16))
-    for q in range(16):
-        exp += iters * (_fragment_product(reg(256, q % 4), reg(0, q // 4)) +
-                        _fragment_product(reg(768, q % 4), reg(512, q // 4)))
+    for q in range(64):
+        exp[:, q % 16] += iters * _fragment_product(B[q % 8], A[q // 8]).sum(axis=1)
     # every wave of every workgroup holds the same sums
     got = sums.reshape(256 * 4, 64, 16)
     assert np.array_equal(got, np.broadcast_to(exp, got.shape))

@@ -308,7 +308,7 @@ def test_mfma32_maps_are_bijections():
 def test_owner_runs_of_four_columns():
     # every run of four consecutive registers holds four consecutive columns
     # of one row: the epilogue's 8-byte vector stores rely on it
-    for cfg in [(16, 64, 32, 1, 1), (256, 256, 32, 2, 2, 32)]:
+    for cfg in [(16, 64, 32, 1, 1), (256, 256, 32, 2, 2, 16), (256, 256, 32, 2, 2, 32)]:
         for w in range(cfg[3] * cfg[4]):
             for l in range(64):
                 for r0 in range(0, L.gemm_regs_per_lane(cfg), 4):
@@ -319,12 +319,13 @@ def test_owner_runs_of_four_columns():
 
 # ---- direct-to-LDS tiles ---------------------------------------------------------
 
-def test_non_power_of_two_tile_owned_exactly_once():
-    # the 256x192 pipelined tile: 2x2 waves of 128x96, 4x3 fragments of 32x32;
-    # its ownership is integer-affine, not GF(2)-linear, so it is checked by
-    # enumeration ("My Triton From Scratch, Part 16: Register Tiles", section
-    # "A strided ownership rule")
-    cfg = (256, 192, 32, 2, 2, 32)
+@pytest.mark.parametrize("mf", [16, 32])
+def test_non_power_of_two_tile_owned_exactly_once(mf):
+    # the 256x192 pipelined tile: 2x2 waves of 128x96, 8x6 fragments of 16x16
+    # (or 4x3 of 32x32); its ownership is integer-affine, not GF(2)-linear, so
+    # it is checked by enumeration ("My Triton From Scratch, Part 16: Register
+    # Tiles", section "A strided ownership rule")
+    cfg = (256, 192, 32, 2, 2, mf)
     regs = L.gemm_regs_per_lane(cfg)
     assert regs == 192
     seen = set()

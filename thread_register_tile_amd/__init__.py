@@ -383,8 +383,9 @@ def mfma_loop_probe(operands, iters, dtype=F16, sink=None):
 
 def mfma_loop_probe_flops(iters, dtype=F16):
     """FLOPs of one trt_mfma_loop_probe launch."""
-    per_product = 2 * 16 * 16 * 4 if dtype == F32 else 2 * 32 * 32 * 16
-    return 256 * 4 * iters * 32 * per_product
+    if dtype == F32:
+        return 256 * 4 * iters * 32 * (2 * 16 * 16 * 4)
+    return 256 * 4 * iters * 64 * (2 * 16 * 16 * 32)
 
 
 # ---- the GF(2) layout algebra (host only; maps as lists of column words) -------

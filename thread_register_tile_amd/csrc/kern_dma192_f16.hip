@@ -1,5 +1,5 @@
 // kern_dma192_f16.hip -- instances of the pipelined direct-to-LDS kernel on
-// the 256x192 tile (4x3 fragments of 32x32 per wave: a register tile that is
+// the 256x192 tile (8x6 fragments of 16x16 per wave: a register tile that is
 // not a power of two) for f16 inputs, in a translation unit of their own.
 #include "gemm_dma.hpp"
 #include "tiles.hpp"

@@ -11,8 +11,8 @@ using TileTiny = Tile<16, 64, 32, 1, 1>;       // one wave, the named GEMM's til
 using Tile64 = Tile<64, 64, 64, 2, 2>;         // 4 waves, 32x32 each
 using Tile128 = Tile<128, 128, 64, 2, 2>;      // 4 waves, 64x64 each
 using Tile256 = Tile<256, 256, 64, 2, 2>;      // 4 waves, 128x128 each
-using Tile256D = Tile<256, 256, 32, 2, 2, 32>; // pipelined, 32x32x16 fragments
-using Tile256x192D = Tile<256, 192, 32, 2, 2, 32>;  // pipelined, 4x3 fragments per wave
+using Tile256D = Tile<256, 256, 32, 2, 2, 16>; // pipelined, 8x8 fragments of 16x16 per wave
+using Tile256x192D = Tile<256, 192, 32, 2, 2, 16>;  // pipelined, 8x6 fragments of 16x16 per wave
 using Tile256F = Tile<256, 256, 32, 2, 2, 16>; // generic kernel on the pipelined tile
 
 // Launch the generic kernel of tile TL (defined, and explicitly instantiated

@@ -368,13 +368,13 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const trt::u32x4* __restr
 }
 
 // Matrix-core yardstick: every wave of 256 workgroups x 4 waves (one per
-// SIMD) runs `iters` rounds of 32 matrix-core products of 32 cycles each
-// (v_mfma_f32_32x32x16 for 16-bit types, v_mfma_f32_16x16x4_f32 for
-// binary32, the instructions the GEMM kernels issue) on operand registers
-// taken from caller data, 16 independent accumulators, nothing else in the
-// loop; each thread then writes sums of its accumulators (so no product is
-// dead).  Timing it gives the rate the matrix cores sustain on this part
-// under the same data and power conditions as the GEMM.
+// SIMD) runs `iters` rounds of matrix-core products, 1024 cycles of them per
+// round -- 64 v_mfma_f32_16x16x32 on 64 accumulators for 16-bit types, 32
+// v_mfma_f32_16x16x4_f32 on 16 accumulators for binary32: the instructions
+// the GEMM kernels issue -- on operand registers taken from caller data,
+// nothing else in the loop; each thread then writes sums of its accumulators
+// (so no product is dead).  Timing it gives the rate the matrix cores sustain
+// on this part under the same data and power conditions as the GEMM.
 constexpr int kMfmaProbeBlocks = 256;
 template <int DT>
 __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const trt::u32x4* __restrict__ src,
@@ -415,19 +415,22 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const trt::u32x4* __r
     sink[(int64_t)blockIdx.x * 256 + t] = out;
     return;
   }
-  trt::f32x16 acc[16];
+  // 16-bit types: operand words A[i] = a[i], a1[i-4] and B[j] = b[j],
+  // b1[j-4]; product q = 8i + j updates accumulator q; element e of the
+  // sums collects the register sums of accumulators q with q % 16 == e
+  const trt::u32x4 A[8] = {a[0], a[1], a[2], a[3], a1[0], a1[1], a1[2], a1[3]};
+  const trt::u32x4 B[8] = {b[0], b[1], b[2], b[3], b1[0], b1[1], b1[2], b1[3]};
+  trt::f32x4 acc[64];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = trt::f32x16{};
+  for (int q = 0; q < 64; ++q) acc[q] = trt::f32x4{};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = trt::mfma32<DT>(b[q % 4], a[q / 4], acc[q]);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = trt::mfma32<DT>(b1[q % 4], a1[q / 4], acc[q]);
+    for (int q = 0; q < 64; ++q) acc[q] = trt::mfma16<DT>(B[q % 8], A[q / 8], acc[q]);
   }
-  trt::f32x16 sum = acc[0];
+  trt::f32x16 out{};
 #pragma unroll
-  for (int q = 1; q < 16; ++q) sum += acc[q];
-  sink[(int64_t)blockIdx.x * 256 + t] = sum;
+  for (int q = 0; q < 64; ++q) out[q % 16] += acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3];
+  sink[(int64_t)blockIdx.x * 256 + t] = out;
 }
 
 // ---- the layout algebra on caller arrays (host only) ------------------------
