@@ -475,7 +475,8 @@ def copy_mncontig(R, G, T, t, i):
 # k-contiguous operand [R rows][4 chunks of 8 k]: chunk (r, g) in slot
 # 4r + (g XOR sk(r)), sk(r) = (bit1(r) XOR bit3(r)) + 2*bit2(r).
 # Rows-contiguous operand [32 k rows][R/8 chunks of 8 rows]: chunk (k, c) in
-# slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*bit0(k) XOR 12*bit1(k).
+# slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*bit0(k) XOR 12*bit1(k) XOR
+# 2*bit3(k).
 
 def _bit(x, i):
     return (x >> i) & 1
@@ -489,12 +490,13 @@ def dma_kc_slot(r, g):
 def dma_mn_slot(R, k, c):
     """Slot of chunk c (8 rows) of k row k in a rows-contiguous operand tile of
     R rows.  With a multiple of 16 chunks per k row the chunk is XOR-ed with
-    6*k0 ^ 12*k1; with 24 chunks (R = 192) the XOR must stay inside aligned
-    groups of 8 chunks: 6*k0 ^ 4*k1."""
+    6*k0 ^ 12*k1 ^ 2*k3; with 24 chunks (R = 192) the XOR must stay inside
+    aligned groups of 8 chunks: 6*k0 ^ 4*k1 ^ 2*k3."""
     if (R // 8) % 16 == 0:
         sm = (6 * _bit(k, 0)) ^ (12 * _bit(k, 1))
     else:
         sm = (6 * _bit(k, 0)) ^ (4 * _bit(k, 1))
+    sm ^= 2 * _bit(k, 3)
     return k * (R // 8) + (c ^ sm)
 
 

@@ -353,28 +353,27 @@ def _conflicts_bytes(addr_bytes, window):
     return max(len(v) for v in banks.values())
 
 
-@pytest.mark.parametrize("R", [128, 192, 256])
+@pytest.mark.parametrize("R", [192, 256])
 def test_dma_kc_fragment_reads_conflict_free(R):
-    # 32x32x16 operand read: lane l reads row rbase + l%32, chunk g = 2s + l//32
-    for rbase in range(0, R, 32):
-        for s in range(2):
-            lanes = [(16 * L.dma_kc_slot(rbase + l % 32, 2 * s + l // 32), 16) for l in range(64)]
-            for n, window in [(8, 128), (16, 256)]:
-                for q in range(0, 64, n):
-                    assert _conflicts_bytes(lanes[q:q + n], window) == 1
+    # 16x16x32 operand read: lane l reads row rbase + l%16, chunk l//16
+    for rbase in range(0, R, 16):
+        lanes = [(16 * L.dma_kc_slot(rbase + l % 16, l // 16), 16) for l in range(64)]
+        for n, window in [(8, 128), (16, 256)]:
+            for q in range(0, 64, n):
+                assert _conflicts_bytes(lanes[q:q + n], window) == 1
 
 
-@pytest.mark.parametrize("R", [128, 192, 256])
+@pytest.mark.parametrize("R", [192, 256])
 def test_dma_mn_transposed_reads_conflict_free(R):
-    # transposing read: lane l (group gq = l//16, l16 = l%16) reads 8 bytes at
-    # k row 8*(gq//2) + 4h + l16//4, columns c0 + 16*(gq%2) + 4*(l16%4)
-    for c0 in range(0, R, 32):
+    # transposing read of a 16x16x32 operand: lane l (group g = l//16, j =
+    # l%16) reads 8 bytes at k row 8g + 4h + j//4, columns c0 + 4*(j%4)
+    for c0 in range(0, R, 16):
         for h in range(2):
             lanes = []
             for l in range(64):
-                gq, l16 = l // 16, l % 16
-                k = 8 * (gq // 2) + 4 * h + l16 // 4
-                col = c0 + 16 * (gq % 2) + 4 * (l16 % 4)
+                g, j = l // 16, l % 16
+                k = 8 * g + 4 * h + j // 4
+                col = c0 + 4 * (j % 4)
                 slot = L.dma_mn_slot(R, k, col // 8)
                 lanes.append((16 * slot + 2 * (col % 8), 8))
             for n, window in [(16, 128), (32, 256)]:

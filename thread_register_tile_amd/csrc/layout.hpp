@@ -440,20 +440,20 @@ struct Tile {
     }
   }
   // rows-contiguous operand, [32 k rows][R/8 chunks of 8 rows]: chunk (k, c)
-  // in slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*k0 XOR 12*k1 in the bits of k.
-  // A transposing fragment read covers 4 consecutive k rows: 32 bytes of each
-  // per 16 lanes, 64 bytes of each per 32 lanes.  sm sends the four rows to
-  // four distinct 32-byte slots of a 128-byte window (bits 1-2) and four
-  // distinct 64-byte slots of a 256-byte window (bits 2-3).
+  // in slot k*(R/8) + (c XOR sm(k)), sm(k) = 6*k0 XOR 12*k1 XOR 2*k3 in the
+  // bits of k.  A transposing fragment read covers 4 consecutive k rows, 32
+  // bytes (two chunks) of each per 16 lanes; the 32 lanes served together
+  // read two such groups 8 k rows apart (k = 8g + 0..3 for lane group g).
+  // k0 and k1 send the four rows of a group to distinct bank groups, and k3
+  // moves the second group off the first one's.
   // With 24 chunks per k row (R = 192) the XOR has to stay inside aligned
-  // groups of 8 chunks: sm(k) = 6*k0 XOR 4*k1, which still sends the four
-  // rows of a read to distinct bank groups (k0 and k1 flip different bits
-  // of the chunk, and rows of the same k0 sit 8 chunks apart in a 256-byte
-  // window only when k1 also differs).
+  // groups of 8 chunks: sm(k) = 6*k0 XOR 4*k1 XOR 2*k3, with the same
+  // effect (checked for both widths by enumerating every read's banks).
   template <int R>
   TRT_HD static int mn_swz(int k) {
-    return (R / 8) % 16 == 0 ? (((k & 1) ? 6 : 0) ^ ((k & 2) ? 12 : 0))
-                             : (((k & 1) ? 6 : 0) ^ ((k & 2) ? 4 : 0));
+    return ((R / 8) % 16 == 0 ? (((k & 1) ? 6 : 0) ^ ((k & 2) ? 12 : 0))
+                              : (((k & 1) ? 6 : 0) ^ ((k & 2) ? 4 : 0))) ^
+           ((k & 8) ? 2 : 0);
   }
   template <int R>
   TRT_HD static int mn_slot(int k, int c) { return k * (R / 8) + (c ^ mn_swz<R>(k)); }
