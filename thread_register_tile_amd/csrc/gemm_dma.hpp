@@ -371,20 +371,29 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x4 (&ac
     epilogue_passes<TL, OT, EPI_FAST>(p, acc, stage, m0, n0, t, bias);
 }
 
-// Fragment addressing for 16-row fragments.  k-contiguous: one base, the
-// swizzle repeats every 16 rows, so fragment f sits 1024 bytes further.
-// rows-contiguous: lane j of 16-lane group g reads 4 rows at k = 8g + j/4,
-// chunk (j%4)/2, half j%2 (the transposing read hands lane i row i of the 4
-// k), and the next 4 k at +8R bytes; one base per fragment.
+// Fragment addressing for 16-row fragments.  Lane group g = lane/16
+// supplies k chunk kchunk(g) = (0, 3, 1, 2)[g] (8 consecutive k); any
+// order common to both operands gives the same sum, and this one keeps
+// the 16-byte reads free of bank conflicts: groups g and g+1 read the same
+// 16 rows, and measured on gfx950 only chunk pairs differing in both bits
+// (0/3, 1/2) cost no extra LDS cycles, whatever the swizzle.
+// k-contiguous: one base, the swizzle repeats every 16 rows, so fragment f
+// sits 1024 bytes further.  rows-contiguous: lane j of group g reads 4 rows
+// at k = 8*kchunk(g) + j/4, chunk (j%4)/2, half j%2 (the transposing read
+// hands lane i row i of the 4 k), and the next 4 k at +8R bytes; one base
+// per fragment.
+__device__ __forceinline__ int frag_kchunk(int g) { return (g & 1) ? 3 - (g >> 1) : (g >> 1); }
+
 template <class TL, int R, bool KC, int F>
 struct FragReader {
   int addr[KC ? 1 : F];
 
   __device__ __forceinline__ void init(int rbase, int lane, int region) {
+    const int g = frag_kchunk(lane >> 4);
     if (KC) {
-      addr[0] = region + 16 * TL::kc_slot(rbase + (lane & 15), lane >> 4);
+      addr[0] = region + 16 * TL::kc_slot(rbase + (lane & 15), g);
     } else {
-      const int j = lane & 15, g = lane >> 4;
+      const int j = lane & 15;
       const int k = 8 * g + (j >> 2);
 #pragma unroll
       for (int f = 0; f < F; ++f) {
