@@ -34,8 +34,9 @@
 //
 // Per K step kt, per wave, one block of FM x FN products on one set of
 // operand registers:
-//   the first half (fragment rows 0..FM/2-1 against every column), with this
-//   thread's copies of step kt+3 into stage (kt+3)%4 interleaved;
+//   the first half (fragment rows 0..FM/2-1 against every column, column by
+//   column), with this thread's copies of step kt+3 into stage (kt+3)%4
+//   spread through it;
 //   wait for this wave's LDS reads and for its copies of step kt+1;
 //   workgroup barrier;
 //   the second half (rows FM/2..FM-1, column by column), refilling the
@@ -414,22 +415,23 @@ struct FragReader {
 };
 
 // Per K step one block of FM*FN products on one set of operand registers:
-// the first half (fragment rows 0..FM/2-1 against every column) interleaved
-// with this thread's copies of step kt+3; then the wait for step kt+1's
+// the first half (fragment rows 0..FM/2-1 against every column, column by
+// column) with this thread's copies of step kt+3 spread through it; then
+// the wait for step kt+1's
 // copies and the barrier; then the second half (rows FM/2..FM-1, column by
 // column) with the next stage's fragments read into the registers as they
 // die: rows 0..FM/2-1 first (dead since the first half), each column right
 // after its last product, rows FM/2..FM-1 at the end (they are needed only
 // in the next step's second half).
-template <class TL, int DT, bool A_KC, bool B_KC>
+template <class TL, int DT, bool A_KC, bool B_KC, int NS = 4>
 __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   static_assert(TL::BK == 32 && TL::MF == 16, "32-wide K steps of 16x16x32 fragments");
+  static_assert(NS >= 3, "copies at least two steps ahead");
   constexpr int BM = TL::BM, BN = TL::BN, FM = TL::FM, FN = TL::FN;
   constexpr int HM = FM / 2, HALF = HM * FN;
   using OpA = DmaOperand<TL, BM, A_KC>;
   using OpB = DmaOperand<TL, BN, B_KC>;
   constexpr int STAGE = OpA::BYTES + OpB::BYTES;
-  constexpr int NS = 4;
   constexpr int LOADS = OpA::NCH + OpB::NCH;
   constexpr int EPI_BYTES = (BM / 2) * (BN + 4) * 4;
   constexpr int LDS_BYTES = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
@@ -465,9 +467,9 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 
   u32x4 fa[FM], fb[FN];
 
-  // prologue: steps 0..2 in flight, step 0's fragments in registers
+  // prologue: steps 0..NS-2 in flight, step 0's fragments in registers
 #pragma unroll
-  for (int step = 0; step < 3; ++step) {
+  for (int step = 0; step < NS - 1; ++step) {
     const uint32_t st = lds_base + step * STAGE;
     const bool lp = partial && step == nk - 1;
     const auto rsa = a.rsrc(step), rsb = b.rsrc(step);
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < OpB::NCH; ++i) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, i);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * LOADS));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -484,26 +486,37 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa[i] = ra.read(lds, i);
 
+  // stage of the copies issued in step kt (step kt+NS-1) and of the
+  // fragments read in it (step kt+1), stepped modulo NS
+  int st_copy = NS - 1, st_next = 1 % NS;
   for (int kt = 0; kt < nk; ++kt) {
-    const int step = kt + 3;
-    const uint32_t st = lds_base + (step & (NS - 1)) * STAGE;
+    const int step = kt + NS - 1;
+    const uint32_t st = lds_base + st_copy * STAGE;
     const bool lp = partial && step == nk - 1;
     const auto rsa = a.rsrc(step), rsb = b.rsrc(step);
-    TRT_LDS char* nxt = lds + ((kt + 1) & (NS - 1)) * STAGE;
+    TRT_LDS char* nxt = lds + st_next * STAGE;
+    st_copy = st_copy == NS - 1 ? 0 : st_copy + 1;
+    st_next = st_next == NS - 1 ? 0 : st_next + 1;
+    // first half, column by column: the column fragment read last in the
+    // previous step is needed last; one copy every HALF/LOADS products
 #pragma unroll
     for (int q = 0; q < HALF; ++q) {
-      const int i = q / FN, j = q % FN;
+      const int j = q / HM, i = q % HM;
       acc[i][j] = mfma16<DT>(fb[j], fa[i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      if (q < OpA::NCH) a.issue_one(rsa, step, st, wave, p.K, lp, q);
-      else if (q < LOADS) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, q - OpA::NCH);
+      constexpr int EVERY = HALF / LOADS;
+      if (q % EVERY == 0) {
+        const int c = q / EVERY;
+        if (c < OpA::NCH) a.issue_one(rsa, step, st, wave, p.K, lp, c);
+        else if (c < LOADS) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, c - OpA::NCH);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // every read of the stage that step kt+4's copies will overwrite was
+    // every read of the stage that the next step's copies overwrite was
     // issued before this point: complete the reads, and step kt+1's copies,
     // before the barrier
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * LOADS));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
