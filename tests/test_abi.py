@@ -147,7 +147,7 @@ def test_tile_table():
 
 
 ALL_TILES = [(16, 64, 32, 1, 1, 16), (64, 64, 64, 2, 2, 16), (128, 128, 64, 2, 2, 16),
-             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 2, 16), (256, 192, 32, 2, 2, 16),
+             (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 4, 16), (256, 192, 32, 2, 2, 16),
              (16, 64, 256, 8, 1, 16)]
 NON_GF2 = (256, 192, 32, 2, 2, 16)   # 6 fragment columns per wave: affine ownership
 SKINNY = (16, 64, 256, 8, 1, 16)

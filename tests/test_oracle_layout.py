@@ -308,7 +308,8 @@ def test_mfma32_maps_are_bijections():
 def test_owner_runs_of_four_columns():
     # every run of four consecutive registers holds four consecutive columns
     # of one row: the epilogue's 8-byte vector stores rely on it
-    for cfg in [(16, 64, 32, 1, 1), (256, 256, 32, 2, 2, 16), (256, 256, 32, 2, 2, 32)]:
+    for cfg in [(16, 64, 32, 1, 1), (256, 256, 32, 2, 2, 16), (256, 256, 32, 2, 4, 16),
+                (256, 256, 32, 2, 2, 32)]:
         for w in range(cfg[3] * cfg[4]):
             for l in range(64):
                 for r0 in range(0, L.gemm_regs_per_lane(cfg), 4):

@@ -1,5 +1,5 @@
 // kern_dma256_f16_am.hip -- instances of the pipelined direct-to-LDS
-// kernel (256x256 tile, K step 32, 16x16x32 fragments) for f16 inputs with
+// kernel (256x256 tile of 8 waves, K step 32, 16x16x32 fragments) for f16 inputs with
 // A stored transposed (m contiguous), in a translation unit of their own so that the
 // library builds in parallel.
 #include "gemm_dma.hpp"

@@ -11,7 +11,7 @@ using TileTiny = Tile<16, 64, 32, 1, 1>;       // one wave, the named GEMM's til
 using Tile64 = Tile<64, 64, 64, 2, 2>;         // 4 waves, 32x32 each
 using Tile128 = Tile<128, 128, 64, 2, 2>;      // 4 waves, 64x64 each
 using Tile256 = Tile<256, 256, 64, 2, 2>;      // 4 waves, 128x128 each
-using Tile256D = Tile<256, 256, 32, 2, 2, 16>; // pipelined, 8x8 fragments of 16x16 per wave
+using Tile256D = Tile<256, 256, 32, 2, 4, 16>; // pipelined, 8 waves of 8x4 fragments of 16x16
 using Tile256x192D = Tile<256, 192, 32, 2, 2, 16>;  // pipelined, 8x6 fragments of 16x16 per wave
 using Tile256F = Tile<256, 256, 32, 2, 2, 16>; // generic kernel on the pipelined tile
 
