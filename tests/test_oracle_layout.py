@@ -320,17 +320,17 @@ def test_owner_runs_of_four_columns():
 
 # ---- direct-to-LDS tiles ---------------------------------------------------------
 
-@pytest.mark.parametrize("mf", [16, 32])
-def test_non_power_of_two_tile_owned_exactly_once(mf):
-    # the 256x192 pipelined tile: 2x2 waves of 128x96, 8x6 fragments of 16x16
-    # (or 4x3 of 32x32); its ownership is integer-affine, not GF(2)-linear, so
-    # it is checked by enumeration ("My Triton From Scratch, Part 16: Register
-    # Tiles", section "A strided ownership rule")
-    cfg = (256, 192, 32, 2, 2, mf)
+@pytest.mark.parametrize("cfg", [(256, 192, 32, 2, 4, 16), (256, 192, 32, 2, 2, 16),
+                                 (256, 192, 32, 2, 2, 32)])
+def test_non_power_of_two_tile_owned_exactly_once(cfg):
+    # the 256x192 pipelined tile: 2x4 waves of 128x48, 8x3 fragments of 16x16
+    # (or 2x2 waves of 128x96); its ownership is integer-affine, not
+    # GF(2)-linear, so it is checked by enumeration ("My Triton From Scratch,
+    # Part 16: Register Tiles", section "A strided ownership rule")
     regs = L.gemm_regs_per_lane(cfg)
-    assert regs == 192
+    assert regs * cfg[3] * cfg[4] * 64 == 256 * 192
     seen = set()
-    for w in range(4):
+    for w in range(cfg[3] * cfg[4]):
         for l in range(64):
             for r in range(regs):
                 seen.add(L.gemm_c_owner(cfg, r, l, w))
