@@ -80,13 +80,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_ad
       : "s"(lds_addr), "v"(voff), "s"(rs));
 }
 
-enum : int {
-  SG_VALU = 0x002,
-  SG_SALU = 0x004,
-  SG_MFMA = 0x008,
-  SG_VMEM_READ = 0x020,
-  SG_DS_READ = 0x100,
-};
 
 // One operand's copies and fragment reads.  R: tile rows (m for A, n for B);
 // KC: k-contiguous storage.

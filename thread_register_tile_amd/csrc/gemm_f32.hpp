@@ -155,10 +155,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma16_f32(bf[j][0][kk], af[i][0][kk], acc[i][j]);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 matrix-core products
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 32, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (more) {
       a.store(lds[cur ^ 1], t);
@@ -172,11 +172,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma16_f32(bf[j][1][kk], af[i][1][kk], acc[i][j]);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 matrix-core products
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU (register transposes)
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // 1 LDS write
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);   // register transposes
+      __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 32, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }

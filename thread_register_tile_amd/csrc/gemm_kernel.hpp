@@ -69,6 +69,14 @@ __device__ __forceinline__ uint32_t from_f32<DT_BF16>(float x) {
 // ---- matrix core ---------------------------------------------------------------
 
 template <int DT>
+// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
+enum : int {
+  SG_VALU = 0x002,
+  SG_MFMA = 0x008,
+  SG_DS_READ = 0x100,
+  SG_DS_WRITE = 0x200,
+};
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
 template <>
 __device__ __forceinline__ f32x4 mfma16<DT_F16>(u32x4 a, u32x4 b, f32x4 c) {
