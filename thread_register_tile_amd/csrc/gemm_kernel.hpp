@@ -68,7 +68,6 @@ __device__ __forceinline__ uint32_t from_f32<DT_BF16>(float x) {
 
 // ---- matrix core ---------------------------------------------------------------
 
-template <int DT>
 // Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
 enum : int {
   SG_VALU = 0x002,
@@ -77,6 +76,7 @@ enum : int {
   SG_DS_WRITE = 0x200,
 };
 
+template <int DT>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
 template <>
 __device__ __forceinline__ f32x4 mfma16<DT_F16>(u32x4 a, u32x4 b, f32x4 c) {
