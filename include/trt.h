@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 9
+#define TRT_ABI_VERSION 10
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -144,6 +144,20 @@ trt_status trt_validate(int64_t M, int64_t N, int64_t K,
                         const void* C, int64_t ldc,
                         int32_t in_dtype, int32_t out_dtype,
                         const trt_epilogue* epi, const trt_tile* tile);
+
+/*
+ * trt_choose_tile -- the workgroup tile trt_gemm uses for an M x N output
+ * with inputs of in_dtype (host only, no HIP call): for M <= 16 the
+ * streaming tile 16x64 (K step 256); otherwise, when either pipelined tile
+ * gives the 256 compute units at least 192 workgroups, the one of
+ * 256x256x32 and 256x192x32 with fewer rounds of 256 workgroups times tile
+ * area; otherwise 128x128x64 if it gives at least 128 workgroups, else
+ * 64x64x64; binary32 inputs always 128x128x32.  Whether the pipelined
+ * kernel or the generic one runs a pipelined tile also depends on the
+ * operands' alignment and extents (see trt_gemm).  Errors: TRT_ERR_NULL,
+ * TRT_ERR_SIZE (M or N outside [1, 2^30]), TRT_ERR_DTYPE.
+ */
+trt_status trt_choose_tile(int64_t M, int64_t N, int32_t in_dtype, trt_tile* tile);
 
 /* Number of compiled workgroup tiles. */
 int32_t trt_tile_count(void);

@@ -486,3 +486,43 @@ def test_torch_wrapper_checks_epilogue_operands():
         with pytest.raises(trt.TrtError) as e:
             fn(A, torch.zeros(5, 6, dtype=torch.float16))
         assert e.value.status == trt.ERR_SIZE
+
+
+# ---- tile choice (host logic) --------------------------------------------------
+
+def _expected_tile(M, N):
+    """The documented rule of trt_choose_tile, restated."""
+    cdiv = lambda a, b: -(-a // b)
+    if M <= 16:
+        return (16, 64, 256)
+    count = lambda bm, bn: cdiv(M, bm) * cdiv(N, bn)
+    cost = lambda bm, bn: cdiv(count(bm, bn), 256) * bm * bn
+    if count(256, 256) >= 192 or count(256, 192) >= 192:
+        return (256, 192, 32) if cost(256, 192) < cost(256, 256) else (256, 256, 32)
+    if count(128, 128) >= 128:
+        return (128, 128, 64)
+    return (64, 64, 64)
+
+
+def test_choose_tile_named_workloads():
+    assert trt.choose_tile(4096, 4096) == (256, 256, 32)          # square
+    assert trt.choose_tile(8192, 8192, trt.BF16) == (256, 256, 32)  # epilogue
+    assert trt.choose_tile(4000, 3072) == (256, 192, 32)          # ragged: one full round
+    assert trt.choose_tile(16, 16384) == (16, 64, 256)            # skinny
+    assert trt.choose_tile(64, 64) == (64, 64, 64)                # tiny (runs its own tile explicitly)
+    assert trt.choose_tile(4096, 4096, trt.F32) == (128, 128, 32)
+
+
+def test_choose_tile_matches_rule():
+    rng = np.random.default_rng(11)
+    for _ in range(2000):
+        M, N = int(rng.integers(1, 20000)), int(rng.integers(1, 20000))
+        assert trt.choose_tile(M, N) == _expected_tile(M, N), (M, N)
+
+
+def test_choose_tile_errors():
+    import ctypes
+    t = trt.TileDesc()
+    assert trt.lib().trt_choose_tile(0, 4, trt.F16, ctypes.byref(t)) == trt.ERR_SIZE
+    assert trt.lib().trt_choose_tile(4, 4, 7, ctypes.byref(t)) == trt.ERR_DTYPE
+    assert trt.lib().trt_choose_tile(4, 4, trt.F16, None) == trt.ERR_NULL

@@ -119,6 +119,8 @@ def lib():
         L.trt_regtile_owner.restype = i32
         L.trt_gemm_regtile.argtypes = gemm_args + [i32, i32, i32, vp]
         L.trt_gemm_regtile.restype = i32
+        L.trt_choose_tile.argtypes = [i64, i64, i32, ctypes.POINTER(TileDesc)]
+        L.trt_choose_tile.restype = i32
         L.trt_abi_version.argtypes = []
         L.trt_abi_version.restype = i32
         L.trt_last_error.argtypes = []
@@ -168,6 +170,13 @@ def validate_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
     """trt_validate: the status a call would return, without any GPU work."""
     return lib().trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
                               out_dtype, _epi(bias, relu, residual, ldr, scale), _tile(tile))
+
+
+def choose_tile(M, N, in_dtype=F16):
+    """trt_choose_tile: the (BM, BN, BK) tile trt_gemm uses for an M x N output."""
+    t = TileDesc()
+    _check(lib().trt_choose_tile(M, N, in_dtype, ctypes.byref(t)))
+    return (t.bm, t.bn, t.bk)
 
 
 def tiles():

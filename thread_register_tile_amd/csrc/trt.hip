@@ -601,6 +601,22 @@ trt_status trt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         nullptr, stream);
 }
 
+trt_status trt_choose_tile(int64_t M, int64_t N, int32_t in_dtype, trt_tile* tile) {
+  if (!tile) return fail(TRT_ERR_NULL, "tile must be non-null");
+  if (M < 1 || N < 1 || M > trt::kMaxDim || N > trt::kMaxDim)
+    return fail(TRT_ERR_SIZE, "M and N must be in [1, 2^30]");
+  if (in_dtype != TRT_F16 && in_dtype != TRT_BF16 && in_dtype != TRT_F32)
+    return fail(TRT_ERR_DTYPE, "in_dtype must be TRT_F16, TRT_BF16 or TRT_F32");
+  if (in_dtype == TRT_F32) {
+    *tile = trt_tile{128, 128, 32};
+  } else {
+    const TileEntry* e = choose_tile(M, N);
+    *tile = trt_tile{e->bm, e->bn, e->bk};
+  }
+  g_err.clear();
+  return TRT_OK;
+}
+
 int32_t trt_tile_count(void) { return kNumTiles; }
 
 trt_status trt_tile_at(int32_t i, trt_tile* tile, int32_t* waves_m, int32_t* waves_n,
