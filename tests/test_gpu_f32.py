@@ -52,6 +52,50 @@ def test_f32_inputs_exact_mode(ops, odt):
                   what=f"{ops} out={odt}")
 
 
+# M, N and K multiples of 4 with 16-byte aligned rows take the direct-to-LDS
+# kernel; the shapes leave ragged tiles and (but for K = 64) a partial last
+# K step, down to a single partial step.
+DIRECT_SHAPES = [(2 * 128 + 36, 3 * 128 + 20, 5 * 32 + 12), (128, 128, 64), (36, 200, 4),
+                 (300, 8, 100)]
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("shape", DIRECT_SHAPES)
+def test_f32_direct_copy_path_exact(ops, shape):
+    M, N, K = shape
+    w = f32_case(M, N, K, ops[0], ops[1], 8 if ops[0] == ops[1] else 0, True,
+                 seed=230 + M % 7, dist="ternary")
+    run = Run(w, ldc=w.N + 4)
+    run.launch()
+    assert_accept(run.result(), reference_block(w, run.host), W.F32, exact=True,
+                  what=f"{ops} {shape}")
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_f32_direct_copy_path_tolerance(ops):
+    w = f32_case(3 * 128 + 4, 2 * 128 + 60, 7 * 32 + 28, ops[0], ops[1], 4, False, seed=240)
+    run = Run(w)
+    run.launch()
+    assert_accept(run.result(), reference_block(w, run.host), W.F32, what=f"{ops}")
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_f32_kernels_agree_bit_for_bit(ops):
+    # the same values with 16-byte aligned rows (direct copies) and with
+    # rows padded by one element (register-staged copies): both kernels run
+    # the same products in the same order
+    M, N, K = 2 * 128 + 36, 128 + 92, 3 * 32 + 20
+    out = []
+    for pad in (4, 1):
+        w = f32_case(M, N, K, ops[0], ops[1], pad, True, seed=250)
+        run = Run(w)
+        run.launch()
+        out.append(run.result())
+    assert np.array_equal(out[0], out[1]), f"{ops}: the two binary32 kernels differ"
+    ref = reference_block(w, run.host)
+    assert_accept(out[0], ref, W.F32, what=f"{ops}")
+
+
 def test_f32_inputs_random_shapes_exact():
     rng = np.random.default_rng(23)
     for trial in range(16):
