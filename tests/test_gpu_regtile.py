@@ -18,9 +18,11 @@ from gpu_util import Run, assert_accept, reference_block, reference_cells, sampl
 pytestmark = pytest.mark.gpu
 
 # (lm, ln, max_threads): the pages' examples under their 32-thread budget,
-# non-power-of-two shapes, and full 64-lane wavefronts
+# non-power-of-two shapes, full 64-lane wavefronts, and tiles of more than 64
+# rows (96, 256), whose K steps are loaded without prefetching
 SHAPES = [(3, 17, 32), (8, 8, 32), (16, 32, 32), (1, 64, 32), (3, 17, 64), (48, 40, 64),
-          (64, 64, 64), (5, 7, 64), (96, 1, 64), (24, 40, 64), (13, 7, 64), (8, 1, 1)]
+          (64, 64, 64), (5, 7, 64), (96, 1, 64), (24, 40, 64), (13, 7, 64), (8, 1, 1),
+          (256, 2, 64)]
 
 
 def rt_case(lm, ln, mt, dtype, opA, opB, pad, epi, seed, dist="ternary", odt=None):

@@ -9,13 +9,21 @@ namespace {
 
 int reg_bound(int r) { return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
 
+template <int DT, int MRM, int MRN>
+void launch_pf(const RegtileArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  if (a.prefetch)
+    hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, MRN, true>), grid, dim3(kRegtileThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, MRN, false>), grid, dim3(kRegtileThreads), lds, s, a);
+}
+
 template <int DT, int MRM>
 void launch_rn(const RegtileArgs& a, int mrn, dim3 grid, size_t lds, hipStream_t s) {
   switch (mrn) {
-    case 1: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 1>), grid, dim3(kRegtileThreads), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 2>), grid, dim3(kRegtileThreads), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 4>), grid, dim3(kRegtileThreads), lds, s, a); break;
-    default: hipLaunchKernelGGL((gemm_regtile_kernel<DT, MRM, 8>), grid, dim3(kRegtileThreads), lds, s, a); break;
+    case 1: launch_pf<DT, MRM, 1>(a, grid, lds, s); break;
+    case 2: launch_pf<DT, MRM, 2>(a, grid, lds, s); break;
+    case 4: launch_pf<DT, MRM, 4>(a, grid, lds, s); break;
+    default: launch_pf<DT, MRM, 8>(a, grid, lds, s); break;
   }
 }
 
@@ -37,6 +45,11 @@ void launch_regtile(RegtileArgs a, int dt, hipStream_t s) {
   a.g.tiles_n = (int)((a.g.N + a.ln - 1) / a.ln);
   const dim3 grid((unsigned)((int64_t)a.g.tiles_m * a.g.tiles_n));
   const size_t lds = sizeof(float) * kRegtileBK * (a.lm + a.ln);
+  // at most kRegtilePF elements of each operand tile per lane, operands
+  // addressable by 32-bit byte offsets
+  a.prefetch = (a.lm * kRegtileBK + kRegtileThreads - 1) / kRegtileThreads <= kRegtilePF &&
+               (a.ln * kRegtileBK + kRegtileThreads - 1) / kRegtileThreads <= kRegtilePF &&
+               a.g.a_bytes < (int64_t(1) << 31) && a.g.b_bytes < (int64_t(1) << 31);
   if (dt == DT_F16) launch_dt<DT_F16>(a, grid, lds, s);
   else if (dt == DT_BF16) launch_dt<DT_BF16>(a, grid, lds, s);
   else launch_dt<DT_F32>(a, grid, lds, s);

@@ -17,7 +17,12 @@
 // [lm x 16] A tile and the [16 x ln] B tile in LDS as fp32, copied by all 64
 // lanes in the order in which each operand is contiguous in global memory.
 // Lanes t < tm*tn then read their lm/tm values of A and ln/tn values of B
-// per k and update every accumulator with one fp32 fused multiply-add.  The
+// per k and update every accumulator with one fp32 fused multiply-add.  When
+// both tiles have at most 64 rows (at most kRegtilePF elements per lane), the
+// global loads of step k+1 are issued into registers before step k's
+// products and written to LDS after them, so their latency is hidden behind
+// the arithmetic; larger tiles load each step's elements in batches of
+// eight before its products.  The
 // epilogue is the fused one of the matrix-core kernels, one element at a
 // time.  Registers per axis are bounded (kRegtileMaxRegs) so that every
 // accumulator index is a compile-time constant; the kernel is instantiated
@@ -34,6 +39,7 @@ namespace trt {
 constexpr int kRegtileThreads = 64;   // one wavefront per tile
 constexpr int kRegtileMaxRegs = 8;    // registers per axis
 constexpr int kRegtileBK = 16;        // K step
+constexpr int kRegtilePF = 16;        // prefetched elements per lane and operand (rows <= 64)
 
 // The thread-shape policy: false if lm, ln or max_threads is not positive.
 inline bool regtile_thread_shape(int64_t lm, int64_t ln, int64_t max_threads, int& tm, int& tn) {
@@ -68,6 +74,7 @@ struct RegtileArgs {
   GemmArgs g;
   int lm, ln, tm, tn, rm, rn;
   int opA, opB;
+  int prefetch;   // the next K step's tiles are loaded during this one's products
 };
 
 template <int DT>
@@ -78,7 +85,7 @@ __device__ __forceinline__ float regtile_in(const void* X, int64_t i) {
     return to_f32<DT>(static_cast<const uint16_t*>(X)[i]);
 }
 
-template <int DT, int MRM, int MRN>
+template <int DT, int MRM, int MRN, bool PREFETCH>
 __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileArgs p) {
   constexpr int BK = kRegtileBK;
   extern __shared__ float rt_lds[];
@@ -138,24 +145,111 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
     }
   };
 
-  for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
-    copy(g.A, g.lda, !p.opA, lm, m0, g.M, k0, As, a_r0, a_k0, a_dr, a_dk, a_rows != 0);
-    copy(g.B, g.ldb, p.opB, ln, n0, g.N, k0, Bs, b_r0, b_k0, b_dr, b_dk, b_rows != 0);
-    __syncthreads();
-    if (active) {
-      for (int kk = 0; kk < BK; ++kk) {
-        float a[MRM], b[MRN];
+  // The products of one K step from the staged tiles.  Register slots past
+  // (rm, rn) read a valid element (the last row or column of the thread)
+  // instead of branching, and feed accumulators the epilogue never stores;
+  // the offsets are fixed for the whole kernel, so a K step's LDS reads
+  // are branch-free and can run ahead of its multiply-adds.
+  int aoff[MRM], boff[MRN];
 #pragma unroll
-        for (int i = 0; i < MRM; ++i) a[i] = i < rm ? As[kk * lm + ti + i * tm] : 0.f;
+  for (int i = 0; i < MRM; ++i) aoff[i] = ti + (i < rm ? i : rm - 1) * tm;
 #pragma unroll
-        for (int j = 0; j < MRN; ++j) b[j] = j < rn ? Bs[kk * ln + tj + j * tn] : 0.f;
+  for (int j = 0; j < MRN; ++j) boff[j] = tj + (j < rn ? j : rn - 1) * tn;
+  auto products = [&]() {
+    if (!active) return;
+#pragma unroll 2
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[MRM], b[MRN];
 #pragma unroll
-        for (int i = 0; i < MRM; ++i)
+      for (int i = 0; i < MRM; ++i) a[i] = As[kk * lm + aoff[i]];
 #pragma unroll
-          for (int j = 0; j < MRN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-      }
+      for (int j = 0; j < MRN; ++j) b[j] = Bs[kk * ln + boff[j]];
+#pragma unroll
+      for (int i = 0; i < MRM; ++i)
+#pragma unroll
+        for (int j = 0; j < MRN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
     }
-    __syncthreads();
+  };
+
+  if constexpr (PREFETCH) {
+    // Lane t's elements e = t + 64u (u < PF) of an operand tile, in the
+    // same order as the batched copy: k-contiguous storage gives (row
+    // t/16 + 4u, k t%16), rows-contiguous storage (row e % rows, k
+    // e / rows).  Their byte offsets from the K step's first element are
+    // computed once (out of range where the row is outside the operand or
+    // the element outside the tile); a buffer descriptor per K step, its
+    // record count what is left of the operand, reads zero past the end.
+    constexpr int PF = kRegtilePF;
+    constexpr uint32_t NONE = 0x80000000u;
+    const int64_t isz = DT == DT_F32 ? 4 : 2;
+    auto offsets = [&](int64_t ld, bool kc, int rows, int64_t r_base, int64_t r_lim,
+                       uint32_t (&off)[PF]) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int e = t + 64 * u;
+        const int r = kc ? t / BK + 4 * u : e % rows, kk = kc ? t % BK : e / rows;
+        const bool ok = r < rows && kk < BK && r_base + r < r_lim;
+        off[u] = ok ? (uint32_t)((kc ? (r_base + r) * ld + kk : kk * ld + r_base + r) * isz) : NONE;
+      }
+    };
+    auto rsrc = [&](const void* X, int64_t bytes, int64_t adv) {
+      int64_t left = bytes - adv;
+      left = left < 0 ? 0 : left;
+      return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)X + (adv < bytes ? adv : 0)),
+                                               (short)0, (int)left, 0x00020000);
+    };
+    auto fetch = [&](__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[PF], bool zero, float (&v)[PF]) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        if constexpr (DT == DT_F32)
+          v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off[u], 0, 0));
+        else
+          v[u] = to_f32<DT>(__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(rs, off[u], 0, 0)));
+        if (zero) v[u] = 0.f;
+      }
+    };
+    // LDS: k-contiguous element (row, k) at k*rows + row; rows-contiguous
+    // element e at e
+    auto put = [&](float* S, bool kc, int rows, const float (&v)[PF]) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        if (kc) {
+          if (t / BK + 4 * u < rows) S[(t % BK) * rows + t / BK + 4 * u] = v[u];
+        } else {
+          if (t + 64 * u < rows * BK) S[t + 64 * u] = v[u];
+        }
+      }
+    };
+    const bool akc = !p.opA, bkc = p.opB;
+    uint32_t oa[PF], ob[PF];
+    offsets(g.lda, akc, lm, m0, g.M, oa);
+    offsets(g.ldb, bkc, ln, n0, g.N, ob);
+    float va[PF], vb[PF];
+    // a k-contiguous element at k >= K lies inside the operand (the next
+    // row); only the last K step has such elements, and only lanes whose k
+    // t % 16 is past K
+    auto step_loads = [&](int64_t k0) {
+      const bool kout = k0 + t % BK >= g.K;
+      fetch(rsrc(g.A, g.a_bytes, k0 * (akc ? 1 : g.lda) * isz), oa, akc && kout, va);
+      fetch(rsrc(g.B, g.b_bytes, k0 * (bkc ? 1 : g.ldb) * isz), ob, bkc && kout, vb);
+    };
+    step_loads(0);
+    for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+      put(As, akc, lm, va);
+      put(Bs, bkc, ln, vb);
+      __syncthreads();
+      if (k0 + BK < g.K) step_loads(k0 + BK);
+      products();
+      __syncthreads();
+    }
+  } else {
+    for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+      copy(g.A, g.lda, !p.opA, lm, m0, g.M, k0, As, a_r0, a_k0, a_dr, a_dk, a_rows != 0);
+      copy(g.B, g.ldb, p.opB, ln, n0, g.N, k0, Bs, b_r0, b_k0, b_dr, b_dk, b_rows != 0);
+      __syncthreads();
+      products();
+      __syncthreads();
+    }
   }
   if (!active) return;
 

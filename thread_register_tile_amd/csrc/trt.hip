@@ -866,6 +866,12 @@ trt_status trt_gemm_regtile(int64_t M, int64_t N, int64_t K, const void* A, int6
   a.rn = ln / tn;
   a.opA = opA;
   a.opB = opB;
+  const int64_t isz = trt::elem_bytes(in_dtype);
+  int64_t sa = 0, sb = 0;
+  trt::span_bytes(opA ? K : M, opA ? M : K, lda, sa, isz);
+  trt::span_bytes(opB ? N : K, opB ? K : N, ldb, sb, isz);
+  a.g.a_bytes = sa;
+  a.g.b_bytes = sb;
   trt::launch_regtile(a, in_dtype, static_cast<hipStream_t>(stream));
   return check_launch("register-tile gemm launch");
 }
