@@ -40,6 +40,7 @@ constexpr int kRegtileThreads = 64;   // one wavefront per tile
 constexpr int kRegtileMaxRegs = 8;    // registers per axis
 constexpr int kRegtileBK = 16;        // K step
 constexpr int kRegtilePF = 16;        // prefetched elements per lane and operand (rows <= 64)
+constexpr int kRegtilePitch = kRegtileBK + 1;   // LDS floats per tile row (odd: rows on distinct banks)
 
 // The thread-shape policy: false if lm, ln or max_threads is not positive.
 inline bool regtile_thread_shape(int64_t lm, int64_t ln, int64_t max_threads, int& tm, int& tn) {
@@ -91,8 +92,9 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
   extern __shared__ float rt_lds[];
   const GemmArgs& g = p.g;
   const int lm = p.lm, ln = p.ln, tm = p.tm, tn = p.tn, rm = p.rm, rn = p.rn;
-  float* As = rt_lds;             // [BK][lm]
-  float* Bs = rt_lds + BK * lm;   // [BK][ln]
+  constexpr int PITCH = kRegtilePitch;
+  float* As = rt_lds;                // [lm][PITCH]: row r's k at r*PITCH + k
+  float* Bs = rt_lds + lm * PITCH;   // [ln][PITCH]
 
   const int t = threadIdx.x;
   const int64_t tile = blockIdx.x;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
   const int b_dk = b_rows ? kRegtileThreads / b_rows : 0;
 
   // One operand tile: `rows` rows (m or n) x BK k, element (r, kk) read
-  // from X[r*ld + k] (k contiguous) or X[k*ld + r], stored at S[kk*rows + r].
+  // from X[r*ld + k] (k contiguous) or X[k*ld + r], stored at S[r*PITCH + kk].
   // Eight elements per batch are loaded before any is written, so that
   // their global loads are in flight together.
   auto copy = [&](const void* X, int64_t ld, bool kc, int rows, int64_t r_base, int64_t r_lim,
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
         const bool in_tile = kk < BK && r < rows;
         const int64_t gr = r_base + r, k = k0 + kk;
         v[u] = 0.f;
-        off[u] = in_tile ? kk * rows + r : -1;
+        off[u] = in_tile ? r * PITCH + kk : -1;
         if (in_tile && gr < r_lim && k < g.K) v[u] = regtile_in<DT>(X, kc ? gr * ld + k : k * ld + gr);
         r += dr;
         kk += dk;
@@ -148,22 +150,23 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
   // The products of one K step from the staged tiles.  Register slots past
   // (rm, rn) read a valid element (the last row or column of the thread)
   // instead of branching, and feed accumulators the epilogue never stores;
-  // the offsets are fixed for the whole kernel, so a K step's LDS reads
-  // are branch-free and can run ahead of its multiply-adds.
+  // a thread's rows start at offsets fixed for the whole kernel and k is
+  // an immediate offset, so a K step's LDS reads need no address
+  // arithmetic and can run ahead of its multiply-adds.
   int aoff[MRM], boff[MRN];
 #pragma unroll
-  for (int i = 0; i < MRM; ++i) aoff[i] = ti + (i < rm ? i : rm - 1) * tm;
+  for (int i = 0; i < MRM; ++i) aoff[i] = (ti + (i < rm ? i : rm - 1) * tm) * PITCH;
 #pragma unroll
-  for (int j = 0; j < MRN; ++j) boff[j] = tj + (j < rn ? j : rn - 1) * tn;
+  for (int j = 0; j < MRN; ++j) boff[j] = (tj + (j < rn ? j : rn - 1) * tn) * PITCH;
   auto products = [&]() {
     if (!active) return;
-#pragma unroll 2
+#pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
       float a[MRM], b[MRN];
 #pragma unroll
-      for (int i = 0; i < MRM; ++i) a[i] = As[kk * lm + aoff[i]];
+      for (int i = 0; i < MRM; ++i) a[i] = As[aoff[i] + kk];
 #pragma unroll
-      for (int j = 0; j < MRN; ++j) b[j] = Bs[kk * ln + boff[j]];
+      for (int j = 0; j < MRN; ++j) b[j] = Bs[boff[j] + kk];
 #pragma unroll
       for (int i = 0; i < MRM; ++i)
 #pragma unroll
@@ -183,13 +186,14 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
     constexpr uint32_t NONE = 0x80000000u;
     const int64_t isz = DT == DT_F32 ? 4 : 2;
     auto offsets = [&](int64_t ld, bool kc, int rows, int64_t r_base, int64_t r_lim,
-                       uint32_t (&off)[PF]) {
+                       uint32_t (&off)[PF], int (&lo)[PF]) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int e = t + 64 * u;
         const int r = kc ? t / BK + 4 * u : e % rows, kk = kc ? t % BK : e / rows;
         const bool ok = r < rows && kk < BK && r_base + r < r_lim;
         off[u] = ok ? (uint32_t)((kc ? (r_base + r) * ld + kk : kk * ld + r_base + r) * isz) : NONE;
+        lo[u] = r < rows && kk < BK ? r * PITCH + kk : -1;
       }
     };
     auto rsrc = [&](const void* X, int64_t bytes, int64_t adv) {
@@ -208,22 +212,23 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
         if (zero) v[u] = 0.f;
       }
     };
-    // LDS: k-contiguous element (row, k) at k*rows + row; rows-contiguous
-    // element e at e
-    auto put = [&](float* S, bool kc, int rows, const float (&v)[PF]) {
+    // LDS: element (row, k) at row*PITCH + k; for k-contiguous storage
+    // lane t's element u is (t/16 + 4u, t%16), a closed form
+    auto put = [&](float* S, bool kc, int rows, const float (&v)[PF], const int (&lo)[PF]) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         if (kc) {
-          if (t / BK + 4 * u < rows) S[(t % BK) * rows + t / BK + 4 * u] = v[u];
+          if (t / BK + 4 * u < rows) S[(t / BK + 4 * u) * PITCH + t % BK] = v[u];
         } else {
-          if (t + 64 * u < rows * BK) S[t + 64 * u] = v[u];
+          if (lo[u] >= 0) S[lo[u]] = v[u];
         }
       }
     };
     const bool akc = !p.opA, bkc = p.opB;
     uint32_t oa[PF], ob[PF];
-    offsets(g.lda, akc, lm, m0, g.M, oa);
-    offsets(g.ldb, bkc, ln, n0, g.N, ob);
+    int la[PF], lb[PF];
+    offsets(g.lda, akc, lm, m0, g.M, oa, la);
+    offsets(g.ldb, bkc, ln, n0, g.N, ob, lb);
     float va[PF], vb[PF];
     // a k-contiguous element at k >= K lies inside the operand (the next
     // row); only the last K step has such elements, and only lanes whose k
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
     };
     step_loads(0);
     for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
-      put(As, akc, lm, va);
-      put(Bs, bkc, ln, vb);
+      put(As, akc, lm, va, la);
+      put(Bs, bkc, ln, vb, lb);
       __syncthreads();
       if (k0 + BK < g.K) step_loads(k0 + BK);
       products();
