@@ -16,6 +16,10 @@ SOURCES = ["trt.hip", "kern_tiny.hip", "kern_64.hip", "kern_128.hip", "kern_256.
            "kern_dma256_bf16_ak.hip", "kern_dma256_bf16_am.hip", "kern_dma192_f16.hip",
            "kern_dma192_bf16.hip", "kern_skinny.hip", "kern_reduce.hip", "kern_f32.hip",
            "kern_regtile.hip"]
+# Per-file flags.  The binary32 kernels keep their accumulators in ordinary
+# VGPRs: left to itself the compiler puts them in AGPRs and moves half of
+# them through VGPRs every K step.
+FILE_FLAGS = {"kern_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 LIB = os.path.join(HERE, "libtrt.so")
 ARCH = "gfx950"
 
@@ -59,7 +63,8 @@ def build(verbose: bool = False, extra=(), jobs: int = 0) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *compile_flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *compile_flags, *FILE_FLAGS.get(src, []), *extra, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or max(1, min(len(cmds), len(os.sched_getaffinity(0)), 16))
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
