@@ -39,12 +39,40 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 WORKLOADS = ("square", "epilogue", "ragged", "skinny", "f32square", "regtile")
 
 
+def _code_tokens(src):
+    """C++ source without its comments, whitespace runs collapsed: what the
+    compiler sees, so that editing a comment does not orphan the counters."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def csrc_digest():
+    """Digest of the kernel sources (comments aside) and the compile flags."""
+    from thread_register_tile_amd import build
     h = hashlib.sha256()
     d = os.path.join(ROOT, "thread_register_tile_amd", "csrc")
     for name in sorted(os.listdir(d)):
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(d, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_tokens(f.read()).encode())
+    h.update(repr((build.FLAGS, build.FILE_FLAGS)).encode())
     return h.hexdigest()[:16]
 
 

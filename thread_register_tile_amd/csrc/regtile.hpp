@@ -14,20 +14,23 @@
 // most one 64-lane wavefront.
 //
 // The kernel: one wavefront per logical tile.  Each K step of 16 stages the
-// [lm x 16] A tile and the [16 x ln] B tile in LDS as fp32, copied by all 64
-// lanes in the order in which each operand is contiguous in global memory.
-// Lanes t < tm*tn then read their lm/tm values of A and ln/tn values of B
-// per k and update every accumulator with one fp32 fused multiply-add.  When
-// both tiles have at most 64 rows (at most kRegtilePF elements per lane), the
-// global loads of step k+1 are issued into registers before step k's
-// products and written to LDS after them, so their latency is hidden behind
-// the arithmetic; larger tiles load each step's elements in batches of
-// eight before its products.  The
-// epilogue is the fused one of the matrix-core kernels, one element at a
-// time.  Registers per axis are bounded (kRegtileMaxRegs) so that every
+// [lm x 16] A tile and the [16 x ln] B tile in LDS as fp32, row-major with
+// an odd pitch of 17 floats, copied by all 64 lanes in the order in which
+// each operand is contiguous in global memory.  Lanes t < tm*tn then read
+// their lm/tm values of A and ln/tn values of B per k (immediate k offsets
+// from row bases fixed for the whole kernel; the rows one read touches fall
+// on distinct banks) and update every accumulator with one fp32 fused
+// multiply-add.  When both tiles have at most 64 rows (at most kRegtilePF
+// elements per lane), the global loads of step k+1 are issued into
+// registers before step k's products and written to LDS after them, so
+// their latency is hidden behind the arithmetic; larger tiles load each
+// step's elements in batches of eight before its products.  The epilogue
+// is the fused one of the matrix-core kernels, one element at a time.
+// Registers per axis are bounded (kRegtileMaxRegs) so that every
 // accumulator index is a compile-time constant; the kernel is instantiated
-// for register bounds MRM x MRN in {1, 2, 4, 8}, the launch taking the
-// smallest bounds that hold (lm/tm, ln/tn).
+// for register bounds MRM x MRN in {1, 2, 4, 8} (with and without the
+// prefetch), the launch taking the smallest bounds that hold (lm/tm,
+// ln/tn).
 #pragma once
 
 #include <stdint.h>
