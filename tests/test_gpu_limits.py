@@ -4,7 +4,8 @@ Every case uses integer operands in {-1, 0, 1} (epilogue terms in {-2..2}),
 so the GPU result must equal the oracle's rounding of the exact sum bit for
 bit.  The large cases cross the 32-bit boundaries the kernels must not wrap
 at: an operand larger than 2 GiB (which the 32-bit buffer offsets of the
-direct-to-LDS copies cannot address, so it takes the generic kernel), an
+direct-to-LDS copies cannot address, so it takes the generic kernel; in
+binary32 also on the vector lanes, whose prefetched loads use such offsets), an
 output and a residual of more than 2^31 elements, and a K of a million.
 Large operands repeat a seeded block of a prime number of rows, so that a
 wrapped offset would read a different row.
@@ -70,6 +71,26 @@ def test_operand_over_2gib():
     got = device_cells(run, ms, ns)
     ref = reference_cells(w, host, ms, ns)
     assert_accept(got, ref, W.F32, exact=True, what="A over 2 GiB")
+
+
+@pytest.mark.parametrize("regtile", [None, (64, 64, 64)])
+def test_f32_operand_over_2gib(regtile):
+    # A [66000][8200] binary32 = 2.16 GB: past the 32-bit offsets of the direct
+    # copies (matrix cores) and of the prefetched loads (vector lanes), so both
+    # paths take their 64-bit addressed loads
+    M, N, K = 66000, 64, 8200
+    assert M * K * 4 > 1 << 31
+    w = W.Workload("big-a-f32", M, N, K, dtype=W.F32, dist="ternary", seed=98, regtile=regtile)
+    host = {"A": tiled_bits(M, K, K, seed=98, dtype=W.F32),
+            "B": tiled_bits(K, N, N, seed=99, period=K, dtype=W.F32),
+            "bias": None, "R": None, "scale": None}
+    run = Run(w, inputs=host)
+    run.launch()
+    torch.cuda.synchronize()
+    ms, ns = boundary_cells(M, N, K, 4, 300, seed=5)
+    got = device_cells(run, ms, ns)
+    ref = reference_cells(w, host, ms, ns)
+    assert_accept(got, ref, W.F32, exact=True, what=f"binary32 A over 2 GiB, regtile={regtile}")
 
 
 def test_output_and_residual_over_2g_elements():
