@@ -64,6 +64,16 @@ def _code_tokens(src):
     return " ".join("".join(out).split())
 
 
+def device_info():
+    """The GPU the run used: name, architecture, compute units, memory."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""),
+            "compute_units": pr.multi_processor_count,
+            "L2_MiB_per_XCD": round(getattr(pr, "L2_cache_size", 0) / 2 ** 20, 1),
+            "memory_GiB": round(pr.total_memory / 2 ** 30, 1)}
+
+
 def csrc_digest():
     """Digest of the kernel sources (comments aside) and the compile flags."""
     from thread_register_tile_amd import build
@@ -265,7 +275,7 @@ def bench_reduce(args, trt, torch, np, W):
         "config": {"workload": f"block sum of {w.n} f16 elements, BLOCK={w.block}",
                    "n": w.n, "block": w.block, "op": ["sum", "max", "min"][w.op],
                    "csrc_digest": csrc_digest()},
-        "roofline": roofline, "cpu_baseline": cpu, "parity": parity,
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "device": device_info(),
     }
     print(json.dumps(line), flush=True)
 
@@ -484,6 +494,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        "device": device_info(),
     }
     print(json.dumps(out), flush=True)
 
