@@ -64,6 +64,18 @@ def _code_tokens(src):
     return " ".join("".join(out).split())
 
 
+def cpu_model():
+    """The host CPU's model name (for the oracle baseline), or "" if unknown."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def device_info():
     """The GPU the run used: name, architecture, compute units, memory."""
     import torch
@@ -260,7 +272,8 @@ def bench_reduce(args, trt, torch, np, W):
         t_cpu = time.perf_counter() - t0
         cpu = {"value": (W.ELEM_BYTES[w.dtype] * nb * w.block + 4 * nb) / t_cpu / 1e9,
                "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"blocks 0..{nb - 1} of {w.nblocks} (python + fsum, one core), {t_cpu:.1f} s"}
+               "sample": f"blocks 0..{nb - 1} of {w.nblocks} (python + fsum, one core), {t_cpu:.1f} s",
+               "cpu_model": cpu_model()}
         import oracle
         err = np.abs(got[:nb].astype(np.float64) - ref)
         absum = np.abs(oracle.decode(bits[:nb * w.block], w.dtype)).reshape(nb, w.block).sum(1)
@@ -461,7 +474,7 @@ def main():
         cpu_tflops = 2.0 * rows * w.N * w.K / t_cpu / 1e12
         cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, fp64 oracle incl. "
-                         f"epilogue), {t_cpu:.1f} s"}
+                         f"epilogue), {t_cpu:.1f} s", "cpu_model": cpu_model()}
         Cg = C.cpu().numpy().view(np.uint32 if out_bytes == 4 else np.uint16)
         Cg = Cg.reshape(w.M, w.ldc_)[:rows, :w.N]
         rep = oracle.accept(np.ascontiguousarray(Cg), ref, w.odt)
