@@ -249,12 +249,15 @@ def bench_reduce(args, trt, torch, np, W):
     for a, b in evs:
         a.record(stream); step(); b.record(stream)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_all = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = float(np.mean(kern_all))
     gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
     kgbs = w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "algorithmic_bytes": w.algorithmic_bytes, "kernel_ms": round(kern_ms, 5)}
+                "algorithmic_bytes": w.algorithmic_bytes, "kernel_ms": round(kern_ms, 5),
+                "kernel_ms_median": round(float(np.median(kern_all)), 5),
+                "kernel_ms_min": round(float(np.min(kern_all)), 5)}
     if not args.no_stream_read:
         sr = stream_read_gbps(trt, torch)
         roofline["stream_read_GBps"] = round(sr, 1)
@@ -400,7 +403,8 @@ def main():
     for a, b in evs:
         a.record(stream); step(); b.record(stream)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_all = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = float(np.mean(kern_all))
 
     tflops = w.flops / (ms * 1e-3) / 1e12
     achieved = w.flops / (kern_ms * 1e-3) / 1e12
@@ -413,6 +417,8 @@ def main():
                 "algorithmic_bytes": w.algorithmic_bytes,
                 "algorithmic_flops": w.flops,
                 "kernel_ms": round(kern_ms, 5),
+                "kernel_ms_median": round(float(np.median(kern_all)), 5),
+                "kernel_ms_min": round(float(np.min(kern_all)), 5),
                 "hbm_GBps_algorithmic": round(w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9, 1),
                 "hbm_GBps_traffic": (round(traffic / (kern_ms * 1e-3) / 1e9, 1)
                                      if traffic else None)}
