@@ -148,11 +148,12 @@ trt_status trt_validate(int64_t M, int64_t N, int64_t K,
 /*
  * trt_choose_tile -- the workgroup tile trt_gemm uses for an M x N output
  * with inputs of in_dtype (host only, no HIP call): for M <= 16 the
- * streaming tile 16x64 (K step 256); otherwise, when either pipelined tile
- * gives the 256 compute units at least 192 workgroups, the one of
- * 256x256x32 and 256x192x32 with fewer rounds of 256 workgroups times tile
- * area; otherwise 128x128x64 if it gives at least 128 workgroups, else
- * 64x64x64; binary32 inputs always 128x128x32.  Whether the pipelined
+ * streaming tile 16x64 (K step 256); otherwise, when either 256-wide
+ * pipelined tile gives the 256 compute units at least 192 workgroups, the
+ * one of 256x256x32 and 256x192x32 with fewer rounds of 256 workgroups
+ * times tile area; otherwise the pipelined 128x128x32 if it gives at least
+ * 64 workgroups, else 64x64x64; binary32 inputs always 128x128x32 (the
+ * binary32 kernel's tile).  Whether the pipelined
  * kernel or the generic one runs a pipelined tile also depends on the
  * operands' alignment and extents (see trt_gemm).  Errors: TRT_ERR_NULL,
  * TRT_ERR_SIZE (M or N outside [1, 2^30]), TRT_ERR_DTYPE.

@@ -148,7 +148,7 @@ def test_tile_table():
 
 ALL_TILES = [(16, 64, 32, 1, 1, 16), (64, 64, 64, 2, 2, 16), (128, 128, 64, 2, 2, 16),
              (256, 256, 64, 2, 2, 16), (256, 256, 32, 2, 4, 16), (256, 192, 32, 2, 2, 16),
-             (16, 64, 256, 8, 1, 16)]
+             (128, 128, 32, 2, 2, 16), (16, 64, 256, 8, 1, 16)]
 NON_GF2 = (256, 192, 32, 2, 2, 16)   # 6 fragment columns per wave: affine ownership
 SKINNY = (16, 64, 256, 8, 1, 16)
 
@@ -499,8 +499,8 @@ def _expected_tile(M, N):
     cost = lambda bm, bn: cdiv(count(bm, bn), 256) * bm * bn
     if count(256, 256) >= 192 or count(256, 192) >= 192:
         return (256, 192, 32) if cost(256, 192) < cost(256, 256) else (256, 256, 32)
-    if count(128, 128) >= 128:
-        return (128, 128, 64)
+    if count(128, 128) >= 64:
+        return (128, 128, 32)
     return (64, 64, 64)
 
 
@@ -510,6 +510,9 @@ def test_choose_tile_named_workloads():
     assert trt.choose_tile(4000, 3072) == (256, 192, 32)          # ragged: one full round
     assert trt.choose_tile(16, 16384) == (16, 64, 256)            # skinny
     assert trt.choose_tile(64, 64) == (64, 64, 64)                # tiny (runs its own tile explicitly)
+    assert trt.choose_tile(2048, 2048) == (128, 128, 32)          # mid-size: pipelined 128x128
+    assert trt.choose_tile(1024, 1024) == (128, 128, 32)
+    assert trt.choose_tile(896, 896) == (64, 64, 64)                # 49 tiles of 128x128
     assert trt.choose_tile(4096, 4096, trt.F32) == (128, 128, 32)
 
 

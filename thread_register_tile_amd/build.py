@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["trt.hip", "kern_tiny.hip", "kern_64.hip", "kern_128.hip", "kern_256.hip",
            "kern_256f.hip", "kern_dma256_f16_ak.hip", "kern_dma256_f16_am.hip",
            "kern_dma256_bf16_ak.hip", "kern_dma256_bf16_am.hip", "kern_dma192_f16.hip",
-           "kern_dma192_bf16.hip", "kern_skinny.hip", "kern_reduce.hip", "kern_f32.hip",
+           "kern_dma192_bf16.hip", "kern_dma128.hip", "kern_skinny.hip", "kern_reduce.hip", "kern_f32.hip",
            "kern_regtile.hip"]
 # Per-file flags.  The binary32 kernels keep their accumulators in ordinary
 # VGPRs: left to itself the compiler puts them in AGPRs and moves half of

@@ -14,6 +14,7 @@ using Tile256 = Tile<256, 256, 64, 2, 2>;      // 4 waves, 128x128 each
 using Tile256D = Tile<256, 256, 32, 2, 4, 16>; // pipelined, 8 waves of 8x4 fragments of 16x16
 using Tile256x192D = Tile<256, 192, 32, 2, 2, 16>;  // pipelined, 8x6 fragments of 16x16 per wave
 using Tile256F = Tile<256, 256, 32, 2, 2, 16>; // generic kernel on the pipelined tile
+using Tile128D = Tile<128, 128, 32, 2, 2, 16>; // pipelined, 4 waves of 4x4 fragments of 16x16
 
 // Launch the generic kernel of tile TL (defined, and explicitly instantiated
 // per tile, in the kern_*.hip translation units).
@@ -22,7 +23,7 @@ void launch_generic(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t 
 
 // Launch the pipelined direct-to-LDS kernel of tile TL for input type DT and
 // A storage (A_KC: k-contiguous), defined per (DT, A storage) in the
-// kern_dma256_*.hip translation units.
+// kern_dma*.hip translation units.
 template <class TL, int DT, bool A_KC>
 void launch_pipelined_a(GemmArgs a, bool b_kc, hipStream_t s);
 

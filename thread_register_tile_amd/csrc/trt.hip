@@ -40,6 +40,7 @@ using trt::Tile256x192D;
 using trt::Tile256D;
 using trt::Tile64;
 using trt::Tile128;
+using trt::Tile128D;
 using trt::TileTiny;
 
 // Whether the pipelined direct-to-LDS kernel applies: aligned 16-byte operand
@@ -74,10 +75,13 @@ void launch_tile(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) 
 }
 
 // The pipelined tile: the direct-to-LDS kernel when it applies, otherwise the
-// generic kernel on the same logical tile (with 16x16 fragments).
+// generic kernel on a tile of the same width (with 16x16 fragments).
 template <class TL>
 void launch_tile_dma(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
-  if (!dma_ok(a, opA, opB, vec)) return trt::launch_generic<trt::Tile256F>(a, dt, opA, opB, vec, s);
+  if (!dma_ok(a, opA, opB, vec)) {
+    if constexpr (TL::BM == 128) return trt::launch_generic<trt::Tile128>(a, dt, opA, opB, vec, s);
+    else return trt::launch_generic<trt::Tile256F>(a, dt, opA, opB, vec, s);
+  }
   trt::launch_pipelined<TL>(a, dt, opA, opB, s);
 }
 
@@ -302,7 +306,8 @@ constexpr TileEntry entry() {
 
 const TileEntry kTiles[] = {entry<TileTiny>(), entry<Tile64>(), entry<Tile128>(),
                             entry<Tile256>(), entry<Tile256D, true>(),
-                            entry<Tile256x192D, true>(), entry<trt::SkinnyTile>()};
+                            entry<Tile256x192D, true>(), entry<Tile128D, true>(),
+                            entry<trt::SkinnyTile>()};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 const TileEntry* find_tile(const trt_tile* t) {
@@ -317,11 +322,13 @@ const TileEntry* tile_named(int bm, int bn, int bk) {
 }
 
 // Tile choice when the caller names none.  M <= 16: the streaming tile.
-// Otherwise, when either pipelined tile gives the 256 compute units a full
-// wave of workgroups, the one that needs the least work per compute unit:
-// rounds of 256 workgroups times the tile's area (the 256x192 tile fills
-// all compute units where 256x256 tiles would leave some idle).  Smaller
-// problems take the generic kernel on 128x128 or 64x64 tiles.
+// Otherwise, when either 256-wide pipelined tile gives the 256 compute units
+// a full wave of workgroups, the one that needs the least work per compute
+// unit: rounds of 256 workgroups times the tile's area (the 256x192 tile
+// fills all compute units where 256x256 tiles would leave some idle).
+// Smaller problems take the pipelined 128x128 tile (two workgroups per
+// compute unit) when it gives at least 64 workgroups, else the generic
+// kernel on 64x64 tiles.
 const TileEntry* choose_tile(int64_t M, int64_t N) {
   auto count = [&](const TileEntry* e) { return ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn); };
   auto cost = [&](const TileEntry* e) { return (count(e) + 255) / 256 * e->bm * e->bn; };
@@ -329,7 +336,7 @@ const TileEntry* choose_tile(int64_t M, int64_t N) {
   const TileEntry* big = tile_named(256, 256, 32);
   const TileEntry* wide = tile_named(256, 192, 32);
   if (count(big) >= 192 || count(wide) >= 192) return cost(wide) < cost(big) ? wide : big;
-  if (count(tile_named(128, 128, 64)) >= 128) return tile_named(128, 128, 64);
+  if (count(tile_named(128, 128, 32)) >= 64) return tile_named(128, 128, 32);
   return tile_named(64, 64, 64);
 }
 
