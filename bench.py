@@ -324,7 +324,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for {args.gpus}); "
               "the path has no multi-GPU sharding.", file=sys.stderr)
         sys.exit(2)
 
