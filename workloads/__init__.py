@@ -105,7 +105,9 @@ class Workload:
         return b
 
 
-# The five workloads of the spec configuration sheet.
+# The five GEMM workloads shaped like the pages' examples: a tiny tile, a square
+# 4096^3 GEMM, a GEMM with bias, ReLU and residual, a transposed, ragged and
+# padded GEMM, and a skinny memory-bound GEMM.
 TINY = Workload("tiny", 64, 64, 32, dtype=F16, dist="uniform", scale=1.0,
                 seed=1, tile=(16, 64, 32))
 SQUARE = Workload("square", 4096, 4096, 4096, dtype=F16, dist="normal",
