@@ -102,6 +102,19 @@ def reference_cells(w, host, ms, ns):
     return oracle.gemm_cells(**oracle_args(w, host), ms=ms, ns=ns)
 
 
+def assert_full_output(w, host, C, n_block=None, what=""):
+    """Every element of C (M x N raw bits) against the oracle, under the
+    tolerance; in column blocks of n_block when given (the oracle decodes the
+    B columns of a block once, so a block bounds its memory)."""
+    n_block = n_block or w.N
+    for n0 in range(0, w.N, n_block):
+        nr = (n0, min(w.N, n0 + n_block))
+        ref = reference_block(w, host, None, nr)
+        assert_accept(np.ascontiguousarray(C[:, nr[0]:nr[1]]), ref, w.odt,
+                      what=f"{what or w.name} columns {nr}")
+        del ref
+
+
 def assert_accept(C_bits, Cref, dtype, exact=False, what=""):
     rep = oracle.accept(C_bits, Cref, dtype)
     assert rep["ok"], f"{what}: {rep}"

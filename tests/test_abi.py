@@ -181,11 +181,16 @@ def test_c_owner_matches_oracle(cfg):
         assert rank == ib == ob == L.log2_exact(cfg[0] * cfg[1])
 
 
-@pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (256, 256, 64, 2, 2),
-                                 (128, 128, 64, 2, 2), (256, 256, 32, 2, 2)])
+# the compiled power-of-two tiles with cooperative copy maps, with their wave
+# grids: (BM, BN, BK, waves along m, waves along n)
+@pytest.mark.parametrize("cfg", [(16, 64, 32, 1, 1), (64, 64, 64, 2, 2), (128, 128, 64, 2, 2),
+                                 (256, 256, 64, 2, 2), (256, 256, 32, 2, 4),
+                                 (128, 128, 32, 2, 2)])
 def test_lds_and_copy_maps_match_oracle(cfg):
     BM, BN, BK, WM, WN = cfg
     tile, G, T = cfg[:3], BK // 8, 64 * WM * WN
+    # the wave grid is the compiled tile's
+    assert [t[3:5] for t in trt.tiles() if t[:3] == tile] == [(WM, WN)]
     for mid, R in [(trt.MAP_LDS_SLOT_A, BM), (trt.MAP_LDS_SLOT_B, BN)]:
         slot, _ = trt.layout_dump_host(mid, tile)
         exp = [L.lds_slot(r, g, G) for r in range(R) for g in range(G)]

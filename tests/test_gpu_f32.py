@@ -14,7 +14,8 @@ import pytest
 import oracle
 import thread_register_tile_amd as trt
 import workloads as W
-from gpu_util import Run, assert_accept, reference_block, reference_cells, sample_cells
+from gpu_util import (Run, assert_accept, assert_full_output, reference_block, reference_cells,
+                      sample_cells)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,16 +135,27 @@ def test_f32_binding_with_torch_tensors():
 
 
 def test_f32square_full_size():
+    # the whole output, element by element
     w = W.F32SQUARE
     run = Run(w)
     run.launch()
-    C = run.result()
-    ms, ns = sample_cells(w, 1500, seed=w.seed)
-    assert_accept(C[ms, ns], reference_cells(w, run.host, ms, ns), W.F32, what="f32square")
-    for m0, n0 in [(0, 0), (w.M - 48, w.N - 80)]:
-        mr, nr = (m0, m0 + 48), (n0, n0 + 80)
-        assert_accept(C[mr[0]:mr[1], nr[0]:nr[1]], reference_block(w, run.host, mr, nr), W.F32,
-                      what="f32square block")
+    assert_full_output(w, run.host, run.result())
+
+
+def test_f32_overlapping_rows():
+    # rows-contiguous binary32 operands whose rows overlap (lda < M, ldb < N)
+    # with a partial last K step: the direct-copy kernel's zero rows past the
+    # operand's end do not exist there, so such strides take the other kernel
+    for trial, (opA, opB, K) in enumerate([(1, 0, 100), (1, 1, 36), (0, 0, 68)]):
+        M, N = 300, 260
+        lda = M - 44 if opA else K + 4
+        ldb = N - 36 if not opB else K + 4
+        w = replace(f32_case(M, N, K, opA, opB, 0, bool(trial % 2), seed=700 + trial,
+                             dist="ternary"), lda=lda, ldb=ldb)
+        run = Run(w)
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), W.F32, exact=True,
+                      what=f"op={opA}{opB} K={K} lda={lda} ldb={ldb}")
 
 
 def test_f32square_exact_mode():

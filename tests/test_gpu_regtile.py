@@ -13,7 +13,8 @@ import pytest
 
 import thread_register_tile_amd as trt
 import workloads as W
-from gpu_util import Run, assert_accept, reference_block, reference_cells, sample_cells
+from gpu_util import (Run, assert_accept, assert_full_output, reference_block, reference_cells,
+                      sample_cells)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,12 +68,11 @@ def test_regtile_policy_in_use():
 
 
 def test_regtile_workload_full_size():
+    # the whole output, element by element
     w = W.REGTILE
     run = Run(w)
     run.launch()
-    C = run.result()
-    ms, ns = sample_cells(w, 1200, seed=w.seed)
-    assert_accept(C[ms, ns], reference_cells(w, run.host, ms, ns), w.odt, what="regtile")
+    assert_full_output(w, run.host, run.result())
 
 
 def test_regtile_workload_exact_mode():

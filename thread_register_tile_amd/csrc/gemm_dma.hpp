@@ -128,14 +128,15 @@ struct DmaOperand {
     step_bytes = KC ? 64 : 64 * ld;
   }
 
-  // Buffer descriptor of K step `step`: based at the step's first byte, its
-  // record count what is left of the operand (zero past the end).
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int step) const {
+  // Buffer descriptor of K step `step` of nk: based at the step's first
+  // byte, its record count what is left of the operand; zero records (every
+  // copy reads zero and fetches nothing) past the operand's end and for the
+  // steps at or after nk that the pipeline issues ahead of the last one.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int step, int nk) const {
     const int64_t adv = (int64_t)step * step_bytes;
-    int64_t left = extent - adv;
-    left = left < 0 ? 0 : left;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (adv < extent ? adv : 0)),
-                                             (short)0, (int)left, 0x00020000);
+    const bool live = step < nk && adv < extent;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (live ? adv : 0)), (short)0,
+                                             live ? (int)(extent - adv) : 0, 0x00020000);
   }
   // Copy i (0 <= i < NCH) of K step `step` into LDS region `dst` (this
   // operand's part of one stage).  last_partial: K % 32 != 0 and `step` is
@@ -178,7 +179,7 @@ enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4 };
 // bias it needs -- is known at compile time.
 template <class TL>
 struct EpiShape {
-  static constexpr int BN = TL::BN;
+  static constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
   static constexpr int PANEL = is_pow2(BN) ? BN : 64;
   static constexpr int PANELS = BN / PANEL;
   static constexpr int COLS_PER_T = 4;
@@ -189,6 +190,44 @@ struct EpiShape {
   static_assert(BN % PANEL == 0 && TL::THREADS % T_PER_ROW == 0 &&
                     HALF_ROWS % ROWS_PER_STEP == 0,
                 "whole rows per step");
+
+  // Staging of the two passes.  Pass 0 takes the upper half of every wave's
+  // rows (fragment rows fm < FM/2), pass 1 the lower half; a staged row
+  // holds one tile row.  HW rows of each wave row block per pass.
+  static constexpr int HW = TL::WTM / 2;
+  TRT_HD static int pass_of(int row) { return (row % TL::WTM) / HW; }
+  TRT_HD static int staged_row(int row) { return (row / TL::WTM) * HW + row % HW; }
+  TRT_HD static int tile_row(int pass, int prow) {
+    return (prow / HW) * TL::WTM + HW * pass + prow % HW;
+  }
+
+  // The staging writes the accumulators where the layout module's ownership
+  // map puts them: for every (register run, lane, wave), the run of four
+  // registers 4*(fm*FN + fn) .. +3 is four consecutive columns of one row
+  // (starting at a multiple of 4: one 16-byte LDS write), the row is staged
+  // in the pass of its fragment row, and its staged row lies in the pass's
+  // range and maps back to it.  With the ownership map exactly once (checked
+  // where the tile is registered) every tile element is staged once per
+  // launch and stored from the row tile_row() gives back.
+  static constexpr bool staging_matches_owner() {
+    for (int w = 0; w < TL::WAVES; ++w)
+      for (int l = 0; l < 64; ++l)
+        for (int fm = 0; fm < FM; ++fm)
+          for (int fn = 0; fn < FN; ++fn) {
+            const int reg = TL::FRAG_REGS * (fm * FN + fn);
+            const int row = TL::owner_row(reg, l, w), col = TL::owner_col(reg, l, w);
+            if (col % 4 != 0) return false;
+            for (int r = 1; r < 4; ++r)
+              if (TL::owner_row(reg + r, l, w) != row || TL::owner_col(reg + r, l, w) != col + r)
+                return false;
+            const int pass = fm < FM / 2 ? 0 : 1;
+            const int prow = staged_row(row);
+            if (pass_of(row) != pass || prow < 0 || prow >= HALF_ROWS ||
+                tile_row(pass, prow) != row)
+              return false;
+          }
+    return true;
+  }
 };
 
 template <class TL, int OT, int MODE_>
@@ -208,8 +247,9 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   constexpr int BATCH = 8;                            // items read ahead of their stores
   static_assert(FM % 2 == 0 && TL::WM == 2, "two passes over the wave rows");
   static_assert(ITERS % BATCH == 0, "whole batches");
+  static_assert(TL::FRAG_REGS == 4 && ES::staging_matches_owner(),
+                "the staging follows the tile's ownership map");
   const int lane = t & 63, wave = t >> 6;
-  const int wr = wave / TL::WN, wc = wave % TL::WN;
   const int tcol = ES::COLS_PER_T * (t % T_PER_ROW);  // this thread's 4 columns in a panel
   const bool relu = p.relu != 0;
   const bool scaled = p.scale != nullptr;
@@ -218,11 +258,6 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   auto prow_of = [&](int it) { return (it / PANELS) * ES::ROWS_PER_STEP + t / T_PER_ROW; };
   auto col_of = [&](int it) { return (it % PANELS) * ES::PANEL + tcol; };
   auto bias_of = [&](int it, int e) { return bias[it % PANELS][e]; };
-  // staged row -> tile row: the wave row block, then the pass's half of it
-  auto tile_row = [&](int pass, int prow) {
-    return (prow / (HALF_ROWS / TL::WM)) * TL::WTM + (HALF_ROWS / TL::WM) * pass +
-           prow % (HALF_ROWS / TL::WM);
-  };
   // Residuals and row scales travel in a ring of RING items per thread, at
   // most 64 registers of residual (the whole pass for 16-bit outputs, up to
   // 16 items for binary32).  Item `it` is loaded when its slot frees, i.e.
@@ -231,7 +266,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   // staging writes.
   constexpr int RING = O::BYTES == 2 ? ITERS : (ITERS < 16 ? ITERS : 16);
   static_assert(RING >= BATCH, "a batch fits the ring");
-  auto row_of = [&](int pass, int it) { return m0 + tile_row(pass, prow_of(it)); };
+  auto row_of = [&](int pass, int it) { return m0 + ES::tile_row(pass, prow_of(it)); };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     typename O::Vec rr[MODE == EPI_FAST_RES ? RING : 1];
@@ -246,16 +281,17 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     };
 #pragma unroll
     for (int it = 0; it < RING; ++it) fetch(it);
-    // accumulators of the pass's fragment rows fm = (FM/2)*pass + f ->
-    // staged rows prow = 64*wr + 16*f + lane%16; a lane holds one run of 4
-    // columns 4*(lane/16) of each 16x16 fragment
+    // the pass's fragment rows fm = (FM/2)*pass + f: each run of four
+    // accumulator registers goes to the (row, column) the ownership map
+    // gives it, the row staged at staged_row(row)
 #pragma unroll
     for (int f = 0; f < FM / 2; ++f) {
       const int fm = (FM / 2) * pass + f;
-      const int prow = (HALF_ROWS / TL::WM) * wr + 16 * f + (lane & 15);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int c = wc * TL::WTN + 16 * fn + 4 * (lane >> 4);
+        const int reg = TL::FRAG_REGS * (fm * FN + fn);
+        const int prow = ES::staged_row(TL::owner_row(reg, lane, wave));
+        const int c = TL::owner_col(reg, lane, wave);
         *reinterpret_cast<f32x4*>(stage + prow * PITCH + c) = acc[fm][fn];
       }
     }
@@ -447,10 +483,12 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   const bool partial = (p.K & 31) != 0;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
+  // fragment reads start at the wave's first tile row / column: where the
+  // ownership map places register 0 of lane 0
   FragReader<TL, BM, A_KC, FM> ra;
   FragReader<TL, BN, B_KC, FN> rb;
-  ra.init((wave / TL::WN) * TL::WTM, lane, 0);
-  rb.init((wave % TL::WN) * TL::WTN, lane, OpA::BYTES);
+  ra.init(TL::owner_row(0, 0, wave), lane, 0);
+  rb.init(TL::owner_col(0, 0, wave), lane, OpA::BYTES);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -465,7 +503,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   for (int step = 0; step < NS - 1; ++step) {
     const uint32_t st = lds_base + step * STAGE;
     const bool lp = partial && step == nk - 1;
-    const auto rsa = a.rsrc(step), rsb = b.rsrc(step);
+    const auto rsa = a.rsrc(step, nk), rsb = b.rsrc(step, nk);
 #pragma unroll
     for (int i = 0; i < OpA::NCH; ++i) a.issue_one(rsa, step, st, wave, p.K, lp, i);
 #pragma unroll
@@ -486,7 +524,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
     const int step = kt + NS - 1;
     const uint32_t st = lds_base + st_copy * STAGE;
     const bool lp = partial && step == nk - 1;
-    const auto rsa = a.rsrc(step), rsb = b.rsrc(step);
+    const auto rsa = a.rsrc(step, nk), rsb = b.rsrc(step, nk);
     TRT_LDS char* nxt = lds + st_next * STAGE;
     st_copy = st_copy == NS - 1 ? 0 : st_copy + 1;
     st_next = st_next == NS - 1 ? 0 : st_next + 1;
@@ -525,8 +563,8 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = HM; i < FM; ++i) fa[i] = ra.read(nxt, i);
   }
-  // drain the copies issued past the end (they read nothing) and all LDS
-  // reads before the staging area reuses the stages
+  // drain the copies issued past the end (zero records: they fetch nothing)
+  // and all LDS reads before the staging area reuses the stages
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
   __syncthreads();

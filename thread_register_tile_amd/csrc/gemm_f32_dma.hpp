@@ -94,12 +94,14 @@ struct F32DmaOperand {
     step_bytes = KC ? 32 * 4 : 32 * 4 * ld;
   }
 
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int step) const {
+  // Descriptor of K step `step` of nk: zero records (nothing fetched) past
+  // the operand's end and for the step after the last, whose copies the
+  // last iteration issues.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int step, int nk) const {
     const int64_t adv = (int64_t)step * step_bytes;
-    int64_t left = extent - adv;
-    left = left < 0 ? 0 : left;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (adv < extent ? adv : 0)),
-                                             (short)0, (int)left, 0x00020000);
+    const bool live = step < nk && adv < extent;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (live ? adv : 0)), (short)0,
+                                             live ? (int)(extent - adv) : 0, 0x00020000);
   }
 
   // Copy i of K step `step` into the region at LDS byte address dst.
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256) void gemm_f32_dma_kernel(GemmArgs p) {
     else b.issue(rsb, step, st + L::BYTES, wave, p.K, lp, c - L::NCH);
   };
   {
-    const auto rsa = a.rsrc(0), rsb = b.rsrc(0);
+    const auto rsa = a.rsrc(0, nk), rsb = b.rsrc(0, nk);
 #pragma unroll
     for (int c = 0; c < LOADS; ++c) copy(rsa, rsb, 0, c);
   }
@@ -179,12 +181,12 @@ __global__ __launch_bounds__(256) void gemm_f32_dma_kernel(GemmArgs p) {
   // products) and this thread's copies of step kt+1 (one every eight
   // products, into the other stage, last read before the previous barrier)
   // in a fixed order; then the second half's 64 products; then the wait for
-  // the copies and the barrier.  After the last step the copies bring zeros
-  // or unread data into the stage that no later step reads.
+  // the copies and the barrier.  The last step's copies (of step nk) read
+  // zeros into the stage that no later step reads.
   for (int kt = 0; kt < nk; ++kt) {
     const TRT_LDS float* la = lds + (kt & 1) * (STAGE / 4);
     const TRT_LDS float* lb = la + L::BYTES / 4;
-    const auto rsa = a.rsrc(kt + 1), rsb = b.rsrc(kt + 1);
+    const auto rsa = a.rsrc(kt + 1, nk), rsb = b.rsrc(kt + 1, nk);
     f32x4 af[FM][2], bf[FN][2];
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i][0] = f32_frag<A_KC>(la, wrow + 16 * i + fr, g, 0);

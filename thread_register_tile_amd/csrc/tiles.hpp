@@ -16,40 +16,43 @@ using Tile256x192D = Tile<256, 192, 32, 2, 2, 16>;  // pipelined, 8x6 fragments 
 using Tile256F = Tile<256, 256, 32, 2, 2, 16>; // generic kernel on the pipelined tile
 using Tile128D = Tile<128, 128, 32, 2, 2, 16>; // pipelined, 4 waves of 4x4 fragments of 16x16
 
-// Launch the generic kernel of tile TL (defined, and explicitly instantiated
-// per tile, in the kern_*.hip translation units).
+// Every launch function returns the runtime's status of its own launch.
+
+// Launch the generic kernel of tile TL (defined in kern_generic.hpp, and
+// explicitly instantiated per tile in the kern_*.hip translation units).
 template <class TL>
-void launch_generic(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s);
+hipError_t launch_generic(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s);
 
 // Launch the pipelined direct-to-LDS kernel of tile TL for input type DT and
-// A storage (A_KC: k-contiguous), defined per (DT, A storage) in the
-// kern_dma*.hip translation units.
+// A storage (A_KC: k-contiguous), defined in kern_pipelined.hpp and
+// instantiated per (tile, DT, A storage) in the kern_dma*.hip units.
 template <class TL, int DT, bool A_KC>
-void launch_pipelined_a(GemmArgs a, bool b_kc, hipStream_t s);
+hipError_t launch_pipelined_a(GemmArgs a, bool b_kc, hipStream_t s);
 
 template <class TL>
-inline void launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s) {
+inline hipError_t launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStream_t s) {
   a.tiles_m = (a.M + TL::BM - 1) / TL::BM;
   a.tiles_n = (a.N + TL::BN - 1) / TL::BN;
   const bool akc = opA == 0, bkc = opB == 1;
   if (dt == DT_F16)
-    akc ? launch_pipelined_a<TL, DT_F16, true>(a, bkc, s) : launch_pipelined_a<TL, DT_F16, false>(a, bkc, s);
-  else
-    akc ? launch_pipelined_a<TL, DT_BF16, true>(a, bkc, s) : launch_pipelined_a<TL, DT_BF16, false>(a, bkc, s);
+    return akc ? launch_pipelined_a<TL, DT_F16, true>(a, bkc, s)
+               : launch_pipelined_a<TL, DT_F16, false>(a, bkc, s);
+  return akc ? launch_pipelined_a<TL, DT_BF16, true>(a, bkc, s)
+             : launch_pipelined_a<TL, DT_BF16, false>(a, bkc, s);
 }
 
 // Launch the HBM-streaming kernel for M <= 16 (kern_skinny.hip).
-void launch_skinny(GemmArgs a, int dt, hipStream_t s);
+hipError_t launch_skinny(GemmArgs a, int dt, hipStream_t s);
 
 // Launch the binary32-operand GEMM on its 128x128x32 tile (kern_f32.hip).
-void launch_f32(GemmArgs a, int opA, int opB, bool vec, hipStream_t s);
+hipError_t launch_f32(GemmArgs a, int opA, int opB, bool vec, hipStream_t s);
 
 // Launch the register-tile GEMM on vector lanes (kern_regtile.hip).
 struct RegtileArgs;
-void launch_regtile(RegtileArgs a, int dt, hipStream_t s);
+hipError_t launch_regtile(RegtileArgs a, int dt, hipStream_t s);
 
 // Launch the rank-1 block reduction (kern_reduce.hip).
 struct ReduceArgs;
-void launch_reduce(const ReduceArgs& a, int dt, int op, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, int dt, int op, hipStream_t s);
 
 }  // namespace trt

@@ -9,6 +9,7 @@
 #include "../../include/trt.h"
 #include "gemm_kernel.hpp"
 #include "gemm_skinny.hpp"
+#include "launch.hpp"
 #include "reduce.hpp"
 #include "regtile.hpp"
 #include "tiles.hpp"
@@ -23,8 +24,8 @@ trt_status fail(trt_status s, const std::string& msg) {
   return s;
 }
 
-trt_status check_launch(const char* what) {
-  const hipError_t e = hipGetLastError();
+// The status of one launch, as the runtime returned it for that launch.
+trt_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(TRT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
   g_err.clear();
@@ -47,10 +48,15 @@ using trt::TileTiny;
 // rows; every 16-byte copy wholly inside or wholly outside its operand's
 // extent (the buffer record check drops a copy that straddles the end as a
 // whole), i.e. K % 8 == 0 for a k-contiguous operand and M (N) % 8 == 0 for
-// a rows-contiguous A (B); operand extents addressable by 32-bit offsets.
+// a rows-contiguous A (B); rows of a rows-contiguous operand that do not
+// overlap (lda >= M, ldb >= N), so that its rows k >= K on a partial last K
+// step start past the extent and read as zero; operand extents addressable
+// by 32-bit offsets.  Other shapes and strides take the generic kernel,
+// which masks k >= K explicitly.
 bool dma_ok(const GemmArgs& a, int opA, int opB, bool vec) {
   const bool a_kc = opA == TRT_OP_N, b_kc = opB == TRT_OP_T;
-  return vec && (a_kc ? a.K % 8 == 0 : a.M % 8 == 0) && (b_kc ? a.K % 8 == 0 : a.N % 8 == 0) &&
+  return vec && (a_kc ? a.K % 8 == 0 : a.M % 8 == 0 && a.lda >= a.M) &&
+         (b_kc ? a.K % 8 == 0 : a.N % 8 == 0 && a.ldb >= a.N) &&
          a.a_bytes < (int64_t(1) << 31) && a.b_bytes < (int64_t(1) << 31);
 }
 
@@ -64,25 +70,25 @@ bool skinny_ok(const GemmArgs& a, int opA, int opB) {
 
 // The streaming tile: the skinny kernel when it applies, otherwise the
 // generic kernel on the 16x64 tile.
-void launch_tile_skinny(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
+hipError_t launch_tile_skinny(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
   if (!skinny_ok(a, opA, opB)) return trt::launch_generic<TileTiny>(a, dt, opA, opB, vec, s);
-  trt::launch_skinny(a, dt, s);
+  return trt::launch_skinny(a, dt, s);
 }
 
 template <class TL>
-void launch_tile(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
-  trt::launch_generic<TL>(a, dt, opA, opB, vec, s);
+hipError_t launch_tile(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
+  return trt::launch_generic<TL>(a, dt, opA, opB, vec, s);
 }
 
 // The pipelined tile: the direct-to-LDS kernel when it applies, otherwise the
 // generic kernel on a tile of the same width (with 16x16 fragments).
 template <class TL>
-void launch_tile_dma(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
+hipError_t launch_tile_dma(GemmArgs a, int dt, int opA, int opB, bool vec, hipStream_t s) {
   if (!dma_ok(a, opA, opB, vec)) {
     if constexpr (TL::BM == 128) return trt::launch_generic<trt::Tile128>(a, dt, opA, opB, vec, s);
     else return trt::launch_generic<trt::Tile256F>(a, dt, opA, opB, vec, s);
   }
-  trt::launch_pipelined<TL>(a, dt, opA, opB, s);
+  return trt::launch_pipelined<TL>(a, dt, opA, opB, s);
 }
 
 // ---- layout maps (host and device evaluate the same functions) ---------------
@@ -226,18 +232,17 @@ __global__ __launch_bounds__(64) void probe32_kernel(const trt::u32x4* a, const 
 
 struct TileEntry {
   int bm, bn, bk, wm, wn, regs, frag;
-  void (*launch)(GemmArgs, int, int, int, bool, hipStream_t);
+  hipError_t (*launch)(GemmArgs, int, int, int, bool, hipStream_t);
   int64_t (*size)(int);
   void (*eval)(int, int64_t, int&, int&);
-  void (*dump)(int, int32_t*, int32_t*, int64_t, hipStream_t);
+  hipError_t (*dump)(int, int32_t*, int32_t*, int64_t, hipStream_t);
   int rank, in_bits, out_bits;
 };
 
 template <class TL>
-void dump_launch(int map, int32_t* rows, int32_t* cols, int64_t n, hipStream_t s) {
+hipError_t dump_launch(int map, int32_t* rows, int32_t* cols, int64_t n, hipStream_t s) {
   const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL((dump_kernel<TL>), dim3((unsigned)blocks), dim3(256), 0, s, map, rows, cols,
-                     n);
+  return trt::launch(dump_kernel<TL>, dim3((unsigned)blocks), dim3(256), 0, s, map, rows, cols, n);
 }
 
 template <class TL>
@@ -594,11 +599,10 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   const uintptr_t va = 4 * (uintptr_t)trt::elem_bytes(out_dtype);
   a.epi_vec = aligned(C, va) && ldc % 4 == 0 && (!a.bias || aligned(a.bias, va)) &&
               (!a.R || (aligned(a.R, va) && a.ldr % 4 == 0));
-  if (in_dtype == TRT_F32)
-    trt::launch_f32(a, opA, opB, vec, static_cast<hipStream_t>(stream));
-  else
-    e->launch(a, in_dtype, opA, opB, vec, static_cast<hipStream_t>(stream));
-  return check_launch("gemm launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(in_dtype == TRT_F32 ? trt::launch_f32(a, opA, opB, vec, st)
+                                      : e->launch(a, in_dtype, opA, opB, vec, st),
+                  "gemm launch");
 }
 
 trt_status trt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
@@ -673,8 +677,8 @@ trt_status trt_layout_dump(int32_t map_id, const trt_tile* tile, int32_t* rows, 
   if (size < 0) return fail(TRT_ERR_ARG, "unknown map id");
   if (n != size) return fail(TRT_ERR_SIZE, "n must equal trt_layout_size(map_id, tile)");
   if (!rows || !cols) return fail(TRT_ERR_NULL, "rows and cols must be non-null");
-  e->dump(map_id, rows, cols, n, static_cast<hipStream_t>(stream));
-  return check_launch("layout dump launch");
+  return launched(e->dump(map_id, rows, cols, n, static_cast<hipStream_t>(stream)),
+                  "layout dump launch");
 }
 
 trt_status trt_layout_rank(const trt_tile* tile, int32_t* rank, int32_t* in_bits,
@@ -703,20 +707,18 @@ trt_status trt_mfma_probe(int32_t dtype, int32_t shape, const void* a, const voi
   const auto* av = static_cast<const trt::u32x4*>(a);
   const auto* bv = static_cast<const trt::u32x4*>(b);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
   if (shape == 16) {
     auto* cv = reinterpret_cast<trt::f32x4*>(c);
-    if (dtype == TRT_F16)
-      hipLaunchKernelGGL((probe_kernel<trt::DT_F16>), dim3(1), dim3(64), 0, s, av, bv, cv);
-    else
-      hipLaunchKernelGGL((probe_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+    e = dtype == TRT_F16 ? trt::launch(probe_kernel<trt::DT_F16>, dim3(1), dim3(64), 0, s, av, bv, cv)
+                         : trt::launch(probe_kernel<trt::DT_BF16>, dim3(1), dim3(64), 0, s, av, bv, cv);
   } else {
     auto* cv = reinterpret_cast<trt::f32x16*>(c);
-    if (dtype == TRT_F16)
-      hipLaunchKernelGGL((probe32_kernel<trt::DT_F16>), dim3(1), dim3(64), 0, s, av, bv, cv);
-    else
-      hipLaunchKernelGGL((probe32_kernel<trt::DT_BF16>), dim3(1), dim3(64), 0, s, av, bv, cv);
+    e = dtype == TRT_F16
+            ? trt::launch(probe32_kernel<trt::DT_F16>, dim3(1), dim3(64), 0, s, av, bv, cv)
+            : trt::launch(probe32_kernel<trt::DT_BF16>, dim3(1), dim3(64), 0, s, av, bv, cv);
   }
-  return check_launch("probe launch");
+  return launched(e, "probe launch");
 }
 
 trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink, int64_t sink_bytes,
@@ -732,10 +734,11 @@ trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink, int64_t 
   if (x0 < s0 + (uintptr_t)TRT_READ_PROBE_SINK_BYTES && s0 < x0 + (uintptr_t)bytes)
     return fail(TRT_ERR_OVERLAP, "sink must not overlap x");
   static_assert(kReadProbeBlocks * 16 == TRT_READ_PROBE_SINK_BYTES, "one digest per workgroup");
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(kReadProbeBlocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const trt::u32x4*>(x),
-                     bytes / 16, static_cast<trt::u32x4*>(sink));
-  return check_launch("read probe launch");
+  return launched(trt::launch(hbm_read_kernel, dim3(kReadProbeBlocks), dim3(256), 0,
+                              static_cast<hipStream_t>(stream),
+                              static_cast<const trt::u32x4*>(x), bytes / 16,
+                              static_cast<trt::u32x4*>(sink)),
+                  "read probe launch");
 }
 
 trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iters, float* sink,
@@ -755,16 +758,12 @@ trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iter
   const auto* src = static_cast<const trt::u32x4*>(operands);
   auto* dst = reinterpret_cast<trt::f32x16*>(sink);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == TRT_F16)
-    hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_F16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
-                       iters, dst);
-  else if (dtype == TRT_F32)
-    hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_F32>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
-                       iters, dst);
-  else
-    hipLaunchKernelGGL(mfma_loop_kernel<trt::DT_BF16>, dim3(kMfmaProbeBlocks), dim3(256), 0, s, src,
-                       iters, dst);
-  return check_launch("matrix-core probe launch");
+  const dim3 grid(kMfmaProbeBlocks), block(256);
+  const hipError_t e =
+      dtype == TRT_F16   ? trt::launch(mfma_loop_kernel<trt::DT_F16>, grid, block, 0, s, src, iters, dst)
+      : dtype == TRT_F32 ? trt::launch(mfma_loop_kernel<trt::DT_F32>, grid, block, 0, s, src, iters, dst)
+                         : trt::launch(mfma_loop_kernel<trt::DT_BF16>, grid, block, 0, s, src, iters, dst);
+  return launched(e, "matrix-core probe launch");
 }
 
 trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dtype, int32_t op,
@@ -790,8 +789,8 @@ trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dty
   a.block = block;
   a.nblocks = nblocks;
   a.vec = aligned(x, 16) && (block * esz) % 16 == 0;
-  trt::launch_reduce(a, dtype, op, static_cast<hipStream_t>(stream));
-  return check_launch("block reduction launch");
+  return launched(trt::launch_reduce(a, dtype, op, static_cast<hipStream_t>(stream)),
+                  "block reduction launch");
 }
 
 trt_status trt_regtile_thread_shape(int32_t lm, int32_t ln, int32_t max_threads, int32_t* tm,
@@ -879,8 +878,8 @@ trt_status trt_gemm_regtile(int64_t M, int64_t N, int64_t K, const void* A, int6
   trt::span_bytes(opB ? N : K, opB ? K : N, ldb, sb, isz);
   a.g.a_bytes = sa;
   a.g.b_bytes = sb;
-  trt::launch_regtile(a, in_dtype, static_cast<hipStream_t>(stream));
-  return check_launch("register-tile gemm launch");
+  return launched(trt::launch_regtile(a, in_dtype, static_cast<hipStream_t>(stream)),
+                  "register-tile gemm launch");
 }
 
 int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }

@@ -12,7 +12,9 @@ stored transposed), rounded to the element type (float16: numpy's
 float64->float16 conversion; bfloat16: float64->float32, then
 round-to-nearest-even on the float32 bits; float32: numpy's float64->float32
 conversion) and written into a padded buffer whose leading-dimension padding
-holds NaN, so that any read of the padding poisons the result.  A and B use
+holds NaN, so that any read of the padding poisons the result.  A leading
+dimension below the row length (rows that overlap in memory) draws the
+operand's whole extent, (rows - 1)*ld + cols values, as one row.  A and B use
 the input type; bias, residual and row scale use the output type.
 """
 from dataclasses import dataclass, field, replace
@@ -196,6 +198,11 @@ def _draw(w: Workload, tensor_id: int, rows: int, cols: int) -> np.ndarray:
 
 def _padded(w: Workload, tensor_id: int, rows: int, cols: int, ld: int, dtype=None) -> np.ndarray:
     dtype = dtype or w.dtype
+    if ld < cols:
+        # overlapping rows (a positive stride below the row length): element
+        # (r, c) sits at r*ld + c, so the buffer is the operand's extent,
+        # drawn as one row of (rows - 1)*ld + cols values
+        return to_bits(_draw(w, tensor_id, 1, (rows - 1) * ld + cols), dtype).reshape(-1)
     bits = to_bits(_draw(w, tensor_id, rows, cols), dtype)
     buf = np.full((rows, ld), NAN_BITS[dtype], dtype=bits.dtype)
     buf[:, :cols] = bits
