@@ -4,18 +4,28 @@
 A step is one call of the whole hot path -- validation, tile selection and
 the single fused GEMM kernel -- on the workload's operands, already resident
 in HBM.  The default workload is the 4096^3 fp16 GEMM (fp32 accumulation,
-fp16 output) with inputs N(0,1)/8.  Prints ONE JSON line:
+fp16 output) with inputs N(0,1)/8.
 
-  value        whole-job TFLOP/s = 2*M*N*K / average step time
+Order of a run: the real-time counter's rate (one long clock probe timed
+with events); the yardsticks -- the streaming read, then the matrix-core-only
+loop for about --settle-ms (which also brings the part from its idle clock
+to its loaded one); --warmup untimed steps; a clock probe; exactly --steps
+steps timed back to back between two HIP events on the launch stream; a
+clock probe; the oracle on the host.  Prints ONE JSON line:
+
+  value        whole-job TFLOP/s = 2*M*N*K / mean step time of the timed region
   roofline     the GEMM kernel against the dense fp16 matrix-core peak
                (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk), or for
-               the M <= 16 workload against the 8 TB/s HBM peak; its HBM
-               GB/s; the read bandwidth of a plain streaming kernel measured
-               in the same run (context); and, when the committed rocprofv3
+               the M <= 16 workload against the 8 TB/s HBM peak, from the
+               same timed region (a step is one kernel launch); the shader
+               clock right before and right after it; its HBM GB/s; the
+               yardsticks' rates (context); and, when the committed rocprofv3
                counters were taken on the current kernel source, the HBM
-               traffic and matrix-core figures from those counters
+               traffic and matrix-core figures from those counters, with
+               where they were taken
   cpu_baseline the oracle (plain fp64 C, all host cores) timed on a bounded
-               row sample of the same workload, scaled to TFLOP/s
+               row sample of the same workload, scaled to TFLOP/s, and its
+               one-core rate on a slice of it
   parity       the GPU result on the same sampled rows against the oracle
 """
 import argparse
@@ -131,12 +141,21 @@ def ingest_counters(root):
     SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE and
     SQ_LDS_BANK_CONFLICT.  Each counter is scaled by what it reads for the
     256 MiB device-to-device copy of the same run (read and written bytes
-    known), and the GEMM launches' median is kept."""
+    known), and the GEMM launches' median is kept.  root/provenance.json, if
+    present, is stored with every workload's figures."""
     import workloads as W
     out = {}
+    # where and how the counters were taken: root/provenance.json, written
+    # by whoever ran the profiler (date, GPU, commands), kept with the figures
+    prov = {}
+    try:
+        with open(os.path.join(root, "provenance.json")) as f:
+            prov = json.load(f)
+    except (OSError, ValueError):
+        pass
     for w in WORKLOADS:
         cfg = W.CONFIGS[w]
-        e = {"csrc_digest": csrc_digest()}
+        e = {"csrc_digest": csrc_digest(), "provenance": prov}
         for cn, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
             path = os.path.join(root, f"pmc_{cn}_{w}", "run_counter_collection.csv")
             if not os.path.exists(path):
@@ -180,13 +199,14 @@ def ingest_counters(root):
     return out
 
 
-def stream_read_gbps(trt, torch, nbytes=1 << 30, reps=20):
+def stream_read_gbps(trt, torch, nbytes=1 << 30, reps=20, settle_ms=0.0):
     """Read bandwidth of the library's plain streaming-read kernel over a
-    buffer larger than the last-level cache, timed like the GEMM."""
+    buffer larger than the last-level cache: `reps` launches timed back to
+    back with events, after enough untimed ones to fill settle_ms."""
     x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.empty(trt.READ_PROBE_SINK_BYTES, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(5):
+    for _ in range(max(5, int(settle_ms / 0.17))):       # ~0.17 ms per 1 GiB read
         trt.hbm_read_probe(x, sink)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -199,26 +219,60 @@ def stream_read_gbps(trt, torch, nbytes=1 << 30, reps=20):
     return nbytes / s / 1e9
 
 
-def mfma_loop_tflops(trt, torch, host_a, dtype, kern_ms, launches):
+def mfma_loop_tflops(trt, torch, host_a, dtype, run_ms, launch_ms=0.1, reps=20):
     """Rate of the library's matrix-core-only loop on operand words taken from
-    the workload's own A data, each launch sized to last about as long as one
-    GEMM launch and run as many times as the GEMM was (warmup + timed)."""
+    the workload's own A data: launches of about launch_ms each, back to back
+    for about run_ms in all; the last `reps` are timed with events."""
     import numpy as np
     words = np.resize(host_a, trt.MFMA_PROBE_OPERAND_BYTES // host_a.itemsize)  # repeats a short input
     ops = torch.from_numpy(words.view(np.int8)).cuda()
     sink = torch.empty(trt.MFMA_PROBE_SINK_BYTES // 4, dtype=torch.float32, device="cuda")
-    iters = max(1, int(kern_ms * 1e-3 * 1.8e9 / (32 * 32)))   # 32 products of 32 cycles per round
+    iters = max(1, int(launch_ms * 1e-3 * 1.8e9 / (32 * 32)))   # 32 products of 32 cycles per round
     stream = torch.cuda.current_stream()
-    for _ in range(max(launches - 20, 0)):
+    for _ in range(max(0, int(run_ms / launch_ms) - reps)):
         trt.mfma_loop_probe(ops, iters, dtype, sink)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(20):
+    for _ in range(reps):
         trt.mfma_loop_probe(ops, iters, dtype, sink)
     e1.record(stream)
     torch.cuda.synchronize()
-    s = e0.elapsed_time(e1) / 20 * 1e-3
+    s = e0.elapsed_time(e1) / reps * 1e-3
     return trt.mfma_loop_probe_flops(iters, dtype) / s / 1e12
+
+
+class Clock:
+    """Shader clock from the library's clock probe (cycles over real-time
+    ticks).  The real-time counter's rate is measured once, by timing a long
+    probe with events; each reading is a short probe enqueued on the current
+    stream, read back after the next synchronisation."""
+
+    def __init__(self, trt, torch):
+        self.trt, self.torch = trt, torch
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ticks = 200_000
+        trt.clock_probe(ticks)                      # first launch: not timed
+        e0.record(s)
+        out = trt.clock_probe(ticks)
+        e1.record(s)
+        torch.cuda.synchronize()
+        self.rt_hz = float(out[:, 1].float().median().item()) / (e0.elapsed_time(e1) * 1e-3)
+        self.pending = {}
+
+    def mark(self, name, ticks=2000):
+        """Enqueue a reading of about ticks / rt_hz seconds (20 us at 100 MHz)."""
+        self.pending[name] = self.trt.clock_probe(ticks)
+
+    def ghz(self, name):
+        c = self.pending[name].cpu().numpy()
+        return round(float((c[:, 0] / c[:, 1]).mean()) * self.rt_hz / 1e9, 3)
+
+
+def counters_entry(counters):
+    """Where the committed counter figures came from."""
+    return {"file": "profiles/counters.json", "csrc_digest": counters.get("csrc_digest"),
+            **counters.get("provenance", {})}
 
 
 def bench_reduce(args, trt, torch, np, W):
@@ -234,6 +288,8 @@ def bench_reduce(args, trt, torch, np, W):
     def step():
         trt.block_reduce_raw(x.data_ptr(), w.n, w.block, w.dtype, w.op, out.data_ptr(), sptr)
 
+    # the streaming-read yardstick first, for about --settle-ms (see main())
+    sr = None if args.no_stream_read else stream_read_gbps(trt, torch, settle_ms=args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -244,24 +300,15 @@ def bench_reduce(args, trt, torch, np, W):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(min(args.steps, 20))]
-    for a, b in evs:
-        a.record(stream); step(); b.record(stream)
-    torch.cuda.synchronize()
-    kern_all = [a.elapsed_time(b) for a, b in evs]
-    kern_ms = float(np.mean(kern_all))
     gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
-    kgbs = w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "algorithmic_bytes": w.algorithmic_bytes, "kernel_ms": round(kern_ms, 5),
-                "kernel_ms_median": round(float(np.median(kern_all)), 5),
-                "kernel_ms_min": round(float(np.min(kern_all)), 5)}
-    if not args.no_stream_read:
-        sr = stream_read_gbps(trt, torch)
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_bytes": w.algorithmic_bytes, "kernel_ms": round(ms, 5),
+                "timing": f"mean of {args.steps} back-to-back launches between HIP events "
+                          "on the launch stream (the timed region)"}
+    if sr is not None:
         roofline["stream_read_GBps"] = round(sr, 1)
-        roofline["frac_of_stream_read"] = round(kgbs / sr, 4)
+        roofline["frac_of_stream_read"] = round(gbs / sr, 4)
     cpu = parity = None
     if not args.no_cpu_baseline:
         got = out.cpu().numpy()
@@ -296,14 +343,66 @@ def bench_reduce(args, trt, torch, np, W):
     print(json.dumps(line), flush=True)
 
 
+def oracle_rows(oracle, w, host, rows, threads, n_range=None):
+    """The oracle on rows 0..rows-1 (and n_range) of workload w; (result, seconds)."""
+    t0 = time.perf_counter()
+    ref = oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_, w.opB,
+                            w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
+                            ldr=w.ldr_ if host["R"] is not None else 0, out_dtype=w.odt,
+                            scale=host["scale"], m_range=(0, rows), n_range=n_range,
+                            threads=threads)
+    return ref, time.perf_counter() - t0
+
+
+def cpu_baseline(args, w, host, C, np):
+    """The oracle timed on the host cores: a row sample of the workload sized
+    to about --cpu-seconds on all cores the process may use, plus a one-core
+    rate on a slice of it; the sample also serves as the run's parity check."""
+    import oracle
+    threads = oracle.default_threads()
+    # calibrate: the per-call cost (decoding B once) and the per-row cost,
+    # from two short runs; then size the sample to the budget
+    r1, r2 = min(threads, w.M), min(4 * threads, w.M)
+    t1 = oracle_rows(oracle, w, host, r1, threads)[1]
+    t2 = oracle_rows(oracle, w, host, r2, threads)[1]
+    per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
+    fixed = max(t1 - r1 * per_row, 0.0)
+    rows = int(min(w.M, max(r1, (args.cpu_seconds - fixed) / per_row)))
+    rows = max(1, rows - rows % max(1, min(threads, rows)))
+    ref, t_cpu = oracle_rows(oracle, w, host, rows, threads)
+    # one core: the first rows (at most 64) over at most 1024 columns
+    r1c, n1c = min(64, w.M), min(1024, w.N)
+    t_1 = oracle_rows(oracle, w, host, r1c, 1, n_range=(0, n1c))[1]
+    cpu = {"value": 2.0 * rows * w.N * w.K / t_cpu / 1e12, "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, fp64 oracle incl. "
+                     f"epilogue), {t_cpu:.1f} s on {threads} threads",
+           "per_core": {"value": 2.0 * r1c * n1c * w.K / t_1 / 1e12, "unit": "TFLOP/s",
+                        "sample": f"rows 0..{r1c - 1}, columns 0..{n1c - 1}, one thread, "
+                                  f"{t_1:.2f} s"},
+           "cpu_model": cpu_model()}
+    out_bytes = W_ELEM_BYTES[w.odt]
+    Cg = C.cpu().numpy().view(np.uint32 if out_bytes == 4 else np.uint16)
+    Cg = Cg.reshape(w.M, w.ldc_)[:rows, :w.N]
+    rep = oracle.accept(np.ascontiguousarray(Cg), ref, w.odt)
+    parity = {"rows": rows, "ok": rep["ok"], "max_abs": rep["max_abs"],
+              "frob_rel": rep["frob_rel"], "bit_match": rep["bit_match"]}
+    return cpu, parity
+
+
+W_ELEM_BYTES = {1: 2, 2: 2, 3: 4}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first: the clock settles under sustained load")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square")
     ap.add_argument("--tile", default=None, help="BM,BN,BK")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="wall time of the yardsticks run before the GEMM (the part leaves "
+                         "its idle clock over the first ~20 ms of load)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -353,6 +452,7 @@ def main():
                     device="cuda")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
+    mfma_bound = w.name != "skinny" and w.regtile is None
 
     def step_regtile():
         lm, ln, mt = w.regtile
@@ -373,6 +473,23 @@ def main():
                      ldr=w.ldr_ if R is not None else 0,
                      scale=scale.data_ptr() if scale is not None else 0, tile=tile, stream=sptr)
 
+    clock = Clock(trt, torch)
+
+    # The yardsticks first: the streaming read (HBM context), then the
+    # matrix-core-only loop on the workload's own A data for about
+    # --settle-ms.  Besides their rates, they take the part out of its idle
+    # clock state, so that the GEMM below is timed under load, as the
+    # yardstick is; the clock probes record the clock around the timed region.
+    roofline_ctx = {}
+    if not args.no_stream_read:
+        sr = stream_read_gbps(trt, torch, settle_ms=0.0 if mfma_bound else args.settle_ms)
+        roofline_ctx["stream_read_GBps"] = round(sr, 1)
+    if mfma_bound and not args.no_mfma_loop:
+        a_rows = host["A"].reshape(-1)[:w.a_cols] if w.lda_ < w.a_cols else \
+            host["A"].reshape(w.a_rows, w.lda_)[:, :w.a_cols].reshape(-1)   # no padding
+        roofline_ctx["mfma_loop_tflops"] = round(
+            mfma_loop_tflops(trt, torch, a_rows, w.dtype, args.settle_ms), 1)
+
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.int16, device="cuda")
@@ -384,108 +501,72 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    clock.mark("before")
     torch.cuda.synchronize()
 
     # timed region: events on the launch stream bracket exactly `steps` calls
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
         step()
     ev1.record(stream)
+    clock.mark("after")
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
 
-    # per-launch durations on the same stream, for the kernel average
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(min(args.steps, 20))]
-    for a, b in evs:
-        a.record(stream); step(); b.record(stream)
-    torch.cuda.synchronize()
-    kern_all = [a.elapsed_time(b) for a, b in evs]
-    kern_ms = float(np.mean(kern_all))
-
+    # A step is one launch of one kernel, enqueued back to back: the timed
+    # region's mean per launch is the kernel's average duration plus the
+    # gap between launches (a few microseconds), so value and roofline
+    # share one timing.
     tflops = w.flops / (ms * 1e-3) / 1e12
-    achieved = w.flops / (kern_ms * 1e-3) / 1e12
     counters = committed_counters(w.name)
     traffic = counters.get("bytes_per_launch") if counters else None
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2),
                 "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
+                "frac": round(tflops / PEAK_TFLOPS[w.dtype], 4),
                 "traffic": traffic,
                 "algorithmic_bytes": w.algorithmic_bytes,
                 "algorithmic_flops": w.flops,
-                "kernel_ms": round(kern_ms, 5),
-                "kernel_ms_median": round(float(np.median(kern_all)), 5),
-                "kernel_ms_min": round(float(np.min(kern_all)), 5),
-                "hbm_GBps_algorithmic": round(w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9, 1),
-                "hbm_GBps_traffic": (round(traffic / (kern_ms * 1e-3) / 1e9, 1)
-                                     if traffic else None)}
+                "timing": f"mean of {args.steps} back-to-back launches between HIP events "
+                          "on the launch stream (the timed region)",
+                "kernel_ms": round(ms, 5),
+                "clock_ghz": {"before": clock.ghz("before"), "after": clock.ghz("after"),
+                              "realtime_counter_MHz": round(clock.rt_hz / 1e6, 2),
+                              "probe": "one wave per compute unit, 20 us, enqueued right "
+                                       "before and right after the timed region; a light "
+                                       "load, so it reads the clock the part offers, "
+                                       "which its matrix cores lower under load"},
+                "hbm_GBps_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1)}
+    if traffic:
+        roofline["hbm_GBps_traffic"] = round(traffic / (ms * 1e-3) / 1e9, 1)
+        roofline["traffic_source"] = counters_entry(counters)
     if w.name == "skinny":
-        gbs = w.algorithmic_bytes / (kern_ms * 1e-3) / 1e9
+        gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
         roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "tflops": round(achieved, 2)})
+                         "tflops": round(tflops, 2)})
     if w.regtile is not None:
         roofline.update({"bound": "alu", "peak": round(PEAK_VALU_F32_TFLOPS, 1),
-                         "frac": round(achieved / PEAK_VALU_F32_TFLOPS, 4),
+                         "frac": round(tflops / PEAK_VALU_F32_TFLOPS, 4),
                          "regtile": {"lm": w.regtile[0], "ln": w.regtile[1],
                                      "thread_shape": trt.regtile_thread_shape(*w.regtile)}})
     if counters and "mfma" in counters:
         m = counters["mfma"]
-        roofline["rocprof_mfma"] = {"tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
-                                    "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
-                                    "flops_counted": m["flops_per_launch"]}
-    if not args.no_mfma_loop and w.name != "skinny" and w.regtile is None:
-        a_rows = host["A"].reshape(w.a_rows, w.lda_)[:, :w.a_cols].reshape(-1)   # no padding
-        ml = mfma_loop_tflops(trt, torch, a_rows, w.dtype, kern_ms, args.warmup + args.steps)
-        roofline["mfma_loop_tflops"] = round(ml, 1)
-        roofline["frac_of_mfma_loop"] = round(achieved / ml, 4)
-    if not args.no_stream_read:
-        sr = stream_read_gbps(trt, torch)
-        roofline["stream_read_GBps"] = round(sr, 1)
-        if w.name == "skinny":
-            roofline["frac_of_stream_read"] = round(roofline["achieved"] / sr, 4)
+        roofline["rocprof_mfma_committed"] = {
+            "tflops": m["tflops"], "frac_of_peak": m["frac_of_peak"],
+            "busy_frac": m["busy_frac"], "clock_ghz": m["clock_ghz"],
+            "flops_counted": m["flops_per_launch"], "source": counters_entry(counters)}
+    roofline.update(roofline_ctx)
+    if "mfma_loop_tflops" in roofline_ctx:
+        roofline["frac_of_mfma_loop"] = round(tflops / roofline_ctx["mfma_loop_tflops"], 4)
+    if w.name == "skinny" and "stream_read_GBps" in roofline_ctx:
+        roofline["frac_of_stream_read"] = round(roofline["achieved"] /
+                                                roofline_ctx["stream_read_GBps"], 4)
 
-    cpu = None
-    parity = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        import oracle
-        threads = oracle.default_threads()
-        # calibrate: the per-call cost (decoding B once) and the per-row
-        # cost, from two short runs; then size the sample to the budget
-        def run_rows(r):
-            t0 = time.perf_counter()
-            oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,
-                              w.opB, w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
-                              ldr=w.ldr_ if host["R"] is not None else 0,
-                              out_dtype=w.odt, scale=host["scale"],
-                              m_range=(0, r), threads=threads)
-            return time.perf_counter() - t0
-        r1 = min(threads, w.M)
-        r2 = min(4 * threads, w.M)
-        t1, t2 = run_rows(r1), run_rows(r2)
-        per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
-        fixed = max(t1 - r1 * per_row, 0.0)
-        rows = int(min(w.M, max(r1, (args.cpu_seconds - fixed) / per_row)))
-        rows = max(1, rows - rows % max(1, min(threads, rows)))
-        t0 = time.perf_counter()
-        ref = oracle.gemm_block(w.M, w.N, w.K, host["A"], w.lda_, w.opA, host["B"], w.ldb_,
-                                w.opB, w.dtype, bias=host["bias"], relu=w.relu, R=host["R"],
-                                ldr=w.ldr_ if host["R"] is not None else 0,
-                                out_dtype=w.odt, scale=host["scale"],
-                                m_range=(0, rows), threads=threads)
-        t_cpu = time.perf_counter() - t0
-        cpu_tflops = 2.0 * rows * w.N * w.K / t_cpu / 1e12
-        cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, fp64 oracle incl. "
-                         f"epilogue), {t_cpu:.1f} s", "cpu_model": cpu_model()}
-        Cg = C.cpu().numpy().view(np.uint32 if out_bytes == 4 else np.uint16)
-        Cg = Cg.reshape(w.M, w.ldc_)[:rows, :w.N]
-        rep = oracle.accept(np.ascontiguousarray(Cg), ref, w.odt)
-        parity = {"rows": rows, "ok": rep["ok"], "max_abs": rep["max_abs"],
-                  "frob_rel": rep["frob_rel"], "bit_match": rep["bit_match"]}
+        cpu, parity = cpu_baseline(args, w, host, C, np)
 
     name = {"square": "square 4096x4096x4096 f16 -> f16, fp32 accumulate"}.get(
         w.name, f"{w.name} {w.M}x{w.N}x{w.K}")
@@ -509,6 +590,7 @@ def main():
                                 "row_scale": w.row_scale},
                    "tile": (f"vector-lane register tile {w.regtile[0]}x{w.regtile[1]}" if w.regtile
                             else list(tile) if tile else "auto"),
+                   "settle_ms": args.settle_ms,
                    "csrc_digest": csrc_digest()},
         "roofline": roofline,
         "cpu_baseline": cpu,

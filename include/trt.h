@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 10
+#define TRT_ABI_VERSION 11
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -106,9 +106,10 @@ typedef struct {
  * cols elements from its base) is ever read.
  *
  * stream: a hipStream_t (NULL = the default stream).  The call enqueues one
- * kernel and returns; TRT_ERR_HIP means the launch failed, with the runtime's
- * message in trt_last_error().  Pointers are device (or device-accessible)
- * addresses owned by the caller.
+ * kernel and returns; TRT_ERR_HIP means that launch failed (the status the
+ * runtime returned for it, not an error left by an earlier HIP call), with
+ * the runtime's message in trt_last_error().  Pointers are device (or
+ * device-accessible) addresses owned by the caller.
  */
 trt_status trt_gemm(int64_t M, int64_t N, int64_t K,
                     const void* A, int64_t lda, int32_t opA,
@@ -118,12 +119,18 @@ trt_status trt_gemm(int64_t M, int64_t N, int64_t K,
                     const trt_epilogue* epi, void* stream);
 
 /*
- * trt_gemm_tiled -- trt_gemm with an explicit workgroup tile.  tile must name
- * a compiled instance (see trt_tile_at); otherwise TRT_ERR_UNSUPPORTED and
+ * trt_gemm_tiled -- trt_gemm with an explicit workgroup tile.  The tile is
+ * the layout's own parameter: "Named layouts" fixes BM, BN, BK = 16, 64, 32
+ * in its GEMM arrangement, and its section "Contract" has declared tile
+ * sizes belong to the layout rather than to a backend's preset list, with
+ * the target's real restrictions still applying.  Here the target's
+ * restriction is what is compiled: tile must name a compiled instance (see
+ * trt_tile_at; 16x64x32 is the page's), otherwise TRT_ERR_UNSUPPORTED and
  * nothing is enqueued.  tile == NULL behaves as trt_gemm.  With binary32
  * inputs the tile must be NULL or 128x128x32: that path has one kernel, a
  * 2x2-wave tile of 16x16x4 f32 matrix-core fragments, double-buffered
- * through LDS (not listed by trt_tile_at).
+ * through LDS (not listed by trt_tile_at).  Arguments, ownership, stream
+ * and errors otherwise as trt_gemm.
  */
 trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K,
                           const void* A, int64_t lda, int32_t opA,
@@ -206,10 +213,17 @@ typedef enum {
 
 /*
  * trt_layout_dump -- evaluate map `map_id` of compiled tile `tile` on the
- * device, with the very device functions the GEMM kernel uses, for inputs
+ * device, with the very device functions the GEMM kernels use (the C
+ * ownership map is the one their epilogues store through), for inputs
  * x = 0..n-1, writing rows[x] and cols[x] (device buffers of n int32, owned
- * by the caller).  n must equal trt_layout_size(map_id, tile).  Enqueued on
- * `stream`.
+ * by the caller, not read).  "My Triton From Scratch, Part 16: Register
+ * Tiles", section "Tests cover the mapping as a contract": every stage has to
+ * agree on one ownership mapping; this call lets a test read the mapping the
+ * device evaluates and compare it with the host's and with the oracle's.
+ * n must equal trt_layout_size(map_id, tile).  Errors before any HIP call:
+ * TRT_ERR_NULL, TRT_ERR_UNSUPPORTED (tile not compiled), TRT_ERR_ARG (map
+ * not defined for the tile), TRT_ERR_SIZE; TRT_ERR_HIP if the launch fails.
+ * Enqueued on `stream`.
  */
 trt_status trt_layout_dump(int32_t map_id, const trt_tile* tile,
                            int32_t* rows, int32_t* cols, int64_t n,
@@ -284,6 +298,23 @@ trt_status trt_hbm_read_probe(const void* x, int64_t bytes, void* sink,
 #define TRT_MFMA_PROBE_SINK_BYTES 4194304
 trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iters,
                                float* sink, int64_t sink_bytes, void* stream);
+
+/*
+ * trt_clock_probe -- measurement yardstick, not part of the GEMM: 256
+ * workgroups of one wave each read the shader-cycle counter and the
+ * constant-rate real-time counter, wait until the real-time counter has
+ * advanced by `ticks` (1 <= ticks <= 2^27), and read both again; workgroup w
+ * writes the shader cycles that passed to sink[2w] and the real-time ticks
+ * to sink[2w+1] (uint64; device buffer owned by the caller, at least
+ * TRT_CLOCK_PROBE_SINK_BYTES, 8-byte aligned).  cycles / ticks times the
+ * real-time counter's rate is the shader clock while the probe ran: timed
+ * right before and right after a measured region, it records the clock the
+ * part ran at around it.  The rate itself follows from timing a long probe.
+ * Errors: TRT_ERR_NULL, TRT_ERR_ARG, TRT_ERR_SIZE, TRT_ERR_ALIGN before any
+ * HIP call; TRT_ERR_HIP if the launch fails.  Enqueued on `stream`.
+ */
+#define TRT_CLOCK_PROBE_SINK_BYTES 4096
+trt_status trt_clock_probe(int64_t ticks, void* sink, int64_t sink_bytes, void* stream);
 
 /*
  * The GF(2) layout algebra of the layout module ("Triton LinearLayout",
@@ -392,10 +423,22 @@ typedef enum { TRT_REDUCE_SUM = 0, TRT_REDUCE_MAX = 1, TRT_REDUCE_MIN = 2 } trt_
 trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dtype,
                             int32_t op, float* out, void* stream);
 
-/* ABI version of the loaded library (TRT_ABI_VERSION at build time). */
+/*
+ * trt_abi_version -- the ABI version of the loaded library (TRT_ABI_VERSION
+ * at build time).  "Named layouts", section "Runtime and compilation": the
+ * launch ABI keeps versioned layout obligations so that caching and reload
+ * cannot drop checks; a caller compares this number with the header it was
+ * built against before it calls anything else.  No error.
+ */
 int32_t trt_abi_version(void);
 
-/* Message describing the last error on the calling thread ("" if none). */
+/*
+ * trt_last_error -- a message describing the last failed call on the calling
+ * thread ("" after a call that succeeded).  The pointer stays valid until the
+ * thread's next call into the library; the text belongs to the library.  No
+ * page defines it: it is this library's way to carry a runtime message with
+ * TRT_ERR_HIP and to say which check an argument failed.
+ */
 const char* trt_last_error(void);
 
 #ifdef __cplusplus

@@ -264,6 +264,20 @@ def test_mfma_probe_rejections(kw, code):
     assert e.value.status == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(sink=0), trt.ERR_NULL), (dict(ticks=0), trt.ERR_ARG),
+    (dict(ticks=(1 << 27) + 1), trt.ERR_ARG),
+    (dict(sink_bytes=trt.CLOCK_PROBE_SINK_BYTES - 8), trt.ERR_SIZE),
+    (dict(sink=BASE + 4), trt.ERR_ALIGN),
+])
+def test_clock_probe_rejections(kw, code):
+    a = dict(ticks=100, sink=BASE, sink_bytes=trt.CLOCK_PROBE_SINK_BYTES)
+    a.update(kw)
+    with pytest.raises(trt.TrtError) as e:
+        trt.clock_probe_raw(a["ticks"], a["sink"], a["sink_bytes"])
+    assert e.value.status == code
+
+
 # ---- output dtypes and the row scale ----------------------------------------------
 
 def test_epilogue_struct_layout():

@@ -24,3 +24,42 @@ def test_code_tokens_ignore_comment_reflow_but_not_code():
     assert bench._code_tokens(a) == bench._code_tokens(b)
     assert bench._code_tokens(a) != bench._code_tokens(c)
 
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write(",".join(header) + "\n")
+        for r in rows:
+            f.write(",".join(str(x) for x in r) + "\n")
+
+
+def test_ingest_counters_scales_by_the_copy_and_keeps_provenance(tmp_path, monkeypatch):
+    import json
+    out = tmp_path / "counters.json"
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(out))
+    monkeypatch.setattr(bench, "WORKLOADS", ("square",))
+    hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    # the copy of 256 MiB reads 2 x its size by this counter: factor 0.5
+    _csv(str(tmp_path / "pmc_fetch_square" / "run_counter_collection.csv"), hdr,
+         [["copyBuffer", 1 << 20, "FETCH_SIZE", 2 * 256 * 1024],
+          ["gemm_dma_kernel", 256, "FETCH_SIZE", 400000],
+          ["gemm_dma_kernel", 256, "FETCH_SIZE", 410000],
+          ["gemm_dma_kernel", 256, "FETCH_SIZE", 390000]])
+    _csv(str(tmp_path / "pmc_write_square" / "run_counter_collection.csv"), hdr,
+         [["copyBuffer", 1 << 20, "WRITE_SIZE", 256 * 1024],
+          ["gemm_dma_kernel", 256, "WRITE_SIZE", 32768]])
+    (tmp_path / "provenance.json").write_text(json.dumps({"taken": "2026-12-02", "gpu": "x"}))
+    e = bench.ingest_counters(str(tmp_path))["square"]
+    assert e["fetch_factor"] == 0.5 and e["fetch_bytes_per_launch"] == 400000 * 1024 // 2
+    assert e["write_bytes_per_launch"] == 32768 * 1024
+    assert e["provenance"] == {"taken": "2026-12-02", "gpu": "x"}
+    got = bench.committed_counters("square")
+    assert got is not None and bench.counters_entry(got)["taken"] == "2026-12-02"

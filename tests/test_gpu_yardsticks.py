@@ -7,7 +7,11 @@ at any size: the XOR of the per-workgroup digests equals the XOR of all
 cores only) is pinned by recomputing every thread's sums of accumulators on
 the host from the operand words and the documented fragment maps (16x16x32
 for 16-bit types, 16x16x4 for binary32), with operands in {-1, 0, 1} so that
-every fp32 sum is exact.
+every fp32 sum is exact.  trt_clock_probe (shader cycles over real-time
+ticks) is checked for what the counters must satisfy: every workgroup waits
+at least the ticks asked for, the real-time counter's rate from a long probe
+timed with events is steady, and the shader clock it implies lies within the
+part's clock range.
 """
 import numpy as np
 import pytest
@@ -108,3 +112,24 @@ def test_mfma_loop_probe_sums_f32():
 def test_mfma_loop_probe_flops():
     assert trt.mfma_loop_probe_flops(1) == 1024 * 32 * 32768
     assert trt.mfma_loop_probe_flops(1, W.F32) == 1024 * 32 * 2048
+
+
+def test_clock_probe_counters():
+    # a long probe, timed with events: the real-time counter advances at a
+    # fixed rate, so ticks / elapsed time is the same for two lengths
+    s = torch.cuda.current_stream()
+    rates = []
+    for ticks in (200_000, 400_000):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        out = trt.clock_probe(ticks)
+        e1.record(s)
+        torch.cuda.synchronize()
+        c = out.cpu().numpy()
+        assert (c[:, 1] >= ticks).all() and (c[:, 1] < ticks + ticks // 10).all()
+        assert (c[:, 0] > 0).all()
+        rates.append(ticks / (e0.elapsed_time(e1) * 1e-3))
+        # shader clock while it ran: within the part's range (0.1 - 3 GHz)
+        ghz = np.median(c[:, 0] / c[:, 1]) * rates[-1] / 1e9
+        assert 0.1 < ghz < 3.0, ghz
+    assert abs(rates[0] - rates[1]) / rates[1] < 0.05, rates

@@ -98,6 +98,8 @@ def lib():
         L.trt_hbm_read_probe.restype = i32
         L.trt_mfma_loop_probe.argtypes = [i32, vp, i32, vp, i64, vp]
         L.trt_mfma_loop_probe.restype = i32
+        L.trt_clock_probe.argtypes = [i64, vp, i64, vp]
+        L.trt_clock_probe.restype = i32
         u32p = ctypes.POINTER(ctypes.c_uint32)
         L.trt_gf2_rank.argtypes = [i32, i32, u32p]
         L.trt_gf2_rank.restype = i32
@@ -395,6 +397,25 @@ def mfma_loop_probe_flops(iters, dtype=F16):
     if dtype == F32:
         return 256 * 4 * iters * 32 * (2 * 16 * 16 * 4)
     return 256 * 4 * iters * 64 * (2 * 16 * 16 * 32)
+
+
+CLOCK_PROBE_SINK_BYTES = 4096     # TRT_CLOCK_PROBE_SINK_BYTES
+
+
+def clock_probe_raw(ticks, sink, sink_bytes, stream=0):
+    """trt_clock_probe on a raw device address; raises TrtError on error."""
+    _check(lib().trt_clock_probe(ticks, sink, sink_bytes, stream))
+
+
+def clock_probe(ticks, device="cuda", sink=None):
+    """Run the clock yardstick once on the current stream; returns the device
+    tensor of [256, 2] int64 (shader cycles, real-time ticks) per workgroup."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(CLOCK_PROBE_SINK_BYTES // 8, dtype=torch.int64, device=device)
+    clock_probe_raw(ticks, sink.data_ptr(), sink.numel() * sink.element_size(),
+                    _stream(sink.device))
+    return sink.view(-1, 2)
 
 
 # ---- the GF(2) layout algebra (host only; maps as lists of column words) -------

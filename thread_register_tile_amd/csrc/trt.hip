@@ -379,6 +379,29 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const trt::u32x4* __restr
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Clock yardstick: each of 256 one-wave workgroups reads the shader-cycle
+// counter and the constant-rate real-time counter, waits until the real-time
+// counter has advanced by `ticks`, reads both again and writes the two
+// differences (lane 0, ordinary vector stores).  Their ratio is the shader
+// clock over the real-time counter's rate, at the moment the probe runs.
+// A read of the real-time counter takes tens of shader cycles and the
+// counter runs far slower than the shader clock, so the wait needs fewer
+// than `ticks` reads; it stops after 64 * ticks + 65536 reads in any case.
+constexpr int kClockProbeBlocks = 256;
+__global__ __launch_bounds__(64) void clock_kernel(int64_t ticks, uint64_t* out) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t r1 = r0;
+  const uint64_t cap = 64 * (uint64_t)ticks + 65536;
+  for (uint64_t i = 0; r1 - r0 < (uint64_t)ticks && i < cap; ++i)
+    r1 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 // Matrix-core yardstick: every wave of 256 workgroups x 4 waves (one per
 // SIMD) runs `iters` rounds of matrix-core products, 1024 cycles of them per
 // round -- 64 v_mfma_f32_16x16x32 on 64 accumulators for 16-bit types, 32
@@ -764,6 +787,19 @@ trt_status trt_mfma_loop_probe(int32_t dtype, const void* operands, int32_t iter
       : dtype == TRT_F32 ? trt::launch(mfma_loop_kernel<trt::DT_F32>, grid, block, 0, s, src, iters, dst)
                          : trt::launch(mfma_loop_kernel<trt::DT_BF16>, grid, block, 0, s, src, iters, dst);
   return launched(e, "matrix-core probe launch");
+}
+
+trt_status trt_clock_probe(int64_t ticks, void* sink, int64_t sink_bytes, void* stream) {
+  if (!sink) return fail(TRT_ERR_NULL, "sink must be non-null");
+  if (ticks < 1 || ticks > (int64_t(1) << 27)) return fail(TRT_ERR_ARG, "ticks must be in [1, 2^27]");
+  if (sink_bytes < TRT_CLOCK_PROBE_SINK_BYTES)
+    return fail(TRT_ERR_SIZE, "sink must hold TRT_CLOCK_PROBE_SINK_BYTES bytes");
+  if (!aligned(sink, 8)) return fail(TRT_ERR_ALIGN, "sink must be 8-byte aligned");
+  static_assert(kClockProbeBlocks * 16 == TRT_CLOCK_PROBE_SINK_BYTES, "two counters per workgroup");
+  return launched(trt::launch(clock_kernel, dim3(kClockProbeBlocks), dim3(64), 0,
+                              static_cast<hipStream_t>(stream), ticks,
+                              static_cast<uint64_t*>(sink)),
+                  "clock probe launch");
 }
 
 trt_status trt_block_reduce(const void* x, int64_t n, int64_t block, int32_t dtype, int32_t op,
