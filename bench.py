@@ -413,6 +413,8 @@ def main():
                     help="skip the streaming-read bandwidth measurement")
     ap.add_argument("--no-mfma-loop", action="store_true",
                     help="skip the matrix-core-only loop measurement")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="call trt_gemm (no workspace) even where trt_gemm_ws would split K")
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
                     help="write profiles/counters.json from rocprofv3 --pmc runs in DIR "
                          "and exit (no GPU needed)")
@@ -463,15 +465,25 @@ def main():
                              ldr=w.ldr_ if R is not None else 0,
                              scale=scale.data_ptr() if scale is not None else 0, stream=sptr)
 
+    # shapes that split K over workgroups (M <= 16) run through trt_gemm_ws,
+    # with the workspace allocated here, before any timing
+    ws_bytes = 0 if (w.regtile is not None or tile is not None or args.no_workspace) else \
+        trt.workspace_size(w.M, w.N, w.K, w.opA, w.opB, w.dtype)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
+
     def step():
         if w.regtile is not None:
             return step_regtile()
+        kw = dict(bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
+                  residual=R.data_ptr() if R is not None else 0,
+                  ldr=w.ldr_ if R is not None else 0,
+                  scale=scale.data_ptr() if scale is not None else 0, stream=sptr)
+        if ws is not None:
+            return trt.gemm_ws_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, w.opA, B.data_ptr(),
+                                   w.ldb_, w.opB, C.data_ptr(), w.ldc_, w.dtype, w.odt,
+                                   workspace=ws.data_ptr(), workspace_bytes=ws_bytes, **kw)
         trt.gemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda_, w.opA, B.data_ptr(), w.ldb_, w.opB,
-                     C.data_ptr(), w.ldc_, w.dtype, w.odt,
-                     bias=bias.data_ptr() if bias is not None else 0, relu=w.relu,
-                     residual=R.data_ptr() if R is not None else 0,
-                     ldr=w.ldr_ if R is not None else 0,
-                     scale=scale.data_ptr() if scale is not None else 0, tile=tile, stream=sptr)
+                     C.data_ptr(), w.ldc_, w.dtype, w.odt, tile=tile, **kw)
 
     clock = Clock(trt, torch)
 
@@ -591,6 +603,9 @@ def main():
                    "tile": (f"vector-lane register tile {w.regtile[0]}x{w.regtile[1]}" if w.regtile
                             else list(tile) if tile else "auto"),
                    "settle_ms": args.settle_ms,
+                   "entry_point": "trt_gemm_ws (split K, workspace of %d bytes)" % ws_bytes
+                   if ws is not None else ("trt_gemm_regtile" if w.regtile is not None
+                                           else "trt_gemm_tiled"),
                    "csrc_digest": csrc_digest()},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -15,9 +15,10 @@
  *
  * The library has no global mutable state and never allocates: all buffers
  * belong to the caller.  Every call validates its arguments on the host
- * before any device work (an error leaves C untouched) and then enqueues
- * exactly one kernel on the caller's stream; the result is valid once that
- * stream has synchronised.  No pointer is kept after a call returns.
+ * before any device work (an error leaves C untouched) and then enqueues its
+ * kernels on the caller's stream (one, or two for trt_gemm_ws's split K);
+ * the result is valid once that stream has synchronised.  No pointer is
+ * kept after a call returns.
  */
 #ifndef TRT_H
 #define TRT_H
@@ -28,7 +29,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 11
+#define TRT_ABI_VERSION 12
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -139,6 +140,47 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K,
                           int32_t in_dtype, int32_t out_dtype,
                           const trt_epilogue* epi, const trt_tile* tile,
                           void* stream);
+
+/*
+ * trt_gemm_workspace_size -- the bytes of workspace trt_gemm_ws uses for an
+ * M x N x K problem with these storage orders and input dtype, or 0 when its
+ * kernels need none; -1 on an argument error (sizes outside [1, 2^30], an
+ * unknown op flag or dtype; message in trt_last_error()).  Host only, no HIP
+ * call.  Nonzero only for the streaming shapes (M <= 16, A and B both
+ * TRT_OP_N, 16-bit inputs, K % 8 == 0, N % 4 == 0) whose K is long enough to
+ * split over workgroups: splits * M * N * 4 bytes of fp32 partial sums.
+ */
+int64_t trt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t opA,
+                                int32_t opB, int32_t in_dtype);
+
+/*
+ * trt_gemm_ws -- trt_gemm with a caller workspace.  The operation, arguments,
+ * validation and errors are trt_gemm's ("Named layouts": the GEMM
+ * arrangement and section "Contract"); the page's loop fixes the
+ * accumulation over K blocks as one sum, which any order of fp32 additions
+ * implements within the accumulation's rounding.  For the streaming shapes
+ * of trt_gemm_workspace_size, when the operands also allow the streaming
+ * kernel's vector loads (A 16-byte and B 8-byte aligned, lda % 8 == 0,
+ * ldb % 4 == 0), K is split into slices over workgroups: each writes fp32
+ * partial sums of its slice to the workspace, and a second kernel, on the
+ * same stream, adds them in slice order (the result does not depend on
+ * timing) and applies the epilogue; otherwise the call is trt_gemm and the
+ * workspace is not touched.
+ * workspace: device memory of at least trt_gemm_workspace_size(...) bytes
+ * owned by the caller, 16-byte aligned, disjoint from A, B, C, bias,
+ * residual and row_scale; it may be NULL (with any workspace_bytes) for
+ * calls that need none.  Its contents on entry do not matter and are
+ * unspecified afterwards; the library keeps no pointer to it.  Errors, before
+ * any HIP call: trt_gemm's, and TRT_ERR_NULL / TRT_ERR_SIZE / TRT_ERR_ALIGN /
+ * TRT_ERR_OVERLAP for a missing, short, misaligned or overlapping workspace.
+ */
+trt_status trt_gemm_ws(int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, int32_t opA,
+                       const void* B, int64_t ldb, int32_t opB,
+                       void* C, int64_t ldc,
+                       int32_t in_dtype, int32_t out_dtype,
+                       const trt_epilogue* epi, void* workspace,
+                       int64_t workspace_bytes, void* stream);
 
 /*
  * trt_validate -- the host-side checks of trt_gemm_tiled, alone: returns the

@@ -67,6 +67,18 @@ class Run:
                      tile=tile if tile is not None else w.tile,
                      stream=torch.cuda.current_stream().cuda_stream)
 
+    def launch_ws(self, workspace, workspace_bytes):
+        """trt_gemm_ws on the same buffers; workspace: a device address (int)."""
+        w = self.w
+        trt.gemm_ws_raw(w.M, w.N, w.K, self.A.data_ptr(), w.lda_, w.opA, self.B.data_ptr(),
+                        w.ldb_, w.opB, self.c_ptr(), self.ldc, w.dtype, w.odt,
+                        bias=self.bias.data_ptr() if self.bias is not None else 0, relu=w.relu,
+                        residual=self.R.data_ptr() if self.R is not None else 0,
+                        ldr=w.ldr_ if self.R is not None else 0,
+                        scale=self.scale.data_ptr() if self.scale is not None else 0,
+                        workspace=workspace, workspace_bytes=workspace_bytes,
+                        stream=torch.cuda.current_stream().cuda_stream)
+
     def result(self):
         """C as an (M, N) array of raw bits (uint16, or uint32 for binary32
         output); asserts guards and ldc padding intact."""

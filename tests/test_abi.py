@@ -548,3 +548,49 @@ def test_choose_tile_errors():
     assert trt.lib().trt_choose_tile(0, 4, trt.F16, ctypes.byref(t)) == trt.ERR_SIZE
     assert trt.lib().trt_choose_tile(4, 4, 7, ctypes.byref(t)) == trt.ERR_DTYPE
     assert trt.lib().trt_choose_tile(4, 4, trt.F16, None) == trt.ERR_NULL
+
+
+# ---- the split-K streaming path's workspace (trt_gemm_ws) -------------------------
+
+def test_workspace_size():
+    # the skinny workload: 64 panels of 256 columns, 8 slices of 64 iterations
+    assert trt.workspace_size(16, 16384, 16384) == 8 * 16 * 16384 * 4
+    assert trt.workspace_size(5, 1000, 8192) > 0
+    # shapes that never split: M > 16, transposed storage, binary32 inputs, short K,
+    # K or N off the vector grid
+    assert trt.workspace_size(17, 16384, 16384) == 0
+    assert trt.workspace_size(16, 16384, 16384, opA=trt.OP_T) == 0
+    assert trt.workspace_size(16, 16384, 16384, opB=trt.OP_T) == 0
+    assert trt.workspace_size(16, 16384, 16384, in_dtype=trt.F32) == 0
+    assert trt.workspace_size(16, 16384, 256) == 0
+    assert trt.workspace_size(16, 16384, 16380) == 0
+    assert trt.workspace_size(16, 16382, 16384) == 0
+    for bad in [dict(M=0), dict(K=1 << 31), dict(opA=2), dict(in_dtype=9)]:
+        a = dict(M=16, N=64, K=4096, opA=0, opB=0, in_dtype=trt.F16)
+        a.update(bad)
+        with pytest.raises(trt.TrtError):
+            trt.workspace_size(a["M"], a["N"], a["K"], a["opA"], a["opB"], a["in_dtype"])
+
+
+GIB = 1 << 30     # fake addresses far apart: B alone spans 512 MiB here
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=0), trt.ERR_NULL),
+    (dict(workspace_bytes=8 * 16 * 16384 * 4 - 16), trt.ERR_SIZE),
+    (dict(workspace=8 * GIB + 8), trt.ERR_ALIGN),
+    (dict(workspace=4 * GIB + 4096), trt.ERR_OVERLAP),      # inside C
+    (dict(workspace=2 * GIB - 4096), trt.ERR_OVERLAP),      # reaches into B from below
+    (dict(workspace=2 * GIB + 4096), trt.ERR_OVERLAP),      # inside B
+    (dict(workspace=GIB - 4096), trt.ERR_OVERLAP),          # reaches into A
+])
+def test_gemm_ws_workspace_errors(kw, code):
+    # every case returns before any HIP call (no GPU is needed)
+    M, N, K = 16, 16384, 16384
+    a = dict(workspace=8 * GIB, workspace_bytes=8 * 16 * 16384 * 4)
+    a.update(kw)
+    with pytest.raises(trt.TrtError) as e:
+        trt.gemm_ws_raw(M, N, K, GIB, K, 0, 2 * GIB, N, 0, 4 * GIB, N, trt.F16, trt.F16,
+                        workspace=a["workspace"], workspace_bytes=a["workspace_bytes"])
+    assert e.value.status == code, trt.last_error()
+    assert "workspace" in trt.last_error()

@@ -78,6 +78,10 @@ def lib():
         L.trt_gemm_tiled.restype = i32
         L.trt_validate.argtypes = gemm_args + [ctypes.POINTER(TileDesc)]
         L.trt_validate.restype = i32
+        L.trt_gemm_ws.argtypes = gemm_args + [vp, i64, vp]
+        L.trt_gemm_ws.restype = i32
+        L.trt_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+        L.trt_gemm_workspace_size.restype = i64
         L.trt_tile_count.argtypes = []
         L.trt_tile_count.restype = i32
         L.trt_tile_at.argtypes = [i32, ctypes.POINTER(TileDesc), ctypes.POINTER(i32),
@@ -165,6 +169,23 @@ def gemm_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
     _check(lib().trt_gemm_tiled(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
                                 out_dtype, _epi(bias, relu, residual, ldr, scale),
                                 _tile(tile), stream or None))
+
+
+def gemm_ws_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
+                bias=0, relu=False, residual=0, ldr=0, scale=0, workspace=0, workspace_bytes=0,
+                stream=0):
+    """trt_gemm_ws on raw device addresses (ints).  Raises TrtError."""
+    _check(lib().trt_gemm_ws(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
+                             _epi(bias, relu, residual, ldr, scale), workspace or None,
+                             workspace_bytes, stream or None))
+
+
+def workspace_size(M, N, K, opA=OP_N, opB=OP_N, in_dtype=F16) -> int:
+    """trt_gemm_workspace_size: bytes of workspace trt_gemm_ws uses (0: none)."""
+    n = lib().trt_gemm_workspace_size(M, N, K, opA, opB, in_dtype)
+    if n < 0:
+        raise TrtError(ERR_ARG, last_error())
+    return n
 
 
 def validate_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,

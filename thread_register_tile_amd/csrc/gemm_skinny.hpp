@@ -65,24 +65,17 @@ struct SkinnyTile {
 };
 static_assert(SkinnyTile::c_map().bijective(), "C ownership must cover the tile exactly once");
 
+// One wave's stream over B: its 64 columns n0 .. n0+63 of B, iterations
+// it0 .. it1-1 of 32 k, accumulated into acc[j] (register r of acc[j] is
+// row 4*(lane/16) + r, column 4*(lane%16) + j of the 64).
 template <int DT>
-__global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmArgs p) {
+__device__ __forceinline__ void skinny_stream(const GemmArgs& p, int n0, int it0, int it1,
+                                              int lane, f32x4 (&acc)[4]) {
   using ST = SkinnyTile;
   constexpr int D = ST::DEPTH;
-  __shared__ f32x4 part[ST::WAVES][4][64];  // partial tiles: [wave][j][lane]
-
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int n0 = blockIdx.x * ST::BN;
   const int c = lane & 15, g = lane >> 4;
   const int n = n0 + 4 * c;                 // this lane's 4 columns of B
   const int ma = lane & 15;                 // this lane's row of A
-
-  // the wave's K slice, in whole iterations of 32
-  const int iters_total = (p.K + ST::KW - 1) / ST::KW;
-  const int per_wave = (iters_total + ST::WAVES - 1) / ST::WAVES;
-  const int it0 = wave * per_wave;
-  const int it1 = min(it0 + per_wave, iters_total);
   const int iters = max(it1 - it0, 0);
 
   u32x2 bq[D][8];
@@ -104,7 +97,6 @@ __global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmAr
     }
   };
 
-  f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -135,6 +127,25 @@ __global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmAr
 #pragma unroll
   for (int s = 0; s < D; ++s)
     if (i + s < iters) consume(s);
+}
+
+template <int DT>
+__global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmArgs p) {
+  using ST = SkinnyTile;
+  __shared__ f32x4 part[ST::WAVES][4][64];  // partial tiles: [wave][j][lane]
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int n0 = blockIdx.x * ST::BN;
+
+  // the wave's K slice, in whole iterations of 32
+  const int iters_total = (p.K + ST::KW - 1) / ST::KW;
+  const int per_wave = (iters_total + ST::WAVES - 1) / ST::WAVES;
+  const int it0 = wave * per_wave;
+  const int it1 = min(it0 + per_wave, iters_total);
+
+  f32x4 acc[4];
+  skinny_stream<DT>(p, n0, it0, it1, lane, acc);
 
   // cross-wave reduction: partial (m, n) of wave w sits at part[w][j][lane]
   // register r with m = 4*(lane/16) + r, n = 4*(lane%16) + j
@@ -170,6 +181,100 @@ __global__ __launch_bounds__(SkinnyTile::THREADS) void gemm_skinny_kernel(GemmAr
       O::st(p.C, (int64_t)m * p.ldc + nc + e, v);
     }
   });
+}
+
+// ---- split K over workgroups, with a workspace ------------------------------
+//
+// The same stream, cut differently: workgroup (split, panel) of the split
+// kernel reads K slice `split` of a 256-column panel, its 4 waves taking 64
+// columns each, so that together they read 512 contiguous bytes of every B
+// row of the slice; with enough slices the grid holds several workgroups per
+// compute unit.  Each wave writes its partial [M, 64] in fp32 to the
+// workspace, ws[(split*M + m)*N + n]; a second kernel adds the partials of a
+// cell in split order (deterministic, no atomics) and applies the epilogue.
+struct SkinnySplit {
+  static constexpr int WAVES = 4, THREADS = 64 * WAVES;
+  static constexpr int PANEL = 64 * WAVES;    // columns per workgroup
+  static constexpr int MIN_ITERS = 8;         // iterations of 32 k per slice at least
+  static constexpr int TARGET_WGS = 512;      // two workgroups per compute unit
+};
+
+// The slices of a split run: `splits` slices of `per_split` iterations of 32
+// k (the last one shorter), and the workspace they fill.  splits < 2: no
+// split (the single-pass kernel is used).
+struct SplitPlan {
+  int splits, per_split;
+  int64_t ws_bytes;
+};
+inline SplitPlan skinny_split_plan(int64_t M, int64_t N, int64_t K) {
+  const int64_t iters = (K + SkinnyTile::KW - 1) / SkinnyTile::KW;
+  const int64_t panels = (N + SkinnySplit::PANEL - 1) / SkinnySplit::PANEL;
+  int64_t splits = (SkinnySplit::TARGET_WGS + panels - 1) / panels;
+  const int64_t most = iters / SkinnySplit::MIN_ITERS;
+  splits = splits < most ? splits : most;
+  if (splits < 2) return SplitPlan{1, (int)iters, 0};
+  const int64_t per = (iters + splits - 1) / splits;
+  splits = (iters + per - 1) / per;     // no empty slice
+  return SplitPlan{(int)splits, (int)per, splits * M * N * 4};
+}
+
+template <int DT>
+__global__ __launch_bounds__(SkinnySplit::THREADS) void gemm_skinny_split_kernel(
+    GemmArgs p, float* ws, int splits, int per_split) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int panels = (p.N + SkinnySplit::PANEL - 1) / SkinnySplit::PANEL;
+  // consecutive workgroups take neighbouring panels of one slice
+  const int split = blockIdx.x / panels, panel = blockIdx.x % panels;
+  const int n0 = panel * SkinnySplit::PANEL + 64 * wave;
+  if (n0 >= p.N) return;   // no barrier below: waves past N leave at once
+  const int iters_total = (p.K + SkinnyTile::KW - 1) / SkinnyTile::KW;
+  const int it0 = split * per_split;
+  const int it1 = min(it0 + per_split, iters_total);
+  f32x4 acc[4];
+  skinny_stream<DT>(p, n0, it0, it1, lane, acc);
+  // register r of acc[j]: row 4*(lane/16) + r, column n0 + 4*(lane%16) + j;
+  // N % 4 == 0, so the lane's four columns are all inside or all outside
+  const int n = n0 + 4 * (lane & 15);
+  if (n >= p.N) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * (lane >> 4) + r;
+    if (m >= p.M) continue;
+    *reinterpret_cast<f32x4*>(ws + ((int64_t)split * p.M + m) * p.N + n) =
+        f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+  }
+}
+
+// Thread q of the reduction owns the run of four columns 4*(q % (N/4)) of
+// row q / (N/4): the sum of the slices' partials in split order, then
+// y = relu(sum * scale[m] + bias[n]) + R[m, n] (each term when present) and
+// one rounding to the output type, as the single-pass kernel does.
+template <int OT>
+__global__ __launch_bounds__(256) void skinny_split_reduce_kernel(GemmArgs p, const float* ws,
+                                                                  int splits) {
+  using O = Out<OT>;
+  const int64_t runs = p.N / 4;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (int64_t)p.M * runs) return;
+  const int m = (int)(q / runs), n = 4 * (int)(q % runs);
+  f32x4 y = *reinterpret_cast<const f32x4*>(ws + (int64_t)m * p.N + n);
+  for (int s = 1; s < splits; ++s) y += *reinterpret_cast<const f32x4*>(ws + ((int64_t)s * p.M + m) * p.N + n);
+  float v[4] = {y[0], y[1], y[2], y[3]};
+  const float sc = p.scale ? O::ld(p.scale, m) : 1.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (p.scale) v[e] *= sc;
+    if (p.bias) v[e] += O::ld(p.bias, n + e);
+    if (p.relu) v[e] = v[e] > 0.f ? v[e] : 0.f;
+    if (p.R) v[e] += O::ld(p.R, (int64_t)m * p.ldr + n + e);
+  }
+  const int64_t c0 = (int64_t)m * p.ldc + n;
+  if (p.epi_vec) {
+    O::st4(p.C, c0, O::pack(v));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O::st(p.C, c0 + e, v[e]);
+  }
 }
 
 }  // namespace trt

@@ -44,6 +44,12 @@ inline hipError_t launch_pipelined(GemmArgs a, int dt, int opA, int opB, hipStre
 // Launch the HBM-streaming kernel for M <= 16 (kern_skinny.hip).
 hipError_t launch_skinny(GemmArgs a, int dt, hipStream_t s);
 
+// Launch the split-K streaming kernel for M <= 16 (`splits` K slices of
+// `per_split` iterations of 32 k, partials in the workspace ws) and the
+// reduction that adds them and applies the epilogue (kern_skinny.hip).
+hipError_t launch_skinny_split(GemmArgs a, int dt, float* ws, int splits, int per_split,
+                               hipStream_t s);
+
 // Launch the binary32-operand GEMM on its 128x128x32 tile (kern_f32.hip).
 hipError_t launch_f32(GemmArgs a, int opA, int opB, bool vec, hipStream_t s);
 

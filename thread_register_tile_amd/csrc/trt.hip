@@ -583,10 +583,34 @@ trt_status trt_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
   return TRT_OK;
 }
 
-trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                          int32_t opA, const void* B, int64_t ldb, int32_t opB, void* C,
-                          int64_t ldc, int32_t in_dtype, int32_t out_dtype,
-                          const trt_epilogue* epi, const trt_tile* tile, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Whether a call may split K over workgroups with a workspace, judged on
+// sizes and storage alone: the streaming tile's kernel conditions without
+// the pointers' alignment (checked at the call).
+bool split_candidate(int64_t M, int64_t N, int64_t K, int32_t opA, int32_t opB,
+                     int32_t in_dtype) {
+  return M <= 16 && opA == TRT_OP_N && opB == TRT_OP_N && in_dtype != TRT_F32 && K % 8 == 0 &&
+         N % 4 == 0;
+}
+
+// The workspace a call uses: the split plan's when it splits, else none.
+int64_t workspace_need(int64_t M, int64_t N, int64_t K, int32_t opA, int32_t opB,
+                       int32_t in_dtype) {
+  if (!split_candidate(M, N, K, opA, opB, in_dtype)) return 0;
+  return trt::skinny_split_plan(M, N, K).ws_bytes;
+}
+
+// The GEMM call behind trt_gemm, trt_gemm_tiled and trt_gemm_ws.  ws: the
+// caller's workspace (use_ws), used to split K over workgroups for M <= 16
+// when the streaming kernel applies; otherwise the same kernels as without.
+trt_status gemm_call(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
+                     const void* B, int64_t ldb, int32_t opB, void* C, int64_t ldc,
+                     int32_t in_dtype, int32_t out_dtype, const trt_epilogue* epi,
+                     const trt_tile* tile, bool use_ws, void* ws, int64_t ws_bytes,
+                     void* stream) {
   const trt_status s =
       trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, tile);
   if (s != TRT_OK) return s;
@@ -623,9 +647,60 @@ trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_
   a.epi_vec = aligned(C, va) && ldc % 4 == 0 && (!a.bias || aligned(a.bias, va)) &&
               (!a.R || (aligned(a.R, va) && a.ldr % 4 == 0));
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_ws && in_dtype != TRT_F32 && e->bm == 16 && skinny_ok(a, opA, opB)) {
+    const trt::SplitPlan plan = trt::skinny_split_plan(M, N, K);
+    if (plan.splits >= 2) {
+      std::string msg;
+      const trt_status w = trt::validate_workspace(M, N, K, A, lda, opA, B, ldb, opB, C, ldc,
+                                                   in_dtype, out_dtype, epi, ws, ws_bytes,
+                                                   plan.ws_bytes, msg);
+      if (w != TRT_OK) return fail(w, msg);
+      return launched(trt::launch_skinny_split(a, in_dtype, static_cast<float*>(ws), plan.splits,
+                                               plan.per_split, st),
+                      "gemm launch");
+    }
+  }
   return launched(in_dtype == TRT_F32 ? trt::launch_f32(a, opA, opB, vec, st)
                                       : e->launch(a, in_dtype, opA, opB, vec, st),
                   "gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+trt_status trt_gemm_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                          int32_t opA, const void* B, int64_t ldb, int32_t opB, void* C,
+                          int64_t ldc, int32_t in_dtype, int32_t out_dtype,
+                          const trt_epilogue* epi, const trt_tile* tile, void* stream) {
+  return gemm_call(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, tile,
+                   false, nullptr, 0, stream);
+}
+
+int64_t trt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t opA, int32_t opB,
+                                int32_t in_dtype) {
+  if (M < 1 || N < 1 || K < 1 || M > trt::kMaxDim || N > trt::kMaxDim || K > trt::kMaxDim) {
+    fail(TRT_ERR_SIZE, "M, N and K must be in [1, 2^30]");
+    return -1;
+  }
+  if ((opA != TRT_OP_N && opA != TRT_OP_T) || (opB != TRT_OP_N && opB != TRT_OP_T)) {
+    fail(TRT_ERR_ARG, "opA and opB must be TRT_OP_N or TRT_OP_T");
+    return -1;
+  }
+  if (in_dtype != TRT_F16 && in_dtype != TRT_BF16 && in_dtype != TRT_F32) {
+    fail(TRT_ERR_DTYPE, "in_dtype must be TRT_F16, TRT_BF16 or TRT_F32");
+    return -1;
+  }
+  g_err.clear();
+  return workspace_need(M, N, K, opA, opB, in_dtype);
+}
+
+trt_status trt_gemm_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,
+                       const void* B, int64_t ldb, int32_t opB, void* C, int64_t ldc,
+                       int32_t in_dtype, int32_t out_dtype, const trt_epilogue* epi,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_call(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, nullptr,
+                   true, workspace, workspace_bytes, stream);
 }
 
 trt_status trt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t opA,

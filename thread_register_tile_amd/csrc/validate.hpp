@@ -131,4 +131,63 @@ inline trt_status validate_gemm(int64_t M, int64_t N, int64_t K, const void* A, 
   return TRT_OK;
 }
 
+// The caller's workspace of a call that validate_gemm accepted: at least
+// `need` bytes when the call uses one, 16-byte aligned, and disjoint from A,
+// B, C and the epilogue operands (the kernels write it while they read the
+// inputs, and C is written from it).  A call that needs none accepts any
+// workspace, NULL included.
+inline trt_status validate_workspace(int64_t M, int64_t N, int64_t K, const void* A,
+                                     int64_t lda, int32_t opA, const void* B, int64_t ldb,
+                                     int32_t opB, const void* C, int64_t ldc, int32_t in_dtype,
+                                     int32_t out_dtype, const trt_epilogue* epi,
+                                     const void* ws, int64_t ws_bytes, int64_t need,
+                                     std::string& msg) {
+  if (need == 0) {
+    msg.clear();
+    return TRT_OK;
+  }
+  if (ws_bytes < 0) {
+    msg = "workspace_bytes must be >= 0";
+    return TRT_ERR_SIZE;
+  }
+  if (!ws) {
+    msg = "this call needs a workspace of " + std::to_string(need) + " bytes";
+    return TRT_ERR_NULL;
+  }
+  if (ws_bytes < need) {
+    msg = "the workspace must hold at least " + std::to_string(need) + " bytes";
+    return TRT_ERR_SIZE;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) & 15u) {
+    msg = "the workspace must be 16-byte aligned";
+    return TRT_ERR_ALIGN;
+  }
+  const int64_t isz = elem_bytes(in_dtype), osz = elem_bytes(out_dtype);
+  const bool has_bias = epi && epi->bias;
+  const bool has_res = epi && epi->residual;
+  const bool has_scale = epi && epi->row_scale;
+  int64_t sa = 0, sb = 0, sc = 0, sr = 0;
+  span_bytes(opA ? K : M, opA ? M : K, lda, sa, isz);
+  span_bytes(opB ? N : K, opB ? K : N, ldb, sb, isz);
+  span_bytes(M, N, ldc, sc, osz);
+  if (has_res) span_bytes(M, N, epi->ldr, sr, osz);
+  auto ext = [](const void* q, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+    return Extent{lo, q ? lo + (uintptr_t)bytes : lo};
+  };
+  const Extent ew = ext(ws, need);
+  const Extent others[6] = {ext(A, sa), ext(B, sb), ext(C, sc),
+                            ext(has_bias ? epi->bias : nullptr, osz * N),
+                            ext(has_res ? epi->residual : nullptr, sr),
+                            ext(has_scale ? epi->row_scale : nullptr, osz * M)};
+  static const char* names[6] = {"A", "B", "C", "bias", "residual", "row_scale"};
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(ew, others[i])) {
+      msg = std::string("the workspace overlaps ") + names[i];
+      return TRT_ERR_OVERLAP;
+    }
+  msg.clear();
+  return TRT_OK;
+}
+
 }  // namespace trt
