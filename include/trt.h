@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define TRT_ABI_VERSION 12
+#define TRT_ABI_VERSION 13
 
 /* Status codes.  Every entry point returns one of these. */
 typedef enum {
@@ -181,6 +181,31 @@ trt_status trt_gemm_ws(int64_t M, int64_t N, int64_t K,
                        int32_t in_dtype, int32_t out_dtype,
                        const trt_epilogue* epi, void* workspace,
                        int64_t workspace_bytes, void* stream);
+
+/*
+ * trt_gemm_noalloc -- trt_gemm_ws for callers that cannot allocate (code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same operation, arguments, validation, kernels and results (bit for bit),
+ * with the workspace taken from a device array of TRT_NOALLOC_SCRATCH_BYTES
+ * that the library's code object holds on each GPU it runs on, for the life
+ * of the process; the call allocates and frees nothing.  Every split plan
+ * needs at most 16,744,448 bytes (16 rows, at most ceil(512 / p) slices of p
+ * column panels), so all fit; a call that needed more would fail with
+ * TRT_ERR_SIZE.  The array's address on a device is looked up on the first
+ * call on that device (the device of `stream`).  All calls on one GPU share
+ * its array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that may overlap in time on one GPU -- on different
+ * streams, or from several threads -- race and must be serialised by the
+ * caller.  Errors: trt_gemm's; TRT_ERR_HIP if the array's address or the
+ * stream's device cannot be read.
+ */
+#define TRT_NOALLOC_SCRATCH_BYTES 16777216
+trt_status trt_gemm_noalloc(int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, int32_t opA,
+                            const void* B, int64_t ldb, int32_t opB,
+                            void* C, int64_t ldc,
+                            int32_t in_dtype, int32_t out_dtype,
+                            const trt_epilogue* epi, void* stream);
 
 /*
  * trt_validate -- the host-side checks of trt_gemm_tiled, alone: returns the

@@ -79,6 +79,18 @@ class Run:
                         workspace=workspace, workspace_bytes=workspace_bytes,
                         stream=torch.cuda.current_stream().cuda_stream)
 
+    def launch_noalloc(self):
+        """trt_gemm_noalloc on the same buffers (its workspace is the library's own)."""
+        w = self.w
+        trt.gemm_noalloc_raw(w.M, w.N, w.K, self.A.data_ptr(), w.lda_, w.opA, self.B.data_ptr(),
+                             w.ldb_, w.opB, self.c_ptr(), self.ldc, w.dtype, w.odt,
+                             bias=self.bias.data_ptr() if self.bias is not None else 0,
+                             relu=w.relu,
+                             residual=self.R.data_ptr() if self.R is not None else 0,
+                             ldr=w.ldr_ if self.R is not None else 0,
+                             scale=self.scale.data_ptr() if self.scale is not None else 0,
+                             stream=torch.cuda.current_stream().cuda_stream)
+
     def result(self):
         """C as an (M, N) array of raw bits (uint16, or uint32 for binary32
         output); asserts guards and ldc padding intact."""

@@ -82,6 +82,8 @@ def lib():
         L.trt_gemm_ws.restype = i32
         L.trt_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
         L.trt_gemm_workspace_size.restype = i64
+        L.trt_gemm_noalloc.argtypes = gemm_args + [vp]
+        L.trt_gemm_noalloc.restype = i32
         L.trt_tile_count.argtypes = []
         L.trt_tile_count.restype = i32
         L.trt_tile_at.argtypes = [i32, ctypes.POINTER(TileDesc), ctypes.POINTER(i32),
@@ -178,6 +180,17 @@ def gemm_ws_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
     _check(lib().trt_gemm_ws(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
                              _epi(bias, relu, residual, ldr, scale), workspace or None,
                              workspace_bytes, stream or None))
+
+
+NOALLOC_SCRATCH_BYTES = 16777216   # TRT_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_noalloc_raw(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype,
+                     bias=0, relu=False, residual=0, ldr=0, scale=0, stream=0):
+    """trt_gemm_noalloc on raw device addresses (ints).  Raises TrtError."""
+    _check(lib().trt_gemm_noalloc(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype,
+                                  out_dtype, _epi(bias, relu, residual, ldr, scale),
+                                  stream or None))
 
 
 def workspace_size(M, N, K, opA=OP_N, opB=OP_N, in_dtype=F16) -> int:

@@ -206,7 +206,7 @@ struct SplitPlan {
   int splits, per_split;
   int64_t ws_bytes;
 };
-inline SplitPlan skinny_split_plan(int64_t M, int64_t N, int64_t K) {
+constexpr SplitPlan skinny_split_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t iters = (K + SkinnyTile::KW - 1) / SkinnyTile::KW;
   const int64_t panels = (N + SkinnySplit::PANEL - 1) / SkinnySplit::PANEL;
   int64_t splits = (SkinnySplit::TARGET_WGS + panels - 1) / panels;

@@ -3,6 +3,7 @@
 // contract of every entry point are in include/trt.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -991,6 +992,87 @@ trt_status trt_gemm_regtile(int64_t M, int64_t N, int64_t K, const void* A, int6
   a.g.b_bytes = sb;
   return launched(trt::launch_regtile(a, in_dtype, static_cast<hipStream_t>(stream)),
                   "register-tile gemm launch");
+}
+
+}  // extern "C"
+
+// ---- the allocation-free variant of trt_gemm_ws --------------------------------
+//
+// Its workspace is this array, one per device, in the library's code object
+// (no allocation by anyone).  Host code never passes the array's name to a
+// kernel: that is a host-side stand-in, not a device address.  The device
+// address is looked up once per device, with that device current, and
+// passed to the kernels like a caller's workspace.
+static __device__ __align__(256) char scratch[TRT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Every split plan fits the array: M <= 16 rows, and for p column panels a
+// plan takes at most ceil(512 / p) slices (fewer when K is short), so its
+// workspace is at most 16 * 4 * 256 p * ceil(512 / p) bytes over all p.
+constexpr bool scratch_fits_every_plan() {
+  for (int64_t p = 1; p <= 4096; ++p)
+    if (trt::skinny_split_plan(16, 256 * p, int64_t(1) << 30).ws_bytes > TRT_NOALLOC_SCRATCH_BYTES)
+      return false;
+  return true;
+}
+static_assert(scratch_fits_every_plan(), "the scratch array holds every split plan's workspace");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The device address of device dev's scratch array, looked up on first use
+// with dev current (the caller's current device is restored).
+trt_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(TRT_ERR_ARG, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess || !ptr)
+      return fail(TRT_ERR_HIP, std::string("scratch address: ") + hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return TRT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+trt_status trt_gemm_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            int32_t opA, const void* B, int64_t ldb, int32_t opB, void* C,
+                            int64_t ldc, int32_t in_dtype, int32_t out_dtype,
+                            const trt_epilogue* epi, void* stream) {
+  const trt_status s =
+      trt_validate(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, nullptr);
+  if (s != TRT_OK) return s;
+  const int64_t need = workspace_need(M, N, K, opA, opB, in_dtype);
+  if (need > TRT_NOALLOC_SCRATCH_BYTES)
+    return fail(TRT_ERR_SIZE, "this call needs " + std::to_string(need) +
+                                  " bytes of workspace, more than the " +
+                                  std::to_string((int64_t)TRT_NOALLOC_SCRATCH_BYTES) +
+                                  " of the allocation-free variant; use trt_gemm_ws");
+  void* ws = nullptr;
+  if (need > 0) {
+    // the device the stream runs on
+    int dev = -1;
+    const hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return fail(TRT_ERR_HIP, std::string("stream device: ") + hipGetErrorString(e));
+    const trt_status a = scratch_address(dev, &ws);
+    if (a != TRT_OK) return a;
+  }
+  return gemm_call(M, N, K, A, lda, opA, B, ldb, opB, C, ldc, in_dtype, out_dtype, epi, nullptr,
+                   true, ws, need > 0 ? TRT_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int32_t trt_abi_version(void) { return TRT_ABI_VERSION; }
