@@ -133,6 +133,22 @@ def _median(v):
     return v[len(v) // 2]
 
 
+def _step_kernel(name):
+    """Whether a kernel is part of a GEMM step: the GEMM kernel itself, or the
+    reduction that completes the split-K streaming path."""
+    return "gemm" in name or "skinny_split_reduce" in name
+
+
+def _per_step(rows, value):
+    """A step's figure: the median over the launches of each of the step's
+    kernels, summed over those kernels (one for most workloads, two for the
+    split-K path)."""
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(value(r))
+    return sum(_median(v) for v in by.values())
+
+
 def ingest_counters(root):
     """Build profiles/counters.json from rocprofv3 --pmc runs of this script.
 
@@ -164,10 +180,10 @@ def ingest_counters(root):
             copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
             big = max(int(r["Grid_Size"]) for r in copies)
             raw_copy = float(next(r["Counter_Value"] for r in copies if int(r["Grid_Size"]) == big))
-            gemm = [r for r in rows if "gemm" in r["Kernel_Name"]]
-            raw = _median([float(r["Counter_Value"]) for r in gemm])
+            gemm = [r for r in rows if _step_kernel(r["Kernel_Name"])]
+            raw = _per_step(gemm, lambda r: float(r["Counter_Value"]))
             factor = 256 * 1024 / raw_copy
-            e["kernel"] = sorted({r["Kernel_Name"] for r in gemm})[0]
+            e["kernel"] = " + ".join(sorted({r["Kernel_Name"] for r in gemm}))
             e[f"{cn}_size_kib_raw"] = raw
             e[f"{cn}_factor"] = round(factor, 5)
             e[f"{cn}_bytes_per_launch"] = int(raw * 1024 * factor)
@@ -175,15 +191,13 @@ def ingest_counters(root):
             e["bytes_per_launch"] = e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
         path = os.path.join(root, f"pmc_mfma_{w}", "run_counter_collection.csv")
         if os.path.exists(path):
-            rows = [r for r in _csv_rows(path) if "gemm" in r["Kernel_Name"]]
-            by = {}
-            for r in rows:
-                by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            med = {k: _median(v) for k, v in by.items()}
-            dur = {}
-            for r in rows:
-                dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-            ns = _median(list(dur.values()))
+            rows = [r for r in _csv_rows(path) if _step_kernel(r["Kernel_Name"])]
+            med = {c: _per_step([r for r in rows if r["Counter_Name"] == c],
+                                lambda r: float(r["Counter_Value"]))
+                   for c in sorted({r["Counter_Name"] for r in rows})}
+            first = rows[0]["Counter_Name"]
+            ns = _per_step([r for r in rows if r["Counter_Name"] == first],
+                           lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
             mops = sum(v for k, v in med.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
             gui = med.get("GRBM_GUI_ACTIVE", 0.0) / 8          # summed over the 8 XCDs
             busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)

@@ -63,3 +63,20 @@ def test_ingest_counters_scales_by_the_copy_and_keeps_provenance(tmp_path, monke
     assert e["provenance"] == {"taken": "2026-12-02", "gpu": "x"}
     got = bench.committed_counters("square")
     assert got is not None and bench.counters_entry(got)["taken"] == "2026-12-02"
+
+
+def test_ingest_counters_sums_the_kernels_of_a_step(tmp_path, monkeypatch):
+    # the split-K streaming step is two kernels: their medians add up
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(tmp_path / "counters.json"))
+    monkeypatch.setattr(bench, "WORKLOADS", ("skinny",))
+    hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    for cn, c in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        _csv(str(tmp_path / f"pmc_{cn}_skinny" / "run_counter_collection.csv"), hdr,
+             [["copyBuffer", 1 << 20, c, 256 * 1024],
+              ["gemm_skinny_split_kernel", 512, c, 1000], ["skinny_split_reduce_kernel", 64, c, 10],
+              ["gemm_skinny_split_kernel", 512, c, 1002], ["skinny_split_reduce_kernel", 64, c, 12],
+              ["gemm_skinny_split_kernel", 512, c, 998], ["skinny_split_reduce_kernel", 64, c, 11]])
+    e = bench.ingest_counters(str(tmp_path))["skinny"]
+    assert e["fetch_bytes_per_launch"] == (1000 + 11) * 1024
+    assert e["bytes_per_launch"] == 2 * (1000 + 11) * 1024
+    assert "skinny_split_reduce_kernel" in e["kernel"]
