@@ -207,6 +207,28 @@ def test_pipelined_192_tile_ragged_shapes():
 
 
 @pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
+def test_pipelined_every_step_count(tile):
+    # the main loop runs whole rounds of four K steps after nk mod 4 single
+    # steps: every residue, with and without a partial last step, from one
+    # step up; k-contiguous operands as short as 8 elements per row (copy
+    # offsets below the 3 KiB descriptor bias)
+    cases = [(8, 0), (32, 1), (40, 2), (64, 3), (96, 0), (104, 1), (128, 2), (136, 3),
+             (160, 0), (264, 1), (288, 2)]
+    for i, (K, ops) in enumerate(cases):
+        opA, opB = ops & 1, ops >> 1
+        M, N = tile[0] + 24, tile[1] + 40
+        dt = W.F16 if i % 2 else W.BF16
+        w = W.Workload("steps", M, N, K, opA=opA, opB=opB, lda=(M if opA else K),
+                       ldb=(K if opB else N), dtype=dt, dist="ternary", seed=6000 + i,
+                       bias=bool(i % 2), relu=bool(i % 3 == 0), residual=bool(i % 4 == 1),
+                       tile=tile)
+        run = Run(w)
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
+                      what=f"{tile} K={K} op={opA}{opB} dt={dt}")
+
+
+@pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
 def test_pipelined_tiles_overlapping_rows(tile):
     # rows-contiguous operands whose rows overlap in memory (a positive stride
     # below the row length: A^T with lda < M, row-major B with ldb < N) and a

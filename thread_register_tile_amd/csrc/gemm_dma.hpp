@@ -81,13 +81,57 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_ad
 }
 
 
+// One operand's copies of one K step for one wave: NCH 16-byte copies per
+// lane into the wave's NCH * 64 consecutive LDS slots.  M0 holds the LDS
+// address of the wave's first slot; copy i adds i KiB through the
+// instruction offset, which the direct-to-LDS load applies to both the
+// global and the LDS address, so one M0 value serves every copy.  Written
+// as inline assembly so that the compiler does not treat the copies as
+// pending LDS stores that every later LDS read must wait for: the kernel
+// orders copies and reads itself with s_waitcnt vmcnt and barriers.  The
+// s_nop covers the wait state between an M0 write and a direct-to-LDS load.
+template <int NCH>
+__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, uint32_t m0v,
+                                          const uint32_t (&v)[NCH]) {
+  static_assert(NCH >= 1 && NCH <= 4, "1 to 4 copies of 1 KiB per wave");
+  if constexpr (NCH == 1)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "{m0}"(m0v), "v"(v[0]), "s"(rs));
+  else if constexpr (NCH == 2)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+                 :: "{m0}"(m0v), "v"(v[0]), "v"(v[1]), "s"(rs));
+  else if constexpr (NCH == 3)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %4, 0 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %4, 0 offen offset:2048 lds"
+                 :: "{m0}"(m0v), "v"(v[0]), "v"(v[1]), "v"(v[2]), "s"(rs));
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
+                 :: "{m0}"(m0v), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(rs));
+}
+
 // One operand's copies and fragment reads.  R: tile rows (m for A, n for B);
 // KC: k-contiguous storage.
+//
+// Copy i of lane l of wave w fills LDS slot (w * NCH + i) * 64 + l; the
+// chunk it fetches is the one the slot holds under the swizzle.  The buffer
+// descriptor of a K step is based BIAS = (NCH - 1) KiB before the step's
+// first byte and each copy's offset register holds its chunk's offset plus
+// BIAS minus the instruction offset i KiB: never negative, and the address
+// the copy reads and the offset the record check sees are the chunk's own
+// (plus BIAS on both sides of the check).  The descriptor advances by one
+// K step per step: the base moves on and the record count shrinks, both in
+// loop-carried scalar registers.
 template <class TL, int R, bool KC>
 struct DmaOperand {
   static constexpr int CHUNKS = R * 32 * 2 / 16;         // 16-byte chunks per stage
   static constexpr int NCH = CHUNKS / TL::THREADS;       // per thread per stage
   static constexpr int BYTES = R * 64;                   // one stage of this operand
+  static constexpr uint32_t BIAS = (NCH - 1) * 1024;
   static_assert(CHUNKS % TL::THREADS == 0, "whole copy iterations");
   static_assert(KC || R >= 128, "the rows-contiguous swizzle needs 16 chunks per k row");
   // power-of-two R: the slot maps are GF(2)-linear bijections and their
@@ -102,50 +146,63 @@ struct DmaOperand {
                                 gf2::identity(ilog2(R / 8) + 5))),
                 "derived inverse slot maps");
   static_assert(TL::template slot_inverses_exact<R>(), "inverse slot maps");
+  // k-contiguous: a lane's copies sit 64 slots (16 rows) apart and the
+  // swizzle only reads row bits 1-3, so all of them carry the same k chunk
+  static constexpr bool same_chunk_per_lane() {
+    for (int s = 0; s + 64 < 4 * R; ++s)
+      if (TL::template kc_slot_g<R>(s) != TL::template kc_slot_g<R>(s + 64)) return false;
+    return true;
+  }
+  static_assert(!KC || same_chunk_per_lane(), "one k chunk per lane");
 
-  const char* base;      // operand base address
-  int64_t extent;        // operand extent in bytes
-  int64_t step_bytes;    // bytes per K step of 32
-  uint32_t voff[NCH];    // byte offset of each chunk this thread copies, at step 0
-  int kchunk;            // k offset (elements) of this thread's chunks (KC only)
+  const char* cur;       // descriptor base of the next step's copies
+  uint32_t rem;          // its record count while the step is live
+  uint32_t step_bytes;   // bytes per K step of 32
+  uint32_t voff[NCH];    // per copy: chunk offset + BIAS - i KiB
+  uint32_t tail_drop;    // k-contiguous: 2^31 where the lane's chunk lies past K
+                         // on the last, partial K step, else 0
 
   __device__ __forceinline__ void init(const uint16_t* X, int64_t ld, int64_t ext, int row0,
-                                       int t) {
-    base = reinterpret_cast<const char*>(X);
-    extent = ext;
+                                       int wave, int lane, int K) {
+    cur = reinterpret_cast<const char*>(X) - BIAS;
+    rem = (uint32_t)ext + BIAS;
+    int kchunk = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int s = i * TL::THREADS + t;  // LDS slot this lane fills
+      const int s = (wave * NCH + i) * 64 + lane;  // LDS slot this copy fills
+      uint32_t off;
       if (KC) {
         const int r = TL::template kc_slot_row<R>(s), g = TL::template kc_slot_g<R>(s);
-        voff[i] = (uint32_t)(((int64_t)(row0 + r) * ld + 8 * g) * 2);
-        kchunk = 8 * g;  // the same for every i: rows advance by THREADS/4
+        off = (uint32_t)(((int64_t)(row0 + r) * ld + 8 * g) * 2);
+        kchunk = 8 * g;
       } else {
         const int k = TL::template mn_slot_k<R>(s), c = TL::template mn_slot_c<R>(s);
-        voff[i] = (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2);
+        off = (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2);
       }
+      voff[i] = off + BIAS - 1024u * i;
     }
-    step_bytes = KC ? 64 : 64 * ld;
+    step_bytes = (uint32_t)(KC ? 64 : 64 * ld);
+    const int nk = (K + 31) / 32;
+    tail_drop = (KC && (K & 31) && (nk - 1) * 32 + kchunk >= K) ? 0x80000000u : 0u;
   }
 
-  // Buffer descriptor of K step `step` of nk: based at the step's first
-  // byte, its record count what is left of the operand; zero records (every
-  // copy reads zero and fetches nothing) past the operand's end and for the
-  // steps at or after nk that the pipeline issues ahead of the last one.
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int step, int nk) const {
-    const int64_t adv = (int64_t)step * step_bytes;
-    const bool live = step < nk && adv < extent;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (live ? adv : 0)), (short)0,
-                                             live ? (int)(extent - adv) : 0, 0x00020000);
-  }
-  // Copy i (0 <= i < NCH) of K step `step` into LDS region `dst` (this
-  // operand's part of one stage).  last_partial: K % 32 != 0 and `step` is
-  // the last step, whose chunks at k >= K are forced out of range.
-  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int step, uint32_t dst,
-                                            int wave, int K, bool last_partial, int i) const {
-    const bool drop = KC && last_partial && (step * 32 + kchunk >= K);
-    const uint32_t off = drop ? 0x80000000u : voff[i];
-    dma16(rs, __builtin_amdgcn_readfirstlane(dst + (i * TL::THREADS + 64 * wave) * 16), off);
+  // Copies of K step `step` of nk into the LDS region at `m0v` (the wave's
+  // first slot); then the descriptor moves to the next step.  Steps at or
+  // after nk (issued ahead of the last step by the pipeline) get zero
+  // records: every copy reads zero and fetches nothing.  On the last,
+  // partial step of a k-contiguous operand the chunks at k >= K are pushed
+  // out of range (offset + 2^31 exceeds every record count).
+  __device__ __forceinline__ void issue(int step, int nk, uint32_t m0v) {
+    const bool live = step < nk;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)cur, (short)0,
+                                                      live ? (int)rem : 0, 0x00020000);
+    uint32_t v[NCH];
+    const uint32_t drop = (KC && step == nk - 1) ? tail_drop : 0u;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) v[i] = KC ? (voff[i] | drop) : voff[i];
+    dma_block<NCH>(rs, m0v, v);
+    cur += step_bytes;
+    rem -= step_bytes;
   }
 };
 
@@ -464,7 +521,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   constexpr int LOADS = OpA::NCH + OpB::NCH;
   constexpr int EPI_BYTES = (BM / 2) * (BN + 4) * 4;
   constexpr int LDS_BYTES = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
-  static_assert(FM % 2 == 0 && LOADS <= HALF, "copies fit the first half");
+  static_assert(FM % 2 == 0 && HALF >= 2, "copies fit the first half");
   __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
   TRT_LDS char* lds = (TRT_LDS char*)lds_raw;
 
@@ -476,12 +533,16 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 
   OpA a;
   OpB b;
-  a.init(p.A, p.lda, p.a_bytes, m0, t);
-  b.init(p.B, p.ldb, p.b_bytes, n0, t);
+  a.init(p.A, p.lda, p.a_bytes, m0, wave, lane, p.K);
+  b.init(p.B, p.ldb, p.b_bytes, n0, wave, lane, p.K);
 
   const int nk = (p.K + 31) / 32;
-  const bool partial = (p.K & 31) != 0;
+  // LDS address of this wave's first copy slot in each operand region of
+  // stage 0 (wave-uniform)
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const uint32_t m0a = __builtin_amdgcn_readfirstlane(lds_base + wave * OpA::NCH * 1024);
+  const uint32_t m0b =
+      __builtin_amdgcn_readfirstlane(lds_base + OpA::BYTES + wave * OpB::NCH * 1024);
 
   // fragment reads start at the wave's first tile row / column: where the
   // ownership map places register 0 of lane 0
@@ -498,49 +559,56 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 
   u32x4 fa[FM], fb[FN];
 
+  // Stage of K step s: (s - r) mod NS, r = nk mod NS.  The main loop then
+  // starts at step r and runs whole rounds of NS steps, unrolled, in which
+  // every stage offset -- of the copies issued in step kt (step kt+NS-1)
+  // and of the fragments read in it (step kt+1) -- is a constant: the LDS
+  // reads take it in their offset field and the copies in their M0 value.
+  // The r steps before it (r < NS) use the same body with run-time offsets.
+  static_assert(is_pow2(NS), "stage index by mask");
+  const int r = nk & (NS - 1);
+  auto stage_of = [&](int s) { return (uint32_t)((s - r) & (NS - 1)) * STAGE; };
+
   // prologue: steps 0..NS-2 in flight, step 0's fragments in registers
 #pragma unroll
   for (int step = 0; step < NS - 1; ++step) {
-    const uint32_t st = lds_base + step * STAGE;
-    const bool lp = partial && step == nk - 1;
-    const auto rsa = a.rsrc(step, nk), rsb = b.rsrc(step, nk);
-#pragma unroll
-    for (int i = 0; i < OpA::NCH; ++i) a.issue_one(rsa, step, st, wave, p.K, lp, i);
-#pragma unroll
-    for (int i = 0; i < OpB::NCH; ++i) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, i);
+    a.issue(step, nk, m0a + stage_of(step));
+    b.issue(step, nk, m0b + stage_of(step));
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * LOADS));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  // the epilogue's strides in scalar registers before the loop: a scalar
+  // load still in flight at the loop's entry would force a full LDS wait
+  // (scalar loads complete out of order) at the top of every round
+  asm volatile("" ::"s"(p.ldc), "s"(p.ldr));
+  {
+    // in the order the loop reads them, so that the wait counts at the top
+    // of every step agree
+    TRT_LDS char* first = lds + stage_of(0);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) fb[j] = rb.read(lds, j);
+    for (int q = 0; q < HALF; ++q) {
+      if (q < HM) fa[q] = ra.read(first, q);
+      if (q % HM == HM - 1) fb[q / HM] = rb.read(first, q / HM);
+    }
 #pragma unroll
-  for (int i = 0; i < FM; ++i) fa[i] = ra.read(lds, i);
+    for (int i = HM; i < FM; ++i) fa[i] = ra.read(first, i);
+  }
 
-  // stage of the copies issued in step kt (step kt+NS-1) and of the
-  // fragments read in it (step kt+1), stepped modulo NS
-  int st_copy = NS - 1, st_next = 1 % NS;
-  for (int kt = 0; kt < nk; ++kt) {
+  // One K step kt: the copies of step kt+NS-1 go to stage offset `cst`, the
+  // fragments of step kt+1 come from `nxt`.
+  auto step_body = [&](int kt, uint32_t cst, TRT_LDS char* nxt) __attribute__((always_inline)) {
     const int step = kt + NS - 1;
-    const uint32_t st = lds_base + st_copy * STAGE;
-    const bool lp = partial && step == nk - 1;
-    const auto rsa = a.rsrc(step, nk), rsb = b.rsrc(step, nk);
-    TRT_LDS char* nxt = lds + st_next * STAGE;
-    st_copy = st_copy == NS - 1 ? 0 : st_copy + 1;
-    st_next = st_next == NS - 1 ? 0 : st_next + 1;
     // first half, column by column: the column fragment read last in the
-    // previous step is needed last; one copy every HALF/LOADS products
+    // previous step is needed last; A's copies after the first product, B's
+    // halfway through
 #pragma unroll
     for (int q = 0; q < HALF; ++q) {
       const int j = q / HM, i = q % HM;
       acc[i][j] = mfma16<DT>(fb[j], fa[i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int EVERY = HALF / LOADS;
-      if (q % EVERY == 0) {
-        const int c = q / EVERY;
-        if (c < OpA::NCH) a.issue_one(rsa, step, st, wave, p.K, lp, c);
-        else if (c < LOADS) b.issue_one(rsb, step, st + OpA::BYTES, wave, p.K, lp, c - OpA::NCH);
-      }
+      if (q == 0) a.issue(step, nk, m0a + cst);
+      if (q == HALF / 2) b.issue(step, nk, m0b + cst);
       __builtin_amdgcn_sched_barrier(0);
     }
     // every read of the stage that the next step's copies overwrite was
@@ -562,6 +630,13 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int i = HM; i < FM; ++i) fa[i] = ra.read(nxt, i);
+  };
+
+  for (int kt = 0; kt < r; ++kt) step_body(kt, stage_of(kt + NS - 1), lds + stage_of(kt + 1));
+  for (int kt = r; kt < nk; kt += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      step_body(kt + u, ((u + NS - 1) % NS) * STAGE, lds + ((u + 1) % NS) * STAGE);
   }
   // drain the copies issued past the end (zero records: they fetch nothing)
   // and all LDS reads before the staging area reuses the stages

@@ -56,9 +56,19 @@ using trt::TileTiny;
 // which masks k >= K explicitly.
 bool dma_ok(const GemmArgs& a, int opA, int opB, bool vec) {
   const bool a_kc = opA == TRT_OP_N, b_kc = opB == TRT_OP_T;
+  // every copy's byte offset from its K step's first byte, plus the
+  // descriptor bias of up to 3 KiB, stays below 2^31: k-contiguous, the
+  // operand's rows padded to a 256-row tile; rows-contiguous, 32 k rows
+  // plus a padded row
+  constexpr int64_t LIM = (int64_t(1) << 31) - 4096;
+  auto pad = [](int64_t n) { return (n + 255) / 256 * 256; };
+  auto fits = [&](bool kc, int64_t rows, int64_t ld, int64_t bytes) {
+    const int64_t span = kc ? pad(rows) * ld * 2 : 32 * ld * 2 + pad(rows) * 2;
+    return bytes < LIM && span < LIM;
+  };
   return vec && (a_kc ? a.K % 8 == 0 : a.M % 8 == 0 && a.lda >= a.M) &&
          (b_kc ? a.K % 8 == 0 : a.N % 8 == 0 && a.ldb >= a.N) &&
-         a.a_bytes < (int64_t(1) << 31) && a.b_bytes < (int64_t(1) << 31);
+         fits(a_kc, a.M, a.lda, a.a_bytes) && fits(b_kc, a.N, a.ldb, a.b_bytes);
 }
 
 // Whether the streaming kernel applies (M <= 16, A k-contiguous, B
