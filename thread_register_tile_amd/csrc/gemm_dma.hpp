@@ -559,15 +559,22 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
 
   u32x4 fa[FM], fb[FN];
 
-  // Stage of K step s: (s - r) mod NS, r = nk mod NS.  The main loop then
-  // starts at step r and runs whole rounds of NS steps, unrolled, in which
-  // every stage offset -- of the copies issued in step kt (step kt+NS-1)
-  // and of the fragments read in it (step kt+1) -- is a constant: the LDS
-  // reads take it in their offset field and the copies in their M0 value.
-  // The r steps before it (r < NS) use the same body with run-time offsets.
-  static_assert(is_pow2(NS), "stage index by mask");
-  const int r = nk & (NS - 1);
-  auto stage_of = [&](int s) { return (uint32_t)((s - r) & (NS - 1)) * STAGE; };
+  // Fragment f of a step in the order the schedule reads it: the first HM
+  // A fragments, then the B fragments, then the other A fragments.
+  auto read_frag = [&](TRT_LDS char* st, int f) __attribute__((always_inline)) {
+    if (f < HM) fa[f] = ra.read(st, f);
+    else if (f < HM + FN) fb[f - HM] = rb.read(st, f - HM);
+    else fa[f - FN] = ra.read(st, f - FN);
+  };
+
+  // Stage of K step s: (s - r) mod NS, r = nk mod NS.  The first r steps
+  // run with run-time stage offsets; the main loop then starts at step r
+  // and runs whole rounds of NS steps, unrolled, in which every stage
+  // offset -- of the copies issued in step kt (step kt+NS-1) and of the
+  // fragments read in it (step kt+1) -- is a constant: the LDS reads take it
+  // in their offset field and the copies in their M0 value.
+  const int r = nk % NS;
+  auto stage_of = [&](int s) { return (uint32_t)((s - r + NS) % NS) * STAGE; };
 
   // prologue: steps 0..NS-2 in flight, step 0's fragments in registers
 #pragma unroll
@@ -582,18 +589,9 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   // load still in flight at the loop's entry would force a full LDS wait
   // (scalar loads complete out of order) at the top of every round
   asm volatile("" ::"s"(p.ldc), "s"(p.ldr));
-  {
-    // in the order the loop reads them, so that the wait counts at the top
-    // of every step agree
-    TRT_LDS char* first = lds + stage_of(0);
+  // in the order the steps read them, so that the wait counts agree
 #pragma unroll
-    for (int q = 0; q < HALF; ++q) {
-      if (q < HM) fa[q] = ra.read(first, q);
-      if (q % HM == HM - 1) fb[q / HM] = rb.read(first, q / HM);
-    }
-#pragma unroll
-    for (int i = HM; i < FM; ++i) fa[i] = ra.read(first, i);
-  }
+  for (int f = 0; f < FM + FN; ++f) read_frag(lds + stage_of(0), f);
 
   // One K step kt: the copies of step kt+NS-1 go to stage offset `cst`, the
   // fragments of step kt+1 come from `nxt`.
@@ -619,17 +617,20 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    // second half: the next step's fragments into the registers as they die
+    // -- rows 0..HM-1 first, each column after its last product, rows
+    // HM..FM-1 at the end
 #pragma unroll
     for (int q = 0; q < HALF; ++q) {
       const int j = q / HM, i = HM + q % HM;
       acc[i][j] = mfma16<DT>(fb[j], fa[i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      if (q < HM) fa[q] = ra.read(nxt, q);
-      if (q % HM == HM - 1) fb[j] = rb.read(nxt, j);
+      if (q < HM) read_frag(nxt, q);
+      if (q % HM == HM - 1) read_frag(nxt, HM + j);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = HM; i < FM; ++i) fa[i] = ra.read(nxt, i);
+    for (int f = HM + FN; f < FM + FN; ++f) read_frag(nxt, f);
   };
 
   for (int kt = 0; kt < r; ++kt) step_body(kt, stage_of(kt + NS - 1), lds + stage_of(kt + 1));
