@@ -208,9 +208,12 @@ struct DmaOperand {
 
 // Fused epilogue of a pipelined tile, restaged through LDS.  The tile is
 // written in two passes of half its fragment rows: each wave stores its raw
-// fp32 accumulators of the pass into an LDS staging array (rows padded by 16
-// bytes so the 32 rows a fragment store touches fall on distinct banks);
-// then every thread takes four consecutive columns of successive rows,
+// fp32 accumulators of the pass into an LDS staging array -- rows of BN
+// floats, the 16-byte column group g of staged row r at position g XOR
+// (r mod 16), so that the 16 rows one fragment store touches fall on
+// distinct banks while every aligned run of 16 groups (256 bytes) stays in
+// its place, whatever the row width; then every thread takes four
+// consecutive columns of successive rows,
 // multiplies by the row scale, adds the bias it read once for those columns,
 // applies ReLU, adds the residual, rounds once to the output type OT and
 // stores one vector -- a wave covers 64 consecutive runs of a row ("My
@@ -297,7 +300,10 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   constexpr int MODE = MODE_ & 3;                      // EPI_MASKED / EPI_FAST / EPI_FAST_RES
   constexpr bool SCALED = (MODE_ & EPI_SCALED) != 0;   // fast modes: row scale present
   constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
-  constexpr int PITCH = BN + 4;                       // floats per staged row
+  constexpr int PITCH = BN;                           // floats per staged row
+  static_assert(BN % 64 == 0, "whole runs of 16 column groups per staged row");
+  // float index of the 4-aligned column c of staged row r
+  auto sidx = [](int r, int c) { return r * PITCH + ((((c >> 2) ^ (r & 15))) << 2); };
   constexpr int HALF_ROWS = ES::HALF_ROWS;
   constexpr int PANELS = ES::PANELS, T_PER_ROW = ES::T_PER_ROW;
   constexpr int ITERS = ES::ITERS;
@@ -349,7 +355,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
         const int reg = TL::FRAG_REGS * (fm * FN + fn);
         const int prow = ES::staged_row(TL::owner_row(reg, lane, wave));
         const int c = TL::owner_col(reg, lane, wave);
-        *reinterpret_cast<f32x4*>(stage + prow * PITCH + c) = acc[fm][fn];
+        *reinterpret_cast<f32x4*>(stage + sidx(prow, c)) = acc[fm][fn];
       }
     }
     __syncthreads();
@@ -359,7 +365,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
         f32x4 v[BATCH];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
-          v[i] = *reinterpret_cast<const f32x4*>(stage + prow_of(b0 + i) * PITCH + col_of(b0 + i));
+          v[i] = *reinterpret_cast<const f32x4*>(stage + sidx(prow_of(b0 + i), col_of(b0 + i)));
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
           const int it = b0 + i;
@@ -386,7 +392,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
         const int n = n0 + col_of(it);
         if (m >= p.M) continue;
         const bool vec = p.epi_vec && n + 4 <= p.N;
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + prow_of(it) * PITCH + col_of(it));
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(stage + sidx(prow_of(it), col_of(it)));
         float y[4] = {a4[0], a4[1], a4[2], a4[3]};
         if (scaled) {
           const float s = O::ld(p.scale, m);
@@ -519,7 +525,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   using OpB = DmaOperand<TL, BN, B_KC>;
   constexpr int STAGE = OpA::BYTES + OpB::BYTES;
   constexpr int LOADS = OpA::NCH + OpB::NCH;
-  constexpr int EPI_BYTES = (BM / 2) * (BN + 4) * 4;
+  constexpr int EPI_BYTES = (BM / 2) * BN * 4;
   constexpr int LDS_BYTES = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
   static_assert(FM % 2 == 0 && HALF >= 2, "copies fit the first half");
   __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
