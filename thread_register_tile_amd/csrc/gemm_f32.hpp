@@ -10,17 +10,21 @@
 //
 // Both operand tiles are staged k-contiguous in LDS, A as [128 m][32 k] and
 // B as [128 n][32 k], rows of 32 floats (eight 16-byte chunks) with chunk kc
-// of row r stored at chunk kc ^ sw(r), sw(r) = ((r >> 1) ^ (r >> 3)) & 7.
+// of row r stored at chunk kc ^ sw(r), sw(r) = (r ^ (r >> 3)) & 7.
 // Matrix-core step kk (0..7) of a K step takes k = 8*(lane/16) + kk: each
-// lane reads its 8 k of a fragment row as two 16-byte LDS loads, and the 16
-// lanes of a k group (16 consecutive rows) meet 16 distinct 16-byte bank
-// groups.  Storage with k contiguous in global memory is copied as 16-byte
-// chunks (row c/8, chunk c%8: one row pair per 16 lanes, conflict-free
-// writes).  Storage with m (or n) contiguous is read as a 4x4 block per
-// thread -- four k rows of four consecutive m, the 32 lanes of a half-wave
-// covering 512 contiguous bytes of one k row -- transposed in registers
-// and written as four k-contiguous chunks (two lanes per bank group, the
-// least for rows of one parity).  Out-of-range rows and k are zero.
+// lane reads its 8 k of a fragment row as two 16-byte LDS loads.  LDS serves
+// a 16-byte-per-lane access eight lanes at a time, each group of eight from
+// one 128-byte bank window: eight consecutive rows of one chunk sit at eight
+// distinct positions of their rows (sw takes row bits 0-2), so the fragment
+// reads are conflict-free (a swizzle on row bits 1-3 put row pairs on one
+// position and read 16.8 M conflict cycles per 4096^3 launch).  Storage with
+// k contiguous in global memory is copied as 16-byte chunks (row c/8, chunk
+// c%8: eight lanes fill one row).  Storage with m (or n) contiguous is read
+// as a 4x4 block per thread -- four k rows of four consecutive m, the 32
+// lanes of a half-wave covering 512 contiguous bytes of one k row --
+// transposed in registers and written as four k-contiguous chunks, eight
+// lanes on rows 4 apart, at distinct positions.  Out-of-range rows and k
+// are zero.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -33,7 +37,7 @@ __device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int f32_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int f32_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Float offset of chunk kc (4 floats of k) of LDS row r.
 __device__ __forceinline__ int f32_slot(int r, int kc) { return r * 32 + 4 * (kc ^ f32_swz(r)); }

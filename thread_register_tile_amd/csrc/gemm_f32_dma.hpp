@@ -46,7 +46,7 @@ struct F32DmaLayout {
 
   // k-contiguous: slot s -> (row, chunk of k)
   static constexpr int kc_row(int s) { return s / 8; }
-  static constexpr int kc_chunk(int s) { return (s % 8) ^ (((s / 8 >> 1) ^ (s / 8 >> 3)) & 7); }
+  static constexpr int kc_chunk(int s) { return (s % 8) ^ (((s / 8) ^ (s / 8 >> 3)) & 7); }
   // rows-contiguous: slot s -> (k, chunk of 4 rows)
   static constexpr int mn_k(int s) { return s / 32; }
   static constexpr int mn_chunk(int s) { return (s % 32) ^ (4 * ((s / 32 >> 3) & 3)); }
