@@ -90,6 +90,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_ad
 // pending LDS stores that every later LDS read must wait for: the kernel
 // orders copies and reads itself with s_waitcnt vmcnt and barriers.  The
 // s_nop covers the wait state between an M0 write and a direct-to-LDS load.
+// The compiler's hazard checks do not look inside the assembly: a scalar
+// operand (descriptor word) written by a vector instruction -- a spilled
+// scalar restored with v_readlane, a v_readfirstlane -- would need five wait
+// states before the load reads it.  The kernels keep their descriptors in
+// scalar arithmetic and spill no scalars; a build-time test checks the
+// compiled code for both.
 template <int NCH>
 __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, uint32_t m0v,
                                           const uint32_t (&v)[NCH]) {
