@@ -44,7 +44,8 @@ hipError_t launch_regtile(RegtileArgs a, int dt, hipStream_t s) {
   a.g.tiles_m = (int)((a.g.M + a.lm - 1) / a.lm);
   a.g.tiles_n = (int)((a.g.N + a.ln - 1) / a.ln);
   const dim3 grid((unsigned)((int64_t)a.g.tiles_m * a.g.tiles_n));
-  const size_t lds = sizeof(float) * kRegtilePitch * (a.lm + a.ln);
+  // both operand tiles, then one float that masked-off copies write to
+  const size_t lds = sizeof(float) * (kRegtilePitch * (a.lm + a.ln) + 1);
   // at most kRegtilePF elements of each operand tile per lane, operands
   // addressable by 32-bit byte offsets
   a.prefetch = (a.lm * kRegtileBK + kRegtileThreads - 1) / kRegtileThreads <= kRegtilePF &&

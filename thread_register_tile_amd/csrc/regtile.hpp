@@ -217,14 +217,20 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
     };
     // LDS: element (row, k) at row*PITCH + k; for k-contiguous storage
     // lane t's element u is (t/16 + 4u, t%16), a closed form
+    // (one branch on the storage order per operand and step, not one per
+    // element; an element outside the tile goes to the spare float after
+    // both tiles instead of being masked, so no lane mask stays live)
     auto put = [&](float* S, bool kc, int rows, const float (&v)[PF], const int (&lo)[PF]) {
+      const int off_spare = (int)(rt_lds + (lm + ln) * PITCH - S);  // the spare float
+      if (kc) {
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
-        if (kc) {
-          if (t / BK + 4 * u < rows) S[(t / BK + 4 * u) * PITCH + t % BK] = v[u];
-        } else {
-          if (lo[u] >= 0) S[lo[u]] = v[u];
+        for (int u = 0; u < PF; ++u) {
+          const int r = t / BK + 4 * u;
+          S[r < rows ? r * PITCH + t % BK : off_spare] = v[u];
         }
+      } else {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) S[lo[u] >= 0 ? lo[u] : off_spare] = v[u];
       }
     };
     const bool akc = !p.opA, bkc = p.opB;
@@ -236,10 +242,19 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
     // a k-contiguous element at k >= K lies inside the operand (the next
     // row); only the last K step has such elements, and only lanes whose k
     // t % 16 is past K
+    // bytes per K step of each operand
+    const int64_t a_step = BK * (akc ? 1 : g.lda) * isz, b_step = BK * (bkc ? 1 : g.ldb) * isz;
     auto step_loads = [&](int64_t k0) {
-      const bool kout = k0 + t % BK >= g.K;
-      fetch(rsrc(g.A, g.a_bytes, k0 * (akc ? 1 : g.lda) * isz), oa, akc && kout, va);
-      fetch(rsrc(g.B, g.b_bytes, k0 * (bkc ? 1 : g.ldb) * isz), ob, bkc && kout, vb);
+      const int64_t s = k0 / BK;
+      const auto ra = rsrc(g.A, g.a_bytes, s * a_step), rb = rsrc(g.B, g.b_bytes, s * b_step);
+      if (k0 + BK <= g.K) {   // (every step but a partial last one)
+        fetch(ra, oa, false, va);
+        fetch(rb, ob, false, vb);
+      } else {
+        const bool kout = k0 + t % BK >= g.K;
+        fetch(ra, oa, akc && kout, va);
+        fetch(rb, ob, bkc && kout, vb);
+      }
     };
     step_loads(0);
     for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
