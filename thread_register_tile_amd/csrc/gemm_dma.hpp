@@ -36,17 +36,17 @@
 // operand registers:
 //   the first half (fragment rows 0..FM/2-1 against every column, column by
 //   column), with this thread's copies of step kt+3 into stage (kt+3)%4
-//   spread through it;
+//   and the reads of step kt's fragment rows FM/2..FM-1 spread through it;
 //   wait for this wave's LDS reads and for its copies of step kt+1;
 //   workgroup barrier;
 //   the second half (rows FM/2..FM-1, column by column), refilling the
 //   operand registers with step kt+1's fragments as they die: rows
-//   0..FM/2-1 first, each column after its last product, rows FM/2..FM-1 at
-//   the end (they are needed only in the next step's second half).
-// Stage (kt+3)%4 was last read by reads issued in step kt-2, completed
-// before the barrier of step kt-1, which precedes the copies of step kt; the
-// copies of step kt+1 are complete and visible once every wave has waited
-// for its own and passed the barrier of step kt.
+//   0..FM/2-1 first, each column after its last product.
+// Stage (kt+3)%4 was last read by reads issued in step kt-2 and in the first
+// half of step kt-1, completed before the barrier of step kt-1, which
+// precedes the copies of step kt; the copies of step kt+1 are complete and
+// visible once every wave has waited for its own and passed the barrier of
+// step kt.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -514,13 +514,12 @@ struct FragReader {
 
 // Per K step one block of FM*FN products on one set of operand registers:
 // the first half (fragment rows 0..FM/2-1 against every column, column by
-// column) with this thread's copies of step kt+3 spread through it; then
-// the wait for step kt+1's
-// copies and the barrier; then the second half (rows FM/2..FM-1, column by
-// column) with the next stage's fragments read into the registers as they
-// die: rows 0..FM/2-1 first (dead since the first half), each column right
-// after its last product, rows FM/2..FM-1 at the end (they are needed only
-// in the next step's second half).
+// column) with this thread's copies of step kt+3 and the reads of the step's
+// own rows FM/2..FM-1 spread through it; then the wait for those reads and
+// for step kt+1's copies, and the barrier; then the second half (rows
+// FM/2..FM-1, column by column) with the next stage's rows 0..FM/2-1 and
+// columns read into the registers as they die (each column right after its
+// last product).
 template <class TL, int DT, bool A_KC, bool B_KC, int NS = 4>
 __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   static_assert(TL::BK == 32 && TL::MF == 16, "32-wide K steps of 16x16x32 fragments");
@@ -601,18 +600,21 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   // load still in flight at the loop's entry would force a full LDS wait
   // (scalar loads complete out of order) at the top of every round
   asm volatile("" ::"s"(p.ldc), "s"(p.ldr));
-  // in the order the steps read them, so that the wait counts agree
+  // in the order the steps read them, so that the wait counts agree (the
+  // lower A rows are read by each step itself, in its first half)
 #pragma unroll
-  for (int f = 0; f < FM + FN; ++f) read_frag(lds + stage_of(0), f);
+  for (int f = 0; f < HM + FN; ++f) read_frag(lds + stage_of(0), f);
 
   // One K step kt: the copies of step kt+NS-1 go to stage offset `cst`, the
   // fragments of step kt+1 come from `nxt`.
-  auto step_body = [&](int kt, uint32_t cst, TRT_LDS char* nxt) __attribute__((always_inline)) {
+  auto step_body = [&](int kt, uint32_t cst, TRT_LDS char* cur, TRT_LDS char* nxt) __attribute__((always_inline)) {
     const int step = kt + NS - 1;
     // first half, column by column: the column fragment read last in the
-    // previous step is needed last; A's copies halfway through, B's two
-    // products before the end (measured 1 % faster than copies after the
-    // first product and halfway, and than three other placements)
+    // previous step is needed last; this step's A rows HM..FM-1 read from
+    // its own stage after every second product (they are used after the
+    // barrier); A's copies halfway through, B's two products before the end
+    // (measured 1 % faster than copies after the first product and halfway,
+    // and than three other placements)
 #pragma unroll
     for (int q = 0; q < HALF; ++q) {
       const int j = q / HM, i = q % HM;
@@ -620,6 +622,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       if (q == HALF / 2) a.issue(step, nk, m0a + cst);
       if (q == HALF - 2) b.issue(step, nk, m0b + cst);
+      if (q % 2 == 1 && q / 2 < FM - HM) read_frag(cur, HM + FN + q / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     // every read of the stage that the next step's copies overwrite was
@@ -631,8 +634,9 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     // second half: the next step's fragments into the registers as they die
-    // -- rows 0..HM-1 first, each column after its last product, rows
-    // HM..FM-1 at the end
+    // -- rows 0..HM-1 first, each column after its last product (rows
+    // HM..FM-1 of the next step are read in its own first half, once this
+    // step's second half has used them)
 #pragma unroll
     for (int q = 0; q < HALF; ++q) {
       const int j = q / HM, i = HM + q % HM;
@@ -642,15 +646,14 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
       if (q % HM == HM - 1) read_frag(nxt, HM + j);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int f = HM + FN; f < FM + FN; ++f) read_frag(nxt, f);
   };
 
-  for (int kt = 0; kt < r; ++kt) step_body(kt, stage_of(kt + NS - 1), lds + stage_of(kt + 1));
+  for (int kt = 0; kt < r; ++kt)
+    step_body(kt, stage_of(kt + NS - 1), lds + stage_of(kt), lds + stage_of(kt + 1));
   for (int kt = r; kt < nk; kt += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u)
-      step_body(kt + u, ((u + NS - 1) % NS) * STAGE, lds + ((u + 1) % NS) * STAGE);
+      step_body(kt + u, ((u + NS - 1) % NS) * STAGE, lds + u * STAGE, lds + ((u + 1) % NS) * STAGE);
   }
   // drain the copies issued past the end (zero records: they fetch nothing)
   // and all LDS reads before the staging area reuses the stages
