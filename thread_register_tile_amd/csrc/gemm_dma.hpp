@@ -229,12 +229,21 @@ struct DmaOperand {
 //
 // MODE, chosen once per tile: EPI_FAST when the whole tile is inside C and
 // vector runs are allowed (EPI_FAST_RES with a residual; either with
-// EPI_SCALED added when there is a row scale), else EPI_MASKED.
+// EPI_SCALED added when there is a row scale, and EPI_RELU with ReLU),
+// else EPI_MASKED.
 // The fast modes have no branch in the store phase: the residual rows (and
 // row scales) of a pass are loaded before its staging writes, and the LDS
 // reads of a batch of rows are all issued before the first of their stores.
+// Their global addresses are a part common to the workgroup (scalar
+// registers) plus one 32-bit byte offset per thread, the same for every
+// item, so that no vector instruction computes an address.
 // EPI_MASKED masks and stores every element on its own.
-enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4 };
+enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4, EPI_RELU = 8 };
+
+// Largest leading dimension (elements) of C and of the residual that the fast
+// modes take: a thread's byte offset, at most ROWS_PER_STEP rows of 4-byte
+// elements into an item, then stays below 2^31.
+constexpr int64_t kEpiFastMaxLd = int64_t(1) << 25;
 
 // The store phase works on items: one item is a row of one column panel,
 // PANEL columns wide (the whole tile row when BN is a power of two, else 64
@@ -256,6 +265,8 @@ struct EpiShape {
   static_assert(BN % PANEL == 0 && TL::THREADS % T_PER_ROW == 0 &&
                     HALF_ROWS % ROWS_PER_STEP == 0,
                 "whole rows per step");
+  static_assert(ROWS_PER_STEP <= 16 && ROWS_PER_STEP * 4 * kEpiFastMaxLd <= (int64_t(1) << 31),
+                "a thread's byte offset into an item fits 31 bits");
 
   // Staging of the two passes.  Pass 0 takes the upper half of every wave's
   // rows (fragment rows fm < FM/2), pass 1 the lower half; a staged row
@@ -265,6 +276,14 @@ struct EpiShape {
   TRT_HD static int staged_row(int row) { return (row / TL::WTM) * HW + row % HW; }
   TRT_HD static int tile_row(int pass, int prow) {
     return (prow / HW) * TL::WTM + HW * pass + prow % HW;
+  }
+  // Tile row of item `it` of a pass for the threads of the first row of an
+  // item (t < T_PER_ROW); thread t takes the row t / T_PER_ROW below it
+  // (ROWS_PER_STEP divides HW, so an item's rows stay in one half of a wave
+  // row block, where tile_row is a shift).
+  static_assert(HW % ROWS_PER_STEP == 0, "an item's rows stay in one half block");
+  TRT_HD static int item_row(int pass, int it) {
+    return tile_row(pass, (it / PANELS) * ROWS_PER_STEP);
   }
 
   // The staging writes the accumulators where the layout module's ownership
@@ -305,12 +324,12 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   using ES = EpiShape<TL>;
   constexpr int MODE = MODE_ & 3;                      // EPI_MASKED / EPI_FAST / EPI_FAST_RES
   constexpr bool SCALED = (MODE_ & EPI_SCALED) != 0;   // fast modes: row scale present
+  constexpr bool RELU = (MODE_ & EPI_RELU) != 0;       // fast modes: ReLU
   constexpr int BN = TL::BN, FM = TL::FM, FN = TL::FN;
   constexpr int PITCH = BN;                           // floats per staged row
   static_assert(BN % 64 == 0, "whole runs of 16 column groups per staged row");
   // float index of the 4-aligned column c of staged row r
   auto sidx = [](int r, int c) { return r * PITCH + ((((c >> 2) ^ (r & 15))) << 2); };
-  constexpr int HALF_ROWS = ES::HALF_ROWS;
   constexpr int PANELS = ES::PANELS, T_PER_ROW = ES::T_PER_ROW;
   constexpr int ITERS = ES::ITERS;
   constexpr int BATCH = 8;                            // items read ahead of their stores
@@ -336,16 +355,43 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   constexpr int RING = O::BYTES == 2 ? ITERS : (ITERS < 16 ? ITERS : 16);
   static_assert(RING >= BATCH, "a batch fits the ring");
   auto row_of = [&](int pass, int it) { return m0 + ES::tile_row(pass, prow_of(it)); };
+  // Fast modes: the byte address of item `it` of a pass in a matrix with
+  // leading dimension ld is a part common to the workgroup plus the
+  // thread's offset (row t / T_PER_ROW of the item, column tcol; below 2^31
+  // because ld is below kEpiFastMaxLd there).  The common part is walked
+  // from item to item in the order the items are accessed; the empty asm
+  // keeps the compiler from computing every item's address ahead, which
+  // would take more scalar registers than there are.
+  const int trow = t / T_PER_ROW;
+  auto first = [&](const void* base, int64_t ld, int pass) {
+    return (const char*)base + ((int64_t)(m0 + ES::item_row(pass, 0)) * ld + n0) * O::BYTES;
+  };
+  auto advance = [&](const char*& q, int64_t ld, int pass, int it) {  // item it -> it + 1
+    const int dr = ES::item_row(pass, it + 1) - ES::item_row(pass, it);
+    const int dc = ((it + 1) % PANELS - it % PANELS) * ES::PANEL;
+    q += (dr * ld + dc) * O::BYTES;
+    asm volatile("" : "+s"(q));
+  };
+  const uint32_t c_off = (uint32_t)(trow * p.ldc + tcol) * O::BYTES;
+  const uint32_t r_off = (uint32_t)(trow * p.ldr + tcol) * O::BYTES;
+  const uint32_t s_off = (uint32_t)trow * O::BYTES;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     typename O::Vec rr[MODE == EPI_FAST_RES ? RING : 1];
     float sc[SCALED ? RING : 1];
+    // residual and row-scale items are fetched in ascending order
+    const char* rq = MODE == EPI_FAST_RES ? first(p.R, p.ldr, pass) : nullptr;
+    const char* sq = SCALED ? (const char*)p.scale + (int64_t)(m0 + ES::item_row(pass, 0)) * O::BYTES : nullptr;
     auto fetch = [&](int it) {
-      if constexpr (MODE != EPI_MASKED) {
-        const int m = row_of(pass, it);
-        if constexpr (MODE == EPI_FAST_RES)
-          rr[it % RING] = O::ld4_once(p.R, (int64_t)m * p.ldr + n0 + col_of(it));
-        if constexpr (SCALED) sc[it % RING] = O::ld(p.scale, m);
+      if constexpr (MODE == EPI_FAST_RES) {
+        rr[it % RING] = O::ld4_once_at(rq + r_off);
+        advance(rq, p.ldr, pass, it);
+      }
+      if constexpr (SCALED) {
+        sc[it % RING] = O::ld_at(sq + s_off);
+        const int dr = ES::item_row(pass, it + 1) - ES::item_row(pass, it);
+        sq += dr * O::BYTES;
+        asm volatile("" : "+s"(sq));
       }
     };
 #pragma unroll
@@ -366,6 +412,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     }
     __syncthreads();
     if constexpr (MODE != EPI_MASKED) {
+      const char* cq = first(p.C, p.ldc, pass);   // C items are stored in ascending order
 #pragma unroll
       for (int b0 = 0; b0 < ITERS; b0 += BATCH) {
         f32x4 v[BATCH];
@@ -381,10 +428,11 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
             // an absent bias is -0, an exact identity (-0 included), so no
             // select is needed
             y[e] = (SCALED ? v[i][e] * sc[it % RING] : v[i][e]) + bias_of(it, e);
-            y[e] = (relu && !(y[e] > 0.f)) ? 0.f : y[e];
+            if constexpr (RELU) y[e] = y[e] > 0.f ? y[e] : 0.f;
             if constexpr (MODE == EPI_FAST_RES) y[e] += O::elem(rr[it % RING], e);
           }
-          O::st4_once(p.C, (int64_t)row_of(pass, it) * p.ldc + n0 + col_of(it), O::pack(y));
+          O::st4_once_at(const_cast<char*>(cq) + c_off, O::pack(y));
+          advance(cq, p.ldc, pass, it);
         }
         // the batch's slots are free: fetch the items RING further on
 #pragma unroll
@@ -457,17 +505,22 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x4 (&ac
       }
     }
   }
-  if (!(p.epi_vec && n0 + TL::BN <= p.N && m0 + TL::BM <= p.M))
-    epilogue_passes<TL, OT, EPI_MASKED>(p, acc, stage, m0, n0, t, bias);
+  const bool fast = p.epi_vec && n0 + TL::BN <= p.N && m0 + TL::BM <= p.M &&
+                    p.ldc < kEpiFastMaxLd && (!p.R || p.ldr < kEpiFastMaxLd);
+  auto run = [&]<int MODE>() { epilogue_passes<TL, OT, MODE>(p, acc, stage, m0, n0, t, bias); };
+  auto fast_relu = [&]<int MODE>() {
+    if (p.relu) run.template operator()<MODE | EPI_RELU>();
+    else run.template operator()<MODE>();
+  };
+  if (!fast)
+    run.template operator()<EPI_MASKED>();
   else if (p.scale)
-    if (p.R)
-      epilogue_passes<TL, OT, EPI_FAST_RES | EPI_SCALED>(p, acc, stage, m0, n0, t, bias);
-    else
-      epilogue_passes<TL, OT, EPI_FAST | EPI_SCALED>(p, acc, stage, m0, n0, t, bias);
+    if (p.R) fast_relu.template operator()<EPI_FAST_RES | EPI_SCALED>();
+    else fast_relu.template operator()<EPI_FAST | EPI_SCALED>();
   else if (p.R)
-    epilogue_passes<TL, OT, EPI_FAST_RES>(p, acc, stage, m0, n0, t, bias);
+    fast_relu.template operator()<EPI_FAST_RES>();
   else
-    epilogue_passes<TL, OT, EPI_FAST>(p, acc, stage, m0, n0, t, bias);
+    fast_relu.template operator()<EPI_FAST>();
 }
 
 // Fragment addressing for 16-row fragments.  Lane group g = lane/16

@@ -66,6 +66,20 @@ __device__ __forceinline__ uint32_t from_f32<DT_BF16>(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two values rounded as from_f32 rounds them, packed with the first in the
+// low half (one conversion instruction on gfx950 for both types).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_f32(float lo, float hi) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+
 // ---- matrix core ---------------------------------------------------------------
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
@@ -134,8 +148,17 @@ struct Out {
     return to_f32<OT>((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
   }
   __device__ static Vec pack(const float (&y)[4]) {
-    return Vec{from_f32<OT>(y[0]) | (from_f32<OT>(y[1]) << 16),
-               from_f32<OT>(y[2]) | (from_f32<OT>(y[3]) << 16)};
+    return Vec{pack2_f32<OT>(y[0], y[1]), pack2_f32<OT>(y[2], y[3])};
+  }
+  // the same at a byte address (read / write once)
+  __device__ static Vec ld4_once_at(const char* a) {
+    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(a));
+  }
+  __device__ static void st4_once_at(char* a, Vec v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(a));
+  }
+  __device__ static float ld_at(const char* a) {
+    return to_f32<OT>(*reinterpret_cast<const uint16_t*>(a));
   }
 };
 template <>
@@ -158,6 +181,13 @@ struct Out<DT_F32> {
   }
   __device__ static float elem(Vec v, int e) { return v[e]; }
   __device__ static Vec pack(const float (&y)[4]) { return Vec{y[0], y[1], y[2], y[3]}; }
+  __device__ static Vec ld4_once_at(const char* a) {
+    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(a));
+  }
+  __device__ static void st4_once_at(char* a, Vec v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(a));
+  }
+  __device__ static float ld_at(const char* a) { return *reinterpret_cast<const float*>(a); }
 };
 
 // Calls f.template operator()<OT>() for the run-time output type (uniform
