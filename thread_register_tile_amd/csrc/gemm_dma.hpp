@@ -332,7 +332,10 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   auto sidx = [](int r, int c) { return r * PITCH + ((((c >> 2) ^ (r & 15))) << 2); };
   constexpr int PANELS = ES::PANELS, T_PER_ROW = ES::T_PER_ROW;
   constexpr int ITERS = ES::ITERS;
-  constexpr int BATCH = 8;                            // items read ahead of their stores
+  // items read ahead of their stores: 8 for 16-bit outputs, 4 for binary32
+  // (whose residual ring already holds 64 registers; with 8 the compiler
+  // spills, 4 % slower on the rowscale workload)
+  constexpr int BATCH = O::BYTES == 2 ? 8 : 4;
   static_assert(FM % 2 == 0 && TL::WM == 2, "two passes over the wave rows");
   static_assert(ITERS % BATCH == 0, "whole batches");
   static_assert(TL::FRAG_REGS == 4 && ES::staging_matches_owner(),
@@ -351,7 +354,10 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   // 16 items for binary32).  Item `it` is loaded when its slot frees, i.e.
   // right after item it - RING was used, so each load has at least one batch
   // of stores ahead of it; the first RING items are loaded before the
-  // staging writes.
+  // staging writes.  For 16-bit outputs (EARLY) the second pass's residual
+  // is loaded right after the first pass's staging writes, when half the
+  // accumulators are free, so that its latency passes under the first
+  // pass's stores (+0.6 % on the epilogue workload).
   constexpr int RING = O::BYTES == 2 ? ITERS : (ITERS < 16 ? ITERS : 16);
   static_assert(RING >= BATCH, "a batch fits the ring");
   auto row_of = [&](int pass, int it) { return m0 + ES::tile_row(pass, prow_of(it)); };
@@ -375,15 +381,26 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   const uint32_t c_off = (uint32_t)(trow * p.ldc + tcol) * O::BYTES;
   const uint32_t r_off = (uint32_t)(trow * p.ldr + tcol) * O::BYTES;
   const uint32_t s_off = (uint32_t)trow * O::BYTES;
+  constexpr bool EARLY = MODE == EPI_FAST_RES && O::BYTES == 2 && RING == ITERS;
+  typename O::Vec rr_all[EARLY ? 2 : 1][MODE == EPI_FAST_RES ? RING : 1];
+  auto fetch_res = [&](int ps) {
+    const char* q = first(p.R, p.ldr, ps);
+#pragma unroll
+    for (int it = 0; it < RING; ++it) {
+      rr_all[ps][it] = O::ld4_once_at(q + r_off);
+      advance(q, p.ldr, ps, it);
+    }
+  };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    typename O::Vec rr[MODE == EPI_FAST_RES ? RING : 1];
+    auto& rr = rr_all[EARLY ? pass : 0];
+    if constexpr (EARLY) if (pass == 0) fetch_res(0);
     float sc[SCALED ? RING : 1];
     // residual and row-scale items are fetched in ascending order
     const char* rq = MODE == EPI_FAST_RES ? first(p.R, p.ldr, pass) : nullptr;
     const char* sq = SCALED ? (const char*)p.scale + (int64_t)(m0 + ES::item_row(pass, 0)) * O::BYTES : nullptr;
     auto fetch = [&](int it) {
-      if constexpr (MODE == EPI_FAST_RES) {
+      if constexpr (MODE == EPI_FAST_RES && !EARLY) {
         rr[it % RING] = O::ld4_once_at(rq + r_off);
         advance(rq, p.ldr, pass, it);
       }
@@ -410,6 +427,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
         *reinterpret_cast<f32x4*>(stage + sidx(prow, c)) = acc[fm][fn];
       }
     }
+    if constexpr (EARLY) if (pass == 0) fetch_res(1);
     __syncthreads();
     if constexpr (MODE != EPI_MASKED) {
       const char* cq = first(p.C, p.ldc, pass);   // C items are stored in ascending order
