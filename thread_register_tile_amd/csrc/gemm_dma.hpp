@@ -193,19 +193,27 @@ struct DmaOperand {
   }
 
   // Copies of K step `step` of nk into the LDS region at `m0v` (the wave's
-  // first slot); then the descriptor moves to the next step.  Steps at or
-  // after nk (issued ahead of the last step by the pipeline) get zero
-  // records: every copy reads zero and fetches nothing.  On the last,
-  // partial step of a k-contiguous operand the chunks at k >= K are pushed
-  // out of range (offset + 2^31 exceeds every record count).
+  // first slot); then the descriptor moves to the next step.  CHECKED:
+  // steps at or after nk (issued ahead of the last step by the pipeline) get
+  // zero records, so every copy reads zero and fetches nothing, and on the
+  // last, partial step of a k-contiguous operand the chunks at k >= K are
+  // pushed out of range (offset + 2^31 exceeds every record count).
+  // Unchecked (the caller knows step < nk - 1): neither test, which saves
+  // the main loop six vector and about as many scalar instructions per step.
+  template <bool CHECKED>
   __device__ __forceinline__ void issue(int step, int nk, uint32_t m0v) {
-    const bool live = step < nk;
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)cur, (short)0,
-                                                      live ? (int)rem : 0, 0x00020000);
     uint32_t v[NCH];
-    const uint32_t drop = (KC && step == nk - 1) ? tail_drop : 0u;
+    int records = (int)rem;
+    if constexpr (CHECKED) {
+      records = step < nk ? (int)rem : 0;
+      const uint32_t drop = (KC && step == nk - 1) ? tail_drop : 0u;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) v[i] = KC ? (voff[i] | drop) : voff[i];
+      for (int i = 0; i < NCH; ++i) v[i] = KC ? (voff[i] | drop) : voff[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) v[i] = voff[i];
+    }
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)cur, (short)0, records, 0x00020000);
     dma_block<NCH>(rs, m0v, v);
     cur += step_bytes;
     rem -= step_bytes;
@@ -661,8 +669,8 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   // prologue: steps 0..NS-2 in flight, step 0's fragments in registers
 #pragma unroll
   for (int step = 0; step < NS - 1; ++step) {
-    a.issue(step, nk, m0a + stage_of(step));
-    b.issue(step, nk, m0b + stage_of(step));
+    a.template issue<true>(step, nk, m0a + stage_of(step));
+    b.template issue<true>(step, nk, m0b + stage_of(step));
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * LOADS));
   __builtin_amdgcn_s_barrier();
@@ -677,8 +685,8 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   for (int f = 0; f < HM + FN; ++f) read_frag(lds + stage_of(0), f);
 
   // One K step kt: the copies of step kt+NS-1 go to stage offset `cst`, the
-  // fragments of step kt+1 come from `nxt`.
-  auto step_body = [&](int kt, uint32_t cst, TRT_LDS char* cur, TRT_LDS char* nxt) __attribute__((always_inline)) {
+  // fragments of step kt+1 come from `nxt`; CHECKED as in DmaOperand::issue.
+  auto step_body = [&]<bool CHECKED>(int kt, uint32_t cst, TRT_LDS char* cur, TRT_LDS char* nxt) __attribute__((always_inline)) {
     const int step = kt + NS - 1;
     // first half, column by column: the column fragment read last in the
     // previous step is needed last; this step's A rows HM..FM-1 read from
@@ -691,8 +699,8 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
       const int j = q / HM, i = q % HM;
       acc[i][j] = mfma16<DT>(fb[j], fa[i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      if (q == HALF / 2) a.issue(step, nk, m0a + cst);
-      if (q == HALF - 2) b.issue(step, nk, m0b + cst);
+      if (q == HALF / 2) a.template issue<CHECKED>(step, nk, m0a + cst);
+      if (q == HALF - 2) b.template issue<CHECKED>(step, nk, m0b + cst);
       if (q % 2 == 1 && q / 2 < FM - HM) read_frag(cur, HM + FN + q / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -720,11 +728,24 @@ __global__ __launch_bounds__(TL::THREADS, 1) void gemm_dma_kernel(GemmArgs p) {
   };
 
   for (int kt = 0; kt < r; ++kt)
-    step_body(kt, stage_of(kt + NS - 1), lds + stage_of(kt), lds + stage_of(kt + 1));
-  for (int kt = r; kt < nk; kt += NS) {
+    step_body.template operator()<true>(kt, stage_of(kt + NS - 1), lds + stage_of(kt),
+                                        lds + stage_of(kt + 1));
+  // Whole rounds of NS steps from step r: every round but the last copies
+  // live steps before the last one only (a round from kt copies steps
+  // kt+NS-1 .. kt+2NS-2 <= nk-2), so it runs unchecked; the last round
+  // copies the last step and the steps past the end.
+  int kt = r;
+  for (; kt < nk - NS; kt += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u)
-      step_body(kt + u, ((u + NS - 1) % NS) * STAGE, lds + u * STAGE, lds + ((u + 1) % NS) * STAGE);
+      step_body.template operator()<false>(kt + u, ((u + NS - 1) % NS) * STAGE, lds + u * STAGE,
+                                           lds + ((u + 1) % NS) * STAGE);
+  }
+  if (kt < nk) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      step_body.template operator()<true>(kt + u, ((u + NS - 1) % NS) * STAGE, lds + u * STAGE,
+                                          lds + ((u + 1) % NS) * STAGE);
   }
   // drain the copies issued past the end (zero records: they fetch nothing)
   // and all LDS reads before the staging area reuses the stages
