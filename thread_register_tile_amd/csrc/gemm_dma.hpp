@@ -213,7 +213,7 @@ struct DmaOperand {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) v[i] = voff[i];
     }
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)cur, (short)0, records, 0x00020000);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)cur, (short)0, records, kBufferFormat);
     dma_block<NCH>(rs, m0v, v);
     cur += step_bytes;
     rem -= step_bytes;
@@ -235,23 +235,26 @@ struct DmaOperand {
 // and "Broadcasts cannot be treated as full register tiles": per-element
 // masks, bias held once per owned column).
 //
-// MODE, chosen once per tile: EPI_FAST when the whole tile is inside C and
-// vector runs are allowed (EPI_FAST_RES with a residual; either with
+// MODE, chosen once per tile: EPI_FAST when the tile's columns are inside C
+// and vector runs are allowed (EPI_FAST_RES with a residual; either with
 // EPI_SCALED added when there is a row scale, and EPI_RELU with ReLU),
 // else EPI_MASKED.
 // The fast modes have no branch in the store phase: the residual rows (and
 // row scales) of a pass are loaded before its staging writes, and the LDS
 // reads of a batch of rows are all issued before the first of their stores.
-// Their global addresses are a part common to the workgroup (scalar
-// registers) plus one 32-bit byte offset per thread, the same for every
-// item, so that no vector instruction computes an address.
+// They reach C, the residual and the row scale through buffer descriptors
+// based at the tile's first row, whose record counts end at row M: a store
+// to a row past M is dropped and a load from one reads zero, so a tile whose
+// last rows lie past M needs no test per element.  An access's byte offset
+// is a part common to the workgroup (scalar registers) plus one offset per
+// thread, the same for every item.
 // EPI_MASKED masks and stores every element on its own.
 enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4, EPI_RELU = 8 };
 
 // Largest leading dimension (elements) of C and of the residual that the fast
-// modes take: a thread's byte offset, at most ROWS_PER_STEP rows of 4-byte
-// elements into an item, then stays below 2^31.
-constexpr int64_t kEpiFastMaxLd = int64_t(1) << 25;
+// modes take: every byte offset into a tile of at most 256 rows of 4-byte
+// elements then fits 32 bits.
+constexpr int64_t kEpiFastMaxLd = int64_t(1) << 22;
 
 // The store phase works on items: one item is a row of one column panel,
 // PANEL columns wide (the whole tile row when BN is a power of two, else 64
@@ -273,8 +276,8 @@ struct EpiShape {
   static_assert(BN % PANEL == 0 && TL::THREADS % T_PER_ROW == 0 &&
                     HALF_ROWS % ROWS_PER_STEP == 0,
                 "whole rows per step");
-  static_assert(ROWS_PER_STEP <= 16 && ROWS_PER_STEP * 4 * kEpiFastMaxLd <= (int64_t(1) << 31),
-                "a thread's byte offset into an item fits 31 bits");
+  static_assert(TL::BM <= 256 && TL::BM * 4 * kEpiFastMaxLd <= (int64_t(1) << 32),
+                "byte offsets into the tile fit 32 bits");
 
   // Staging of the two passes.  Pass 0 takes the upper half of every wave's
   // rows (fragment rows fm < FM/2), pass 1 the lower half; a staged row
@@ -369,21 +372,27 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   constexpr int RING = O::BYTES == 2 ? ITERS : (ITERS < 16 ? ITERS : 16);
   static_assert(RING >= BATCH, "a batch fits the ring");
   auto row_of = [&](int pass, int it) { return m0 + ES::tile_row(pass, prow_of(it)); };
-  // Fast modes: the byte address of item `it` of a pass in a matrix with
-  // leading dimension ld is a part common to the workgroup plus the
-  // thread's offset (row t / T_PER_ROW of the item, column tcol; below 2^31
-  // because ld is below kEpiFastMaxLd there).  The common part is walked
-  // from item to item in the order the items are accessed; the empty asm
-  // keeps the compiler from computing every item's address ahead, which
-  // would take more scalar registers than there are.
+  // Fast modes: the byte offset of item `it` of a pass from the tile's
+  // corner in a matrix with leading dimension ld is a part common to the
+  // workgroup plus the thread's offset (row t / T_PER_ROW of the item,
+  // column tcol).  The common part is walked from item to item in the order
+  // the items are accessed; the empty asm keeps the compiler from computing
+  // every item's offset ahead, which would take more scalar registers than
+  // there are.  Descriptors: based at the tile's first row (and column),
+  // records up to row min(M, m0 + BM).
   const int trow = t / T_PER_ROW;
-  auto first = [&](const void* base, int64_t ld, int pass) {
-    return (const char*)base + ((int64_t)(m0 + ES::item_row(pass, 0)) * ld + n0) * O::BYTES;
+  const int rows = p.M - m0 < TL::BM ? p.M - m0 : TL::BM;
+  auto desc = [&](const void* base, int64_t ld, int64_t col) {
+    // integer arithmetic: base is null for an absent operand (the descriptor is then unused)
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((uintptr_t)base + (uintptr_t)(((int64_t)m0 * ld + col) * O::BYTES)), (short)0,
+        (int)((uint32_t)rows * (uint32_t)ld * O::BYTES), kBufferFormat);
   };
-  auto advance = [&](const char*& q, int64_t ld, int pass, int it) {  // item it -> it + 1
+  auto first = [&](int64_t ld, int pass) { return (uint32_t)(ES::item_row(pass, 0) * ld) * O::BYTES; };
+  auto advance = [&](uint32_t& q, int64_t ld, int pass, int it) {  // item it -> it + 1
     const int dr = ES::item_row(pass, it + 1) - ES::item_row(pass, it);
     const int dc = ((it + 1) % PANELS - it % PANELS) * ES::PANEL;
-    q += (dr * ld + dc) * O::BYTES;
+    q += (uint32_t)(dr * ld + dc) * O::BYTES;
     asm volatile("" : "+s"(q));
   };
   const uint32_t c_off = (uint32_t)(trow * p.ldc + tcol) * O::BYTES;
@@ -391,11 +400,12 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
   const uint32_t s_off = (uint32_t)trow * O::BYTES;
   constexpr bool EARLY = MODE == EPI_FAST_RES && O::BYTES == 2 && RING == ITERS;
   typename O::Vec rr_all[EARLY ? 2 : 1][MODE == EPI_FAST_RES ? RING : 1];
+  const auto rdesc = desc(p.R, p.ldr, n0), sdesc = desc(p.scale, 1, 0), cdesc = desc(p.C, p.ldc, n0);
   auto fetch_res = [&](int ps) {
-    const char* q = first(p.R, p.ldr, ps);
+    uint32_t q = first(p.ldr, ps);
 #pragma unroll
     for (int it = 0; it < RING; ++it) {
-      rr_all[ps][it] = O::ld4_once_at(q + r_off);
+      rr_all[ps][it] = O::ld4_buf(rdesc, q + r_off);
       advance(q, p.ldr, ps, it);
     }
   };
@@ -405,17 +415,15 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     if constexpr (EARLY) if (pass == 0) fetch_res(0);
     float sc[SCALED ? RING : 1];
     // residual and row-scale items are fetched in ascending order
-    const char* rq = MODE == EPI_FAST_RES ? first(p.R, p.ldr, pass) : nullptr;
-    const char* sq = SCALED ? (const char*)p.scale + (int64_t)(m0 + ES::item_row(pass, 0)) * O::BYTES : nullptr;
+    uint32_t rq = first(p.ldr, pass), sq = first(1, pass);
     auto fetch = [&](int it) {
       if constexpr (MODE == EPI_FAST_RES && !EARLY) {
-        rr[it % RING] = O::ld4_once_at(rq + r_off);
+        rr[it % RING] = O::ld4_buf(rdesc, rq + r_off);
         advance(rq, p.ldr, pass, it);
       }
       if constexpr (SCALED) {
-        sc[it % RING] = O::ld_at(sq + s_off);
-        const int dr = ES::item_row(pass, it + 1) - ES::item_row(pass, it);
-        sq += dr * O::BYTES;
+        sc[it % RING] = O::ld_buf(sdesc, sq + s_off);
+        sq += (uint32_t)(ES::item_row(pass, it + 1) - ES::item_row(pass, it)) * O::BYTES;
         asm volatile("" : "+s"(sq));
       }
     };
@@ -438,7 +446,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     if constexpr (EARLY) if (pass == 0) fetch_res(1);
     __syncthreads();
     if constexpr (MODE != EPI_MASKED) {
-      const char* cq = first(p.C, p.ldc, pass);   // C items are stored in ascending order
+      uint32_t cq = first(p.ldc, pass);   // C items are stored in ascending order
 #pragma unroll
       for (int b0 = 0; b0 < ITERS; b0 += BATCH) {
         f32x4 v[BATCH];
@@ -457,7 +465,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
             if constexpr (RELU) y[e] = y[e] > 0.f ? y[e] : 0.f;
             if constexpr (MODE == EPI_FAST_RES) y[e] += O::elem(rr[it % RING], e);
           }
-          O::st4_once_at(const_cast<char*>(cq) + c_off, O::pack(y));
+          O::st4_buf(cdesc, cq + c_off, O::pack(y));
           advance(cq, p.ldc, pass, it);
         }
         // the batch's slots are free: fetch the items RING further on
@@ -531,8 +539,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x4 (&ac
       }
     }
   }
-  const bool fast = p.epi_vec && n0 + TL::BN <= p.N && m0 + TL::BM <= p.M &&
-                    p.ldc < kEpiFastMaxLd && (!p.R || p.ldr < kEpiFastMaxLd);
+  const bool fast = p.epi_vec && n0 + TL::BN <= p.N && p.ldc < kEpiFastMaxLd &&
+                    (!p.R || p.ldr < kEpiFastMaxLd);
   auto run = [&]<int MODE>() { epilogue_passes<TL, OT, MODE>(p, acc, stage, m0, n0, t, bias); };
   auto fast_relu = [&]<int MODE>() {
     if (p.relu) run.template operator()<MODE | EPI_RELU>();

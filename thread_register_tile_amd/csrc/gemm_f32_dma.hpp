@@ -101,7 +101,7 @@ struct F32DmaOperand {
     const int64_t adv = (int64_t)step * step_bytes;
     const bool live = step < nk && adv < extent;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (live ? adv : 0)), (short)0,
-                                             live ? (int)(extent - adv) : 0, 0x00020000);
+                                             live ? (int)(extent - adv) : 0, kBufferFormat);
   }
 
   // Copy i of K step `step` into the region at LDS byte address dst.

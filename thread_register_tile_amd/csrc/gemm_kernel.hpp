@@ -117,6 +117,11 @@ __device__ __forceinline__ f32x16 mfma32<DT_BF16>(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // ---- output elements ---------------------------------------------------------------
+
+// Cache-policy operand of the buffer load / store builtins: non-temporal.
+constexpr int kNonTemporal = 2;
+// Format word (word 3) of the buffer descriptors this library builds.
+constexpr int kBufferFormat = 0x00020000;
 // C, bias, residual and row scale hold elements of the output type OT.  Out
 // reads and writes one element, or a run of four consecutive ones as one
 // vector (8 bytes for 16-bit types, 16 for binary32) when the caller has
@@ -150,15 +155,17 @@ struct Out {
   __device__ static Vec pack(const float (&y)[4]) {
     return Vec{pack2_f32<OT>(y[0], y[1]), pack2_f32<OT>(y[2], y[3])};
   }
-  // the same at a byte address (read / write once)
-  __device__ static Vec ld4_once_at(const char* a) {
-    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(a));
+  // the same through a buffer descriptor at byte offset off: a load past
+  // the record count reads zero, a store past it is dropped (the run of
+  // four read / written once: non-temporal)
+  __device__ static Vec ld4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, kNonTemporal);
   }
-  __device__ static void st4_once_at(char* a, Vec v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(a));
+  __device__ static void st4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, Vec v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)off, 0, kNonTemporal);
   }
-  __device__ static float ld_at(const char* a) {
-    return to_f32<OT>(*reinterpret_cast<const uint16_t*>(a));
+  __device__ static float ld_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return to_f32<OT>(__builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0));
   }
 };
 template <>
@@ -181,13 +188,15 @@ struct Out<DT_F32> {
   }
   __device__ static float elem(Vec v, int e) { return v[e]; }
   __device__ static Vec pack(const float (&y)[4]) { return Vec{y[0], y[1], y[2], y[3]}; }
-  __device__ static Vec ld4_once_at(const char* a) {
-    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(a));
+  __device__ static Vec ld4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(Vec, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kNonTemporal));
   }
-  __device__ static void st4_once_at(char* a, Vec v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(a));
+  __device__ static void st4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, Vec v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)off, 0, kNonTemporal);
   }
-  __device__ static float ld_at(const char* a) { return *reinterpret_cast<const float*>(a); }
+  __device__ static float ld_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0));
+  }
 };
 
 // Calls f.template operator()<OT>() for the run-time output type (uniform

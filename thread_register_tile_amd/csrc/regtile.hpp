@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kRegtileThreads) void gemm_regtile_kernel(RegtileAr
       int64_t left = bytes - adv;
       left = left < 0 ? 0 : left;
       return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)X + (adv < bytes ? adv : 0)),
-                                               (short)0, (int)left, 0x00020000);
+                                               (short)0, (int)left, kBufferFormat);
     };
     auto fetch = [&](__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[PF], bool zero, float (&v)[PF]) {
 #pragma unroll
