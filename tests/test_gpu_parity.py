@@ -229,6 +229,34 @@ def test_pipelined_every_step_count(tile):
 
 
 @pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
+def test_pipelined_epilogue_cut_tiles(tile):
+    # tiles cut by M and by N: with N a multiple of 4 the fast store phase
+    # takes them (stores past row M or column N dropped, residual and row
+    # scale there read as zero), otherwise the masked one; C has padded rows
+    # and guard bands, every output dtype, every epilogue operand
+    BM, BN = tile[0], tile[1]
+    cases = [  # M, N, opA, opB, in dtype, out dtype, row scale
+        (BM + 37, BN + 4, 0, 1, W.F16, W.F16, False),
+        (2 * BM - 8, 2 * BN - 12, 1, 1, W.BF16, W.F32, True),
+        (BM + 8, BN + 36, 0, 1, W.BF16, W.BF16, False),
+        (BM + 1, 2 * BN - 8, 0, 0, W.F16, W.BF16, True),
+        (BM + 5, BN + 6, 0, 1, W.F16, W.F16, True),          # N % 4 != 0: masked
+        (3, BN + 20, 0, 1, W.BF16, W.F16, False),             # one partial tile row
+    ]
+    for i, (M, N, opA, opB, dt, odt, scale) in enumerate(cases):
+        K = 72
+        a_cols = M if opA else K
+        b_cols = K if opB else N
+        w = W.Workload("cut", M, N, K, opA=opA, opB=opB, lda=a_cols + 8, ldb=b_cols + 8,
+                       dtype=dt, out_dtype=odt, dist="ternary", seed=6100 + i, bias=True,
+                       relu=bool(i % 2), residual=True, row_scale=scale, tile=tile)
+        run = Run(w, ldc=N + 4 + 4 * (i % 2))
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), odt, exact=True,
+                      what=f"{tile} M={M} N={N} op={opA}{opB} {dt}->{odt}")
+
+
+@pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
 def test_pipelined_tiles_overlapping_rows(tile):
     # rows-contiguous operands whose rows overlap in memory (a positive stride
     # below the row length: A^T with lda < M, row-major B with ldb < N) and a

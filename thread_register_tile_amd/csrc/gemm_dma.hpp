@@ -235,26 +235,30 @@ struct DmaOperand {
 // and "Broadcasts cannot be treated as full register tiles": per-element
 // masks, bias held once per owned column).
 //
-// MODE, chosen once per tile: EPI_FAST when the tile's columns are inside C
-// and vector runs are allowed (EPI_FAST_RES with a residual; either with
-// EPI_SCALED added when there is a row scale, and EPI_RELU with ReLU),
-// else EPI_MASKED.
+// MODE, chosen once per tile: EPI_FAST when vector runs are allowed and
+// every run of four columns lies wholly inside or wholly outside C (the
+// tile's columns are inside C, or N is a multiple of 4), EPI_FAST_RES with a
+// residual; either with EPI_SCALED added when there is a row scale, and
+// EPI_RELU with ReLU; else EPI_MASKED.
 // The fast modes have no branch in the store phase: the residual rows (and
 // row scales) of a pass are loaded before its staging writes, and the LDS
 // reads of a batch of rows are all issued before the first of their stores.
 // They reach C, the residual and the row scale through buffer descriptors
 // based at the tile's first row, whose record counts end at row M: a store
 // to a row past M is dropped and a load from one reads zero, so a tile whose
-// last rows lie past M needs no test per element.  An access's byte offset
-// is a part common to the workgroup (scalar registers) plus one offset per
-// thread, the same for every item.
+// last rows lie past M needs no test per element.  Columns past N are
+// handled the same way: the thread's offset for such a run is pushed past
+// 2^31, beyond every record count.  An access's byte offset is a part
+// common to the workgroup (scalar registers) plus one offset per thread and
+// column panel, the same for every item.
 // EPI_MASKED masks and stores every element on its own.
 enum { EPI_MASKED = 0, EPI_FAST = 1, EPI_FAST_RES = 2, EPI_SCALED = 4, EPI_RELU = 8 };
 
 // Largest leading dimension (elements) of C and of the residual that the fast
 // modes take: every byte offset into a tile of at most 256 rows of 4-byte
-// elements then fits 32 bits.
-constexpr int64_t kEpiFastMaxLd = int64_t(1) << 22;
+// elements then stays below 2^31 (and with 2^31 added for a run past N,
+// below 2^32).
+constexpr int64_t kEpiFastMaxLd = int64_t(1) << 21;
 
 // The store phase works on items: one item is a row of one column panel,
 // PANEL columns wide (the whole tile row when BN is a power of two, else 64
@@ -276,8 +280,8 @@ struct EpiShape {
   static_assert(BN % PANEL == 0 && TL::THREADS % T_PER_ROW == 0 &&
                     HALF_ROWS % ROWS_PER_STEP == 0,
                 "whole rows per step");
-  static_assert(TL::BM <= 256 && TL::BM * 4 * kEpiFastMaxLd <= (int64_t(1) << 32),
-                "byte offsets into the tile fit 32 bits");
+  static_assert(TL::BM <= 256 && TL::BM * 4 * kEpiFastMaxLd <= (int64_t(1) << 31),
+                "byte offsets into the tile stay below 2^31");
 
   // Staging of the two passes.  Pass 0 takes the upper half of every wave's
   // rows (fragment rows fm < FM/2), pass 1 the lower half; a staged row
@@ -395,8 +399,14 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     q += (uint32_t)(dr * ld + dc) * O::BYTES;
     asm volatile("" : "+s"(q));
   };
-  const uint32_t c_off = (uint32_t)(trow * p.ldc + tcol) * O::BYTES;
-  const uint32_t r_off = (uint32_t)(trow * p.ldr + tcol) * O::BYTES;
+  // per column panel: the thread's run of four columns inside C, or not
+  uint32_t c_off[PANELS], r_off[PANELS];
+#pragma unroll
+  for (int q = 0; q < PANELS; ++q) {
+    const uint32_t out = n0 + q * ES::PANEL + tcol < p.N ? 0u : 0x80000000u;
+    c_off[q] = (uint32_t)(trow * p.ldc + tcol) * O::BYTES | out;
+    r_off[q] = (uint32_t)(trow * p.ldr + tcol) * O::BYTES | out;
+  }
   const uint32_t s_off = (uint32_t)trow * O::BYTES;
   constexpr bool EARLY = MODE == EPI_FAST_RES && O::BYTES == 2 && RING == ITERS;
   typename O::Vec rr_all[EARLY ? 2 : 1][MODE == EPI_FAST_RES ? RING : 1];
@@ -405,7 +415,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     uint32_t q = first(p.ldr, ps);
 #pragma unroll
     for (int it = 0; it < RING; ++it) {
-      rr_all[ps][it] = O::ld4_buf(rdesc, q + r_off);
+      rr_all[ps][it] = O::ld4_buf(rdesc, q + r_off[it % PANELS]);
       advance(q, p.ldr, ps, it);
     }
   };
@@ -418,7 +428,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
     uint32_t rq = first(p.ldr, pass), sq = first(1, pass);
     auto fetch = [&](int it) {
       if constexpr (MODE == EPI_FAST_RES && !EARLY) {
-        rr[it % RING] = O::ld4_buf(rdesc, rq + r_off);
+        rr[it % RING] = O::ld4_buf(rdesc, rq + r_off[it % PANELS]);
         advance(rq, p.ldr, pass, it);
       }
       if constexpr (SCALED) {
@@ -465,7 +475,7 @@ __device__ __forceinline__ void epilogue_passes(const GemmArgs& p,
             if constexpr (RELU) y[e] = y[e] > 0.f ? y[e] : 0.f;
             if constexpr (MODE == EPI_FAST_RES) y[e] += O::elem(rr[it % RING], e);
           }
-          O::st4_buf(cdesc, cq + c_off, O::pack(y));
+          O::st4_buf(cdesc, cq + c_off[it % PANELS], O::pack(y));
           advance(cq, p.ldc, pass, it);
         }
         // the batch's slots are free: fetch the items RING further on
@@ -539,8 +549,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x4 (&ac
       }
     }
   }
-  const bool fast = p.epi_vec && n0 + TL::BN <= p.N && p.ldc < kEpiFastMaxLd &&
-                    (!p.R || p.ldr < kEpiFastMaxLd);
+  const bool fast = p.epi_vec && (n0 + TL::BN <= p.N || p.N % 4 == 0) &&
+                    p.ldc < kEpiFastMaxLd && (!p.R || p.ldr < kEpiFastMaxLd);
   auto run = [&]<int MODE>() { epilogue_passes<TL, OT, MODE>(p, acc, stage, m0, n0, t, bias); };
   auto fast_relu = [&]<int MODE>() {
     if (p.relu) run.template operator()<MODE | EPI_RELU>();
