@@ -257,6 +257,24 @@ def test_pipelined_epilogue_cut_tiles(tile):
 
 
 @pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
+def test_pipelined_residual_strides(tile):
+    # residual rows that overlap (a positive ldr below N: the masked store
+    # phase) or are padded (the fast one), on tiles cut by M and N
+    BM, BN = tile[0], tile[1]
+    for i, (M, N, ldr, dt) in enumerate([(BM + 40, BN + 8, BN - 24, W.F16),
+                                         (2 * BM - 8, BN + 16, 1, W.BF16),
+                                         (BM + 8, 2 * BN, 2 * BN + 12, W.BF16)]):
+        K = 64
+        w = W.Workload("ldr", M, N, K, lda=K + 8, ldb=N + 8, dtype=dt, dist="ternary",
+                       seed=6200 + i, bias=True, relu=bool(i % 2), residual=True, ldr=ldr,
+                       tile=tile)
+        run = Run(w, ldc=N + 4)
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), dt, exact=True,
+                      what=f"{tile} M={M} N={N} ldr={ldr}")
+
+
+@pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
 def test_pipelined_tiles_overlapping_rows(tile):
     # rows-contiguous operands whose rows overlap in memory (a positive stride
     # below the row length: A^T with lda < M, row-major B with ldb < N) and a

@@ -549,8 +549,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& p, const f32x4 (&ac
       }
     }
   }
+  // a residual whose rows overlap (ldr < N) has real columns past its
+  // record count: it takes the masked phase
   const bool fast = p.epi_vec && (n0 + TL::BN <= p.N || p.N % 4 == 0) &&
-                    p.ldc < kEpiFastMaxLd && (!p.R || p.ldr < kEpiFastMaxLd);
+                    p.ldc < kEpiFastMaxLd && (!p.R || (p.ldr >= p.N && p.ldr < kEpiFastMaxLd));
   auto run = [&]<int MODE>() { epilogue_passes<TL, OT, MODE>(p, acc, stage, m0, n0, t, bias); };
   auto fast_relu = [&]<int MODE>() {
     if (p.relu) run.template operator()<MODE | EPI_RELU>();

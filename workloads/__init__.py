@@ -42,6 +42,7 @@ class Workload:
     lda: Optional[int] = None
     ldb: Optional[int] = None
     ldc: Optional[int] = None
+    ldr: Optional[int] = None     # residual leading dimension; None: N
     dtype: int = F16       # input type of A and B (F16, BF16 or F32)
     out_dtype: Optional[int] = None   # output type (C, bias, residual, row scale); None: dtype
     row_scale: bool = False
@@ -84,7 +85,7 @@ class Workload:
 
     @property
     def ldr_(self):
-        return self.N
+        return self.ldr if self.ldr is not None else self.N
 
     @property
     def odt(self):
@@ -150,7 +151,7 @@ def shrink(w: Workload, M=None, N=None, K=None, **kw) -> Workload:
     M = M or w.M
     N = N or w.N
     K = K or w.K
-    new = replace(w, M=M, N=N, K=K, lda=None, ldb=None, ldc=None, **kw)
+    new = replace(w, M=M, N=N, K=K, lda=None, ldb=None, ldc=None, ldr=None, **kw)
     pad_a = (w.lda_ - w.a_cols) if w.lda is not None else 0
     pad_b = (w.ldb_ - w.b_cols) if w.ldb is not None else 0
     return replace(new, lda=new.a_cols + pad_a if pad_a else None,
@@ -211,7 +212,7 @@ def _padded(w: Workload, tensor_id: int, rows: int, cols: int, ld: int, dtype=No
 
 def make_inputs(w: Workload) -> dict:
     """Raw host buffers for a workload: A, B (flat raw bits of the input type)
-    and, if enabled, bias [N], residual [M, N] (leading dimension N) and row
+    and, if enabled, bias [N], residual [M, N] (leading dimension ldr_) and row
     scale [M] (flat, of the output type: uint16, or uint32 for F32)."""
     out = {
         "A": _padded(w, TENSOR_A, w.a_rows, w.a_cols, w.lda_),
@@ -223,7 +224,7 @@ def make_inputs(w: Workload) -> dict:
     if w.bias:
         out["bias"] = _padded(w, TENSOR_BIAS, 1, w.N, w.N, w.odt)
     if w.residual:
-        out["R"] = _padded(w, TENSOR_R, w.M, w.N, w.N, w.odt)
+        out["R"] = _padded(w, TENSOR_R, w.M, w.N, w.ldr_, w.odt)
     if w.row_scale:
         out["scale"] = _padded(w, TENSOR_SCALE, 1, w.M, w.M, w.odt)
     return out
