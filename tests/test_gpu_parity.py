@@ -274,6 +274,46 @@ def test_pipelined_residual_strides(tile):
                       what=f"{tile} M={M} N={N} ldr={ldr}")
 
 
+def test_randomized_shapes_strides_and_epilogues():
+    # a seeded sweep over what the boundary accepts: shapes from 1 to 700,
+    # storage orders, padded or overlapping input and residual rows, padded C,
+    # every input and output type, every epilogue operand, automatic and
+    # explicit tiles (binary32 operands: automatic or 128x128x32, the only
+    # tile they run on); every element compared with the oracle, bit-exact
+    rng = np.random.default_rng(77)
+    tiles = [None, None, (256, 256, 32), (256, 192, 32), (128, 128, 32), (64, 64, 64),
+             (16, 64, 32), (128, 128, 64)]
+    for i in range(80):
+        M, N, K = (int(rng.integers(1, 700)) for _ in range(3))
+        if rng.random() < 0.5:
+            M, N, K = (8 * max(1, x // 8) for x in (M, N, K))
+        opA, opB = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+        dt = [W.F16, W.BF16, W.F32][int(rng.integers(0, 3))]
+        odt = [None, W.F16, W.BF16, W.F32][int(rng.integers(0, 4))]
+
+        def ld(cols):  # padded, or (one case in ten) rows that overlap
+            if rng.random() < 0.9:
+                return cols + int(rng.choice([0, 0, 4, 8, 24]))
+            return max(1, cols - int(rng.integers(1, max(2, cols))))
+        lda, ldb = ld(M if opA else K), ld(K if opB else N)
+        res = bool(rng.random() < 0.4)
+        ldr = ld(N)
+        tile = tiles[int(rng.integers(0, len(tiles)))]
+        if dt == W.F32 and tile is not None:
+            tile = (128, 128, 32)
+        if tile == (16, 64, 32) and M > 64:
+            tile = None
+        w = W.Workload("sweep", M, N, K, opA=opA, opB=opB, lda=lda, ldb=ldb, dtype=dt,
+                       out_dtype=odt, dist="ternary", seed=9000 + i, bias=bool(rng.random() < 0.5),
+                       relu=bool(rng.random() < 0.4), residual=res, ldr=ldr if res else None,
+                       row_scale=bool(rng.random() < 0.3), tile=tile)
+        run = Run(w, ldc=N + int(rng.choice([0, 0, 4, 8, 12])))
+        run.launch()
+        assert_accept(run.result(), reference_block(w, run.host), w.odt, exact=True,
+                      what=f"case {i}: M={M} N={N} K={K} op={opA}{opB} lda={lda} ldb={ldb} "
+                           f"dt={dt} odt={w.odt} tile={tile} res={res} ldr={w.ldr_}")
+
+
 @pytest.mark.parametrize("tile", [(256, 256, 32), (256, 192, 32), (128, 128, 32)])
 def test_pipelined_tiles_overlapping_rows(tile):
     # rows-contiguous operands whose rows overlap in memory (a positive stride
