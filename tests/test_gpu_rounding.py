@@ -1,11 +1,12 @@
-"""Rounding of the fp32 accumulator to a binary16 output on every kernel
-family, on sums that fall exactly halfway between neighbouring binary16
-values: above 2048 (where the spacing is 2 or more) and in the subnormal
-range (spacing 2^-24).  The pages fix the accumulation in fp32 and one cast
-at the end ("My Triton From Scratch, Part 16: Register Tiles", the named
-GEMM of "Named layouts"); the cast rounds to nearest, ties to even.  Every
-input is a normal binary16 number and every sum is exact in fp32, so the
-expected bits are the oracle's round-to-nearest-even of the exact sum.
+"""Rounding of the fp32 accumulator to a 16-bit output on every kernel
+family, on sums that fall exactly halfway between neighbouring output
+values: binary16 above 2048 (where the spacing is 2 or more) and in its
+subnormal range (spacing 2^-24), bfloat16 above 256.  The pages fix the
+accumulation in fp32 and one cast at the end ("My Triton From Scratch,
+Part 16: Register Tiles", the named GEMM of "Named layouts"); the cast
+rounds to nearest, ties to even.  Every input is a normal number of the
+input type and every sum is exact in fp32, so the expected bits are the
+oracle's round-to-nearest-even of the exact sum.
 """
 import numpy as np
 import pytest
@@ -29,6 +30,17 @@ def _host(w, a_vals, b_vals, a_p, b_p, seed):
     return {"A": A.astype(np.float16).view(np.uint16).reshape(-1),
             "B": B.astype(np.float16).view(np.uint16).reshape(-1),
             "bias": None, "R": None, "scale": None}
+
+
+def _host_bf16(w, a_vals, b_vals, a_p, b_p, seed):
+    # the values are small integers and powers of two: exact in bfloat16,
+    # whose bits are the top half of the binary32 bits
+    rng = np.random.default_rng(seed)
+    A = rng.choice(np.array(a_vals, np.float32), size=(w.M, w.K), p=a_p)
+    B = rng.choice(np.array(b_vals, np.float32), size=(w.K, w.N), p=b_p)
+    bits = lambda X: (X.view(np.uint32) >> 16).astype(np.uint16).reshape(-1)
+    assert (bits(A).astype(np.uint32) << 16 == A.view(np.uint32).reshape(-1)).all()
+    return {"A": bits(A), "B": bits(B), "bias": None, "R": None, "scale": None}
 
 
 @pytest.mark.parametrize("tile,M", CASES)
@@ -60,3 +72,17 @@ def test_f16_subnormal_ties(tile, M):
     run = Run(w, inputs=host)
     run.launch()
     assert_accept(run.result(), ref, W.F16, exact=True, what=f"{tile} subnormal ties")
+
+
+@pytest.mark.parametrize("tile,M", CASES)
+def test_bf16_ties_above_256(tile, M):
+    # sums 256 a + b of small integers: every odd value in [256, 512), every
+    # value 2 mod 4 in [512, 1024), ... is a tie
+    w = W.Workload("tiesbf", M, 320, 64, dtype=W.BF16, tile=tile)
+    host = _host_bf16(w, [-256, -1, 0, 1, 256], [-1, 0, 1],
+                      [0.1, 0.2, 0.4, 0.2, 0.1], [0.25, 0.5, 0.25], seed=73)
+    ref = reference_block(w, host)
+    assert (np.abs(ref) > 256).mean() > 0.05, "the case must contain sums past 256"
+    run = Run(w, inputs=host)
+    run.launch()
+    assert_accept(run.result(), ref, W.BF16, exact=True, what=f"{tile} bf16 ties above 256")
