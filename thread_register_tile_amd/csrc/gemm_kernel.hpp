@@ -142,22 +142,15 @@ struct Out {
   __device__ static void st4(void* p, int64_t i, Vec v) {
     *reinterpret_cast<Vec*>(static_cast<uint16_t*>(p) + i) = v;
   }
-  // read / write once: non-temporal (the residual and C of the fast epilogue)
-  __device__ static Vec ld4_once(const void* p, int64_t i) {
-    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(static_cast<const uint16_t*>(p) + i));
-  }
-  __device__ static void st4_once(void* p, int64_t i, Vec v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(static_cast<uint16_t*>(p) + i));
-  }
   __device__ static float elem(Vec v, int e) {
     return to_f32<OT>((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
   }
   __device__ static Vec pack(const float (&y)[4]) {
     return Vec{pack2_f32<OT>(y[0], y[1]), pack2_f32<OT>(y[2], y[3])};
   }
-  // the same through a buffer descriptor at byte offset off: a load past
-  // the record count reads zero, a store past it is dropped (the run of
-  // four read / written once: non-temporal)
+  // a run of four through a buffer descriptor at byte offset off, read or
+  // written once (non-temporal: the residual and C of the fast epilogue); a
+  // load past the record count reads zero, a store past it is dropped
   __device__ static Vec ld4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, kNonTemporal);
   }
@@ -179,12 +172,6 @@ struct Out<DT_F32> {
   }
   __device__ static void st4(void* p, int64_t i, Vec v) {
     *reinterpret_cast<Vec*>(static_cast<float*>(p) + i) = v;
-  }
-  __device__ static Vec ld4_once(const void* p, int64_t i) {
-    return __builtin_nontemporal_load(reinterpret_cast<const Vec*>(static_cast<const float*>(p) + i));
-  }
-  __device__ static void st4_once(void* p, int64_t i, Vec v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<Vec*>(static_cast<float*>(p) + i));
   }
   __device__ static float elem(Vec v, int e) { return v[e]; }
   __device__ static Vec pack(const float (&y)[4]) { return Vec{y[0], y[1], y[2], y[3]}; }
